@@ -1,0 +1,363 @@
+"""Independent pins for the fp64 oracle (imported by test_oracle.py).
+
+Each ``pin_*`` function checks the oracle (the default build, or a variant
+library passed as ``lib``) against something that is not the oracle itself:
+
+* brute force: pure-Python ``math.fsum`` attention over K/V rows gathered by
+  a Python page walk, on tiny random batches;
+* closed forms: a single key, equal scores, two keys, the causal staircase
+  (q = 0 and V_j = j), strictly dominant last key;
+* hand-derived cases in ``tests/golden/worked_examples.json``;
+* invariants: physical page permutation, NaN poison outside valid slots, GQA
+  equals MHA with repeated K/V heads, merge of key splits;
+* reduction to ``torch.nn.functional.scaled_dot_product_attention`` (float64,
+  explicit bottom-right causal mask) and ``torch.logsumexp``.
+
+Each raises AssertionError on a mismatch.  They are functions (not tests) so
+that the mutation test can run all of them against an oracle with a planted
+mistake and demand that at least one fails.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle
+from paged_kv_cache_gqa_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "worked_examples.json")
+PS = 16
+
+
+# ---------------------------------------------------------------------------
+# helpers (no attention arithmetic beyond the brute-force statement itself)
+# ---------------------------------------------------------------------------
+
+def widen(a: np.ndarray) -> np.ndarray:
+    """float64 values of a float32 or bf16-bits array."""
+    if a.dtype == np.uint16:
+        return W.bf16_bits_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def narrow(x, dtype: str) -> np.ndarray:
+    x = np.asarray(x, dtype=np.float32)
+    return W.f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def dense_kv(w, s: int):
+    """K and V of sequence s as float64 [Hkv][n][D], by a Python page walk."""
+    n = int(w.seq_lens[s])
+    k = widen(w.k_pool)
+    v = widen(w.v_pool)
+    Hkv, D = w.num_kv_heads, w.head_dim
+    K = np.zeros((Hkv, n, D))
+    V = np.zeros((Hkv, n, D))
+    for j in range(n):
+        pg = int(w.block_table[s, j // PS])
+        t = j % PS
+        for g in range(Hkv):
+            K[g, j, :] = k[pg, g, t, :]
+            V[g, j, :] = v[pg, g, :, t]
+    return K, V
+
+
+def brute_force(w):
+    """Pure-Python attention (math.fsum sums, math.exp weights)."""
+    T, Hq, D = w.num_q_tokens, w.num_q_heads, w.head_dim
+    G = Hq // w.num_kv_heads
+    q = widen(w.q)
+    out = np.zeros((T, Hq, D))
+    lse = np.zeros((T, Hq))
+    for s in range(w.num_seqs):
+        K, V = dense_kv(w, s)
+        n = int(w.seq_lens[s])
+        q0, q1 = int(w.query_start_loc[s]), int(w.query_start_loc[s + 1])
+        for i, r in enumerate(range(q0, q1)):
+            last = n - (q1 - q0) + i
+            for h in range(Hq):
+                g = h // G
+                x = [w.scale * math.fsum(float(a) * float(b) for a, b in zip(q[r, h], K[g, j]))
+                     for j in range(last + 1)]
+                m = max(x)
+                e = [math.exp(xj - m) for xj in x]
+                tot = math.fsum(e)
+                for d in range(D):
+                    out[r, h, d] = math.fsum(e[j] * V[g, j, d] for j in range(last + 1)) / tot
+                lse[r, h] = m + math.log(tot)
+    return out, lse
+
+
+def run(w, lib=None):
+    return oracle.attention_workload(w, lib=lib)
+
+
+def poison_unused(w):
+    """Copy of w whose pool slots outside every sequence's valid keys hold NaN."""
+    k = w.k_pool.copy()
+    v = w.v_pool.copy()
+    valid = np.zeros((w.num_pages, PS), dtype=bool)
+    for s in range(w.num_seqs):
+        n = int(w.seq_lens[s])
+        for j in range(n):
+            valid[int(w.block_table[s, j // PS]), j % PS] = True
+    nan = W.f32_to_bf16_bits(np.float32(np.nan)) if w.dtype == "bf16" else np.float32(np.nan)
+    for pg in range(w.num_pages):
+        for t in range(PS):
+            if not valid[pg, t]:
+                k[pg, :, t, :] = nan
+                v[pg, :, :, t] = nan
+    return _replace(w, k_pool=k, v_pool=v)
+
+
+def permute_pages(w, seed: int):
+    """Same logical cache with physical pages renumbered by a random permutation."""
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(w.num_pages)  # old page id -> new page id
+    k = np.empty_like(w.k_pool)
+    v = np.empty_like(w.v_pool)
+    k[perm] = w.k_pool
+    v[perm] = w.v_pool
+    bt = np.where(w.block_table >= 0, perm[np.maximum(w.block_table, 0)], -1).astype(np.int32)
+    return _replace(w, k_pool=k, v_pool=v, block_table=bt)
+
+
+def _replace(w, **kw):
+    d = dict(name=w.name, dtype=w.dtype, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+             head_dim=w.head_dim, scale=w.scale, seq_lens=w.seq_lens, query_start_loc=w.query_start_loc,
+             block_table=w.block_table, q=w.q, k_pool=w.k_pool, v_pool=w.v_pool, meta=dict(w.meta))
+    d.update(kw)
+    return W.Workload(**d)
+
+
+def from_logical(dtype, Hq, Hkv, D, scale, num_pages, seqs):
+    """Build a batch from logical rows.  seqs: list of dicts with 'page_ids', 'keys', 'values'
+    ([key][kv_head][d] arrays) and 'queries' ([token][q_head][d]).  Unlisted slots hold NaN."""
+    nan = np.float32(np.nan)
+    kf = np.full((num_pages, Hkv, PS, D), nan, dtype=np.float32)
+    vf = np.full((num_pages, Hkv, D, PS), nan, dtype=np.float32)
+    max_pages = max(len(sq["page_ids"]) for sq in seqs)
+    bt = np.full((len(seqs), max_pages), -1, dtype=np.int32)
+    lens, qs = [], []
+    for s, sq in enumerate(seqs):
+        keys = np.asarray(sq["keys"], dtype=np.float64)
+        vals = np.asarray(sq["values"], dtype=np.float64)
+        n = keys.shape[0]
+        bt[s, :len(sq["page_ids"])] = sq["page_ids"]
+        for j in range(n):
+            pg = sq["page_ids"][j // PS]
+            kf[pg, :, j % PS, :] = keys[j]
+            vf[pg, :, :, j % PS] = vals[j]
+        lens.append(n)
+        qs.append(np.asarray(sq["queries"], dtype=np.float32).reshape(-1, Hq, D))
+    q = np.concatenate(qs, axis=0)
+    qsl = np.zeros(len(seqs) + 1, dtype=np.int32)
+    qsl[1:] = np.cumsum([x.shape[0] for x in qs])
+    return W.Workload(name="logical", dtype=dtype, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                      scale=float(scale), seq_lens=np.asarray(lens, dtype=np.int32), query_start_loc=qsl,
+                      block_table=bt, q=narrow(q, dtype), k_pool=narrow(kf, dtype), v_pool=narrow(vf, dtype))
+
+
+def tiny_batches():
+    """Random tiny batches: ragged lengths, windows of several rows, GQA, both dtypes."""
+    out = []
+    for seed, (B, maxlen, Hq, Hkv, D, dt, maxq) in enumerate([
+            (3, 40, 4, 2, 8, "f32", 6), (2, 35, 4, 1, 4, "bf16", 35), (3, 20, 2, 2, 8, "f32", 1),
+            (2, 33, 6, 3, 4, "bf16", 4)]):
+        out.append(W.make_random(100 + seed, B, maxlen, Hq, Hkv, D, dt, max_q=maxq))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# pins
+# ---------------------------------------------------------------------------
+
+def pin_brute_force(lib=None):
+    for w in tiny_batches():
+        o, l = run(w, lib)
+        bo, bl = brute_force(w)
+        assert np.max(np.abs(o - bo)) <= 1e-12, (w.name, np.max(np.abs(o - bo)))
+        assert np.max(np.abs(l - bl)) <= 1e-12, (w.name, np.max(np.abs(l - bl)))
+
+
+def pin_golden(lib=None):
+    doc = json.load(open(GOLDEN))
+    for case in doc["cases"]:
+        Hq, Hkv, D = case["num_q_heads"], case["num_kv_heads"], case["head_dim"]
+        seqs = []
+        for sq in case["sequences"]:
+            keys = np.asarray(sq["keys"], dtype=np.float64)
+            vals = np.asarray(sq["values"], dtype=np.float64)
+            if not sq.get("per_head"):
+                keys = np.repeat(keys[:, None, :], Hkv, axis=1)
+                vals = np.repeat(vals[:, None, :], Hkv, axis=1)
+            seqs.append(dict(sq, keys=keys, values=vals))
+        exp_out = [np.asarray(x, dtype=np.float64) for x in
+                   [[[float(v) for v in h] for h in tok] for tok in case["out"]]]
+        exp_lse = np.asarray([[float(v) for v in tok] for tok in case["lse"]], dtype=np.float64)
+        for dt in case["dtype"]:
+            w = from_logical(dt, Hq, Hkv, D, case["scale"], case["num_pages"], seqs)
+            o, l = run(w, lib)
+            assert np.max(np.abs(o - np.asarray(exp_out))) <= 1e-12, (case["name"], dt)
+            assert np.max(np.abs(l - exp_lse)) <= 1e-12, (case["name"], dt)
+
+
+def pin_closed_forms(lib=None):
+    rng = np.random.default_rng(7)
+    D, Hq, Hkv = 8, 4, 2
+    # (i) one key: out = V_0, lse = scale * q.k_0
+    for dt in ("f32", "bf16"):
+        k = rng.standard_normal((1, Hkv, D))
+        v = rng.standard_normal((1, Hkv, D))
+        q = rng.standard_normal((1, Hq, D))
+        w = from_logical(dt, Hq, Hkv, D, 0.3, 2, [dict(page_ids=[1], keys=k, values=v, queries=q)])
+        o, l = run(w, lib)
+        kk, vv, qq = widen(w.k_pool)[1, :, 0, :], widen(w.v_pool)[1, :, :, 0], widen(w.q)[0]
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            assert np.array_equal(o[0, h], vv[g]), "single key must return V_0 exactly"
+            assert abs(l[0, h] - 0.3 * math.fsum(qq[h] * kk[g])) <= 1e-12
+    # (ii) equal scores (q = 0): out = mean of visible V rows, lse = ln(#visible); over 3 pages
+    n, win = 37, 5
+    k = rng.standard_normal((n, Hkv, D))
+    v = rng.standard_normal((n, Hkv, D))
+    q = np.zeros((win, Hq, D))
+    w = from_logical("f32", Hq, Hkv, D, 1.0, 4, [dict(page_ids=[3, 0, 2], keys=k, values=v, queries=q)])
+    o, l = run(w, lib)
+    vv = v.astype(np.float32).astype(np.float64)
+    for i in range(win):
+        last = n - win + i
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            assert np.max(np.abs(o[i, h] - vv[:last + 1, g].mean(axis=0))) <= 1e-12
+            assert abs(l[i, h] - math.log(last + 1)) <= 1e-12
+    # (iii) two keys: weights sigmoid(x0 - x1), sigmoid(x1 - x0)
+    k = rng.standard_normal((2, 1, D))
+    v = rng.standard_normal((2, 1, D))
+    q = rng.standard_normal((1, 1, D))
+    w = from_logical("f32", 1, 1, D, 0.7, 1, [dict(page_ids=[0], keys=k, values=v, queries=q)])
+    o, l = run(w, lib)
+    kk, vv, qq = widen(w.k_pool)[0, 0, :2, :], widen(w.v_pool)[0, 0, :, :2].T, widen(w.q)[0, 0]
+    x0, x1 = 0.7 * math.fsum(qq * kk[0]), 0.7 * math.fsum(qq * kk[1])
+    a = 1.0 / (1.0 + math.exp(x1 - x0))
+    assert np.max(np.abs(o[0, 0] - (a * vv[0] + (1 - a) * vv[1]))) <= 1e-12
+    assert abs(l[0, 0] - (max(x0, x1) + math.log1p(math.exp(-abs(x0 - x1))))) <= 1e-12
+    # (iv) causal staircase: q = 0, V_j = j -> row i of a window over prior P: out = (P+i)/2
+    P, win = 21, 12
+    n = P + win
+    k = rng.standard_normal((n, 1, 4))
+    v = np.repeat(np.arange(n, dtype=np.float64)[:, None, None], 4, axis=2)
+    for dt in ("f32", "bf16"):
+        w = from_logical(dt, 2, 1, 4, 0.25, 3, [dict(page_ids=[2, 1, 0], keys=k, values=v,
+                                                     queries=np.zeros((win, 2, 4)))])
+        o, l = run(w, lib)
+        for i in range(win):
+            assert np.max(np.abs(o[i] - (P + i) / 2.0)) <= 1e-12, ("staircase", dt, i)
+            assert np.max(np.abs(l[i] - math.log(P + i + 1))) <= 1e-12
+    # (v) strictly increasing, widely spaced scores: out = V of the last visible key
+    n, win = 20, 4
+    k = np.zeros((n, 1, 2))
+    k[:, 0, 0] = 50.0 * np.arange(n)
+    v = rng.standard_normal((n, 1, 2))
+    w = from_logical("f32", 1, 1, 2, 1.0, 2, [dict(page_ids=[1, 0], keys=k, values=v,
+                                                   queries=np.tile([[[1.0, 0.0]]], (win, 1, 1)))])
+    o, l = run(w, lib)
+    vv = v.astype(np.float32).astype(np.float64)
+    for i in range(win):
+        last = n - win + i
+        assert np.max(np.abs(o[i, 0] - vv[last, 0])) <= 1e-12
+        assert abs(l[i, 0] - 50.0 * last) <= 1e-9
+
+
+def pin_invariants(lib=None):
+    for w in tiny_batches()[:2] + [W.make_config(1)]:
+        o, l = run(w, lib)
+        o2, l2 = run(permute_pages(w, 5), lib)
+        assert np.array_equal(o, o2) and np.array_equal(l, l2), "page permutation changed the result"
+        o3, l3 = run(poison_unused(w), lib)
+        assert np.array_equal(o, o3) and np.array_equal(l, l3), "unused slots leaked into the result"
+    # GQA == MHA with each K/V head repeated G times
+    w = W.make_random(301, 3, 30, 6, 2, 8, "f32", max_q=5)
+    G = 3
+    mha = _replace(w, num_kv_heads=6, k_pool=np.repeat(w.k_pool, G, axis=1),
+                   v_pool=np.repeat(w.v_pool, G, axis=1))
+    o, l = run(w, lib)
+    o2, l2 = run(mha, lib)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2), "GQA differs from MHA with repeated K/V"
+
+
+def pin_merge_of_splits(lib=None):
+    """Attention over keys [0, a) and [a, n) merged == attention over [0, n), for every a."""
+    rng = np.random.default_rng(11)
+    n, D, Hq, Hkv = 37, 8, 4, 2
+    k = rng.standard_normal((n, Hkv, D))
+    v = rng.standard_normal((n, Hkv, D))
+    q = rng.standard_normal((1, Hq, D))
+    full = from_logical("f32", Hq, Hkv, D, 0.4, 3, [dict(page_ids=[0, 1, 2], keys=k, values=v, queries=q)])
+    o, l = run(full, lib)
+    for a in range(1, n):
+        left = from_logical("f32", Hq, Hkv, D, 0.4, 3, [dict(page_ids=[2, 0, 1][:(a + 15) // 16], keys=k[:a],
+                                                            values=v[:a], queries=q)])
+        right = from_logical("f32", Hq, Hkv, D, 0.4, 3, [dict(page_ids=[1, 2, 0][:(n - a + 15) // 16],
+                                                             keys=k[a:], values=v[a:], queries=q)])
+        o1, l1 = run(left, lib)
+        o2, l2 = run(right, lib)
+        om, lm = oracle.merge(np.stack([o1.reshape(Hq, D), o2.reshape(Hq, D)]), np.stack([l1[0], l2[0]]), lib=lib)
+        assert np.max(np.abs(om - o.reshape(Hq, D))) <= 1e-12, a
+        assert np.max(np.abs(lm - l[0])) <= 1e-12, a
+    # a part that saw no key (lse = -inf) contributes nothing
+    om, lm = oracle.merge(np.stack([o.reshape(Hq, D), np.full((Hq, D), 123.0)]),
+                          np.stack([l[0], np.full(Hq, -np.inf)]), lib=lib)
+    assert np.max(np.abs(om - o.reshape(Hq, D))) <= 1e-15 and np.max(np.abs(lm - l[0])) <= 1e-15
+    # closed form: parts with lse ln 1 and ln 3 weigh 1/4 and 3/4
+    om, lm = oracle.merge(np.array([[[4.0]], [[8.0]]]), np.array([[0.0], [math.log(3.0)]]), lib=lib)
+    assert abs(om[0, 0] - 7.0) <= 1e-14 and abs(lm[0] - math.log(4.0)) <= 1e-14
+
+
+def pin_sdpa(lib=None):
+    """fp64 torch scaled_dot_product_attention with an explicit bottom-right causal mask."""
+    import torch
+    for seed, (B, maxlen, Hq, Hkv, D, dt, maxq) in enumerate([
+            (3, 300, 8, 2, 64, "f32", 40), (2, 200, 4, 4, 128, "bf16", 200), (4, 90, 8, 1, 64, "bf16", 3)]):
+        w = W.make_random(200 + seed, B, maxlen, Hq, Hkv, D, dt, max_q=maxq)
+        o, l = run(w, lib)
+        G = Hq // Hkv
+        q = torch.from_numpy(widen(w.q))
+        for s in range(w.num_seqs):
+            q0, q1 = int(w.query_start_loc[s]), int(w.query_start_loc[s + 1])
+            if q1 == q0:
+                continue
+            n = int(w.seq_lens[s])
+            K, V = dense_kv(w, s)
+            Kt = torch.from_numpy(K).repeat_interleave(G, dim=0)  # [Hq][n][D]
+            Vt = torch.from_numpy(V).repeat_interleave(G, dim=0)
+            Q = q[q0:q1].transpose(0, 1).contiguous()  # [Hq][win][D]
+            win = q1 - q0
+            mask = torch.arange(n)[None, :] <= (n - win + torch.arange(win))[:, None]
+            ref = torch.nn.functional.scaled_dot_product_attention(Q[None], Kt[None], Vt[None],
+                                                                   attn_mask=mask[None, None], scale=w.scale)[0]
+            scores = (Q @ Kt.transpose(1, 2).contiguous()) * w.scale
+            ref_lse = torch.logsumexp(scores.masked_fill(~mask[None], -math.inf), dim=-1)  # [Hq][win]
+            assert np.max(np.abs(o[q0:q1] - ref.transpose(0, 1).numpy())) <= 1e-12, (seed, s)
+            assert np.max(np.abs(l[q0:q1] - ref_lse.transpose(0, 1).numpy())) <= 1e-12, (seed, s)
+
+
+def pin_gather(lib=None):
+    for w in tiny_batches()[:2]:
+        for s in range(w.num_seqs):
+            n = int(w.seq_lens[s])
+            pages = w.block_table[s, (np.arange(n) // PS)]
+            slots = np.arange(n) % PS
+            ek = w.k_pool[pages, :, slots, :].transpose(1, 0, 2)  # numpy fancy-index gather
+            ev = w.v_pool[pages, :, :, slots].transpose(1, 0, 2)
+            gk = oracle.gather(w.k_pool, w.block_table, w.seq_lens, s, "k", lib=lib)
+            gv = oracle.gather(w.v_pool, w.block_table, w.seq_lens, s, "v", lib=lib)
+            assert gk.tobytes() == np.ascontiguousarray(ek).tobytes()
+            assert gv.tobytes() == np.ascontiguousarray(ev).tobytes()
+
+
+ALL_PINS = [pin_brute_force, pin_golden, pin_closed_forms, pin_invariants, pin_merge_of_splits,
+            pin_sdpa, pin_gather]
