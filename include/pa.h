@@ -1,0 +1,213 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged-KV grouped-query attention library.
+ *
+ * One call computes causal grouped-query attention for a mixed batch of
+ * prefill chunks, decode steps and speculative-verify windows whose keys and
+ * values sit in fixed-size pages addressed through a block table, and returns
+ * the output and the per-row log-sum-exp.
+ *
+ * Sources for what is computed:
+ *   - XY-Serve verdict page, pith_extraction.key_machinery: the attention
+ *     primitive is a tile of the matmul-softmax-matmul pattern over a set of
+ *     query rows and a K/V length.
+ *   - same page, core_discovery: prefill, decode and verify tokens are batched
+ *     together; K/V live in a PagedAttention-style block cache; tiles that the
+ *     causal mask makes empty are skipped.
+ *   - same page, forward_implications: one kernel with row-wise mask control
+ *     serves all three kinds of rows.
+ *   - "Understanding Inference Scaling for LLMs" review, Reference graph [4]:
+ *     grouped-query attention (a group of query heads shares one K/V head).
+ *
+ * For sequence s with n_s = seq_lens[s] keys and q_s = query_start_loc[s+1] -
+ * query_start_loc[s] query tokens, window row i (query token
+ * r = query_start_loc[s] + i) sits at absolute position p = n_s - q_s + i and
+ * sees keys 0..p (bottom-right causal alignment; the new tokens' own K/V are
+ * already in the pool).  Query head h reads K/V head h / (Hq / Hkv).
+ *     out[r][h][:] = sum_j softmax_j(scale * q[r][h].k_j) v_j
+ *     lse[r][h]    = ln sum_j exp(scale * q[r][h].k_j)          (natural log)
+ *
+ * Memory layout (all device memory, row-major, no padding):
+ *   q            [T_q][Hq][D]          dtype      T_q = query_start_loc[B]
+ *   k_pool       [NP][Hkv][16][D]      dtype      a page holds 16 token slots
+ *   v_pool       [NP][Hkv][D][16]      dtype      the same pages with slots innermost
+ *   block_table  [B][max_pages_per_seq] int32     physical page of logical page j of
+ *                                                 sequence s; entries >= ceil(n_s/16)
+ *                                                 are never read (pad with -1)
+ *   seq_lens     [B]                   int32      keys per sequence (new tokens included)
+ *   query_start_loc [B+1]              int32      0 = qsl[0] <= qsl[1] <= ... = T_q
+ *   out          [T_q][Hq][D]          dtype
+ *   lse          [T_q][Hq]             float32
+ * Slots beyond n_s in a sequence's last page and pages no sequence uses may
+ * hold any bits (NaN included); they never reach the result.
+ *
+ * Ownership and streams: the caller allocates and owns every buffer; the
+ * library never allocates or frees device memory on these calls and keeps no
+ * state between calls.  Work is enqueued on `stream` (a hipStream_t; NULL is
+ * the default stream) and the call returns without waiting, except
+ * pa_validate, which synchronizes.  Two calls that share a workspace must be
+ * ordered on one stream.
+ *
+ * Errors: descriptor and pointer checks run on the host before anything is
+ * enqueued and return a pa_status; a failed launch returns PA_ERR_HIP.  The
+ * contents of seq_lens, query_start_loc and block_table are not checked on the
+ * attention path (q_len > seq_len or a page id outside [0, NP) is undefined
+ * behaviour there); pa_validate checks them.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+#define PA_PAGE_SIZE 16
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL_POINTER = 1,       /* a required pointer is NULL */
+  PA_ERR_BAD_SHAPE = 2,          /* negative size, Hq % Hkv != 0, ... */
+  PA_ERR_UNSUPPORTED = 3,        /* head_dim not 64/128, page_size not 16, unknown dtype */
+  PA_ERR_WORKSPACE_TOO_SMALL = 4,
+  PA_ERR_HIP = 5,                /* a HIP runtime call or kernel launch failed */
+  PA_ERR_INVALID_CONTENT = 6     /* pa_validate found bad seq_lens / query_start_loc / block_table */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Shapes of one batch.  All fields are host values. */
+typedef struct pa_desc {
+  int32_t num_seqs;          /* B >= 0 */
+  int32_t num_q_tokens;      /* T_q >= 0; must equal query_start_loc[B] */
+  int32_t num_q_heads;       /* Hq >= 1 */
+  int32_t num_kv_heads;      /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;          /* D: 64 or 128 */
+  int32_t page_size;         /* must be PA_PAGE_SIZE (16) */
+  int32_t num_pages;         /* NP >= 1: pages in each pool */
+  int32_t max_pages_per_seq; /* block_table row stride, >= ceil(max n_s / 16) */
+  int32_t dtype;             /* pa_dtype of q, k_pool, v_pool and out */
+  float scale;               /* multiplies q.k before the softmax */
+} pa_desc;
+
+/* PA_ABI_VERSION of the loaded library. */
+int pa_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* pa_status_string(pa_status status);
+
+/* Host-only check of a descriptor (no HIP call): PA_OK, PA_ERR_BAD_SHAPE or PA_ERR_UNSUPPORTED. */
+pa_status pa_check_desc(const pa_desc* desc);
+
+/*
+ * Bytes of device workspace pa_attention needs for `desc` on the current HIP
+ * device (the plan, the work list and the split-key partial results).  The
+ * size depends only on the descriptor and on the device's compute-unit count.
+ * Writes *bytes; returns PA_ERR_NULL_POINTER, a descriptor error or PA_ERR_HIP.
+ */
+pa_status pa_workspace_size(const pa_desc* desc, size_t* bytes);
+
+/*
+ * Causal GQA attention over the paged cache for a mixed prefill / decode /
+ * verify batch (the formula and layouts above).  Enqueues, in order on
+ * `stream`: the planner (work list from seq_lens and query_start_loc), the
+ * attention kernel (one persistent launch over all rows: decode and verify
+ * rows split keys across waves, prefill rows share K/V tiles through LDS;
+ * every (row, head) whose keys were split is written as partial results), and
+ * the log-sum-exp merge of split rows.  `workspace` must hold at least
+ * pa_workspace_size bytes and be 256-byte aligned.  T_q == 0 enqueues nothing.
+ */
+pa_status pa_attention(const pa_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_table, const int32_t* seq_lens,
+                       const int32_t* query_start_loc, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * The three stages of pa_attention, for callers that time or reuse them.
+ * pa_plan writes the work list into the workspace (it reads only seq_lens and
+ * query_start_loc; a plan stays valid while those and desc are unchanged).
+ * pa_attention_planned runs the attention kernel on a planned workspace:
+ * unsplit rows get their final out/lse, split rows leave partial results in
+ * the workspace.  pa_merge_planned combines those partials into out/lse.
+ * pa_attention == pa_plan + pa_attention_planned + pa_merge_planned.
+ */
+pa_status pa_plan(const pa_desc* desc, const int32_t* seq_lens, const int32_t* query_start_loc,
+                  void* workspace, size_t workspace_bytes, void* stream);
+pa_status pa_attention_planned(const pa_desc* desc, const void* q, const void* k_pool,
+                               const void* v_pool, const int32_t* block_table,
+                               const int32_t* seq_lens, const int32_t* query_start_loc, void* out,
+                               float* lse, void* workspace, size_t workspace_bytes, void* stream);
+pa_status pa_merge_planned(const pa_desc* desc, const int32_t* query_start_loc, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Plan inspection (debug / tests).  A plan is a list of work units; unit u
+ * covers query rows [row0, row0 + n_rows) of sequence `seq` for K/V head
+ * `kv_head` (row index = window token * (Hq/Hkv) + head within the group)
+ * against keys [0, n_keys), cut into ceil(n_keys / 32) chunks of 32 keys.
+ * Units are laid out on one cost axis (cost0 = prefix of n_chunks * cost
+ * weight); the persistent launch's workgroup k takes the chunks whose start
+ * lies in [floor(k*C/S), floor((k+1)*C/S)), C = total cost, S = n_slots.
+ * kind 0: rows <= 32, the four waves of a workgroup split the chunks;
+ * kind 1: rows <= 128, each wave takes 32 rows and the chunks are shared.
+ * n_pieces > 1 means the unit's keys were split between workgroups and merged.
+ */
+typedef struct pa_plan_unit {
+  int32_t seq, kv_head, row0, n_rows;
+  int32_t n_keys, n_chunks, kind, cost_weight;
+  int64_t cost0;
+  int32_t piece_base, n_pieces;
+} pa_plan_unit;
+
+typedef struct pa_plan_header {
+  int32_t n_units, n_split, n_slots, grid;
+  int64_t total_cost, partial_rows;
+} pa_plan_header;
+
+/*
+ * Copy the plan held in `workspace` to host memory: *header, and up to
+ * max_units units.  Synchronizes `stream`.
+ */
+pa_status pa_plan_read(const pa_desc* desc, const void* workspace, size_t workspace_bytes,
+                       pa_plan_header* header, pa_plan_unit* units, int32_t max_units, void* stream);
+
+/*
+ * Gather keys [0, n_keys) of sequence `seq` from one pool into dense
+ * [Hkv][n_keys][D] (element bits copied unchanged), walking the block table.
+ * which = 0 reads a K pool ([NP][Hkv][16][D]), which = 1 a V pool
+ * ([NP][Hkv][D][16]).  Keys at or beyond seq_lens[seq] are written as zero bits.
+ */
+pa_status pa_gather_kv(const pa_desc* desc, int32_t which, const void* pool, const int32_t* block_table,
+                       const int32_t* seq_lens, int32_t seq, int32_t n_keys, void* dense_out,
+                       void* stream);
+
+/*
+ * Log-sum-exp merge of attention results over disjoint key sets (for keys
+ * split across launches or devices):
+ *     lse[r] = ln sum_i exp(lse_parts[i][r]),
+ *     out[r][:] = sum_i exp(lse_parts[i][r] - lse[r]) * o_parts[i][r][:]
+ * o_parts [n_parts][rows][D] float32, lse_parts [n_parts][rows] float32 (a
+ * part with lse = -inf saw no key and contributes nothing), out [rows][D] in
+ * out_dtype (pa_dtype), lse [rows] float32.  D: 64 or 128.
+ */
+pa_status pa_merge(int32_t n_parts, int64_t rows, int32_t head_dim, const float* o_parts,
+                   const float* lse_parts, int32_t out_dtype, void* out, float* lse, void* stream);
+
+/*
+ * Check the batch contents on the device: query_start_loc starts at 0, is
+ * non-decreasing and ends at T_q; 0 <= q_len <= seq_len; ceil(seq_len/16) <=
+ * max_pages_per_seq; every block-table entry a sequence reads lies in
+ * [0, num_pages).  Uses the first 256 bytes of `workspace` and synchronizes
+ * `stream`.  Returns PA_OK or PA_ERR_INVALID_CONTENT.
+ */
+pa_status pa_validate(const pa_desc* desc, const int32_t* block_table, const int32_t* seq_lens,
+                      const int32_t* query_start_loc, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

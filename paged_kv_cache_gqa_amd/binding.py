@@ -1,0 +1,245 @@
+"""ctypes binding of the C ABI in ``include/pa.h`` (argument marshalling only).
+
+Every function has the name of its C entry point without the ``pa_`` prefix.
+torch supplies device memory and the current stream; all arithmetic runs in
+the gfx950 kernels of ``libpa_mi355x.so``.  There is no fallback: if the
+library is missing or a call fails, a ``PagedAttentionError`` is raised.
+
+torch is imported before the library is opened so that the library binds to
+the HIP runtime torch already loaded (one runtime per process).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+PAGE_SIZE = 16
+PA_F32, PA_BF16 = 0, 1
+_DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, call: str, status: int, text: str):
+        super().__init__(f"{call}: {text} (status {status})")
+        self.status = status
+
+
+class PaDesc(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_q_tokens", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class PlanUnit(ctypes.Structure):
+    _fields_ = [("seq", ctypes.c_int32), ("kv_head", ctypes.c_int32), ("row0", ctypes.c_int32),
+                ("n_rows", ctypes.c_int32), ("n_keys", ctypes.c_int32), ("n_chunks", ctypes.c_int32),
+                ("kind", ctypes.c_int32), ("cost_weight", ctypes.c_int32), ("cost0", ctypes.c_int64),
+                ("piece_base", ctypes.c_int32), ("n_pieces", ctypes.c_int32)]
+
+
+class PlanHeader(ctypes.Structure):
+    _fields_ = [("n_units", ctypes.c_int32), ("n_split", ctypes.c_int32), ("n_slots", ctypes.c_int32),
+                ("grid", ctypes.c_int32), ("total_cost", ctypes.c_int64), ("partial_rows", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise PagedAttentionError("load", -1, f"{LIB_PATH} is missing; run paged_kv_cache_gqa_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        dp = ctypes.POINTER(PaDesc)
+        L.pa_abi_version.restype = ctypes.c_int
+        L.pa_status_string.restype = ctypes.c_char_p
+        L.pa_status_string.argtypes = [ctypes.c_int]
+        L.pa_check_desc.argtypes = [dp]
+        L.pa_workspace_size.argtypes = [dp, ctypes.POINTER(sz)]
+        L.pa_attention.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.pa_plan.argtypes = [dp, vp, vp, vp, sz, vp]
+        L.pa_attention_planned.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.pa_merge_planned.argtypes = [dp, vp, vp, vp, vp, sz, vp]
+        L.pa_plan_read.argtypes = [dp, vp, sz, ctypes.POINTER(PlanHeader), ctypes.POINTER(PlanUnit), i32, vp]
+        L.pa_gather_kv.argtypes = [dp, i32, vp, vp, vp, i32, i32, vp, vp]
+        L.pa_merge.argtypes = [i32, i64, i32, vp, vp, i32, vp, vp, vp]
+        L.pa_validate.argtypes = [dp, vp, vp, vp, vp, sz, vp]
+        for name in ("pa_check_desc", "pa_workspace_size", "pa_attention", "pa_plan", "pa_attention_planned",
+                     "pa_merge_planned", "pa_plan_read", "pa_gather_kv", "pa_merge", "pa_validate"):
+            getattr(L, name).restype = ctypes.c_int
+        if L.pa_abi_version() != 1:
+            raise PagedAttentionError("load", -1, "ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().pa_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(lib().pa_abi_version())
+
+
+def _check(call: str, status: int) -> None:
+    if status != 0:
+        raise PagedAttentionError(call, status, status_string(status))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_desc(q, k_pool, block_table, seq_lens, scale: float) -> PaDesc:
+    """Descriptor from tensor shapes (host values only; nothing is read from the device)."""
+    T, Hq, D = q.shape
+    NP, Hkv, ps, D2 = k_pool.shape
+    if ps != PAGE_SIZE or D2 != D:
+        raise ValueError(f"k_pool must be [NP][Hkv][16][{D}], got {tuple(k_pool.shape)}")
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    return PaDesc(num_seqs=seq_lens.shape[0], num_q_tokens=T, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                  page_size=PAGE_SIZE, num_pages=NP, max_pages_per_seq=block_table.shape[1],
+                  dtype=_DTYPES[q.dtype], scale=float(scale))
+
+
+def check_desc(desc: PaDesc) -> int:
+    return int(lib().pa_check_desc(ctypes.byref(desc)))
+
+
+def workspace_size(desc: PaDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check("pa_workspace_size", lib().pa_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return int(n.value)
+
+
+def alloc_workspace(desc: PaDesc, device=None) -> torch.Tensor:
+    """A 256-byte-aligned uint8 device buffer of workspace_size(desc) bytes (torch's allocator aligns)."""
+    return torch.empty(max(workspace_size(desc), 256), dtype=torch.uint8, device=device or "cuda")
+
+
+def _check_inputs(q, k_pool, v_pool, block_table, seq_lens, query_start_loc):
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("block_table", block_table),
+                    ("seq_lens", seq_lens), ("query_start_loc", query_start_loc)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for name, t in (("block_table", block_table), ("seq_lens", seq_lens), ("query_start_loc", query_start_loc)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    if k_pool.dtype != q.dtype or v_pool.dtype != q.dtype:
+        raise TypeError("q, k_pool and v_pool must share a dtype")
+    NP, Hkv, ps, D = k_pool.shape
+    if tuple(v_pool.shape) != (NP, Hkv, D, ps):
+        raise ValueError(f"v_pool must be [NP][Hkv][D][16] = {(NP, Hkv, D, ps)}, got {tuple(v_pool.shape)}")
+    if query_start_loc.shape[0] != seq_lens.shape[0] + 1 or block_table.shape[0] != seq_lens.shape[0]:
+        raise ValueError("seq_lens [B], query_start_loc [B+1] and block_table [B][*] disagree")
+
+
+def attention(q, k_pool, v_pool, block_table, seq_lens, query_start_loc, scale: float, out=None, lse=None,
+              workspace=None, stream=None):
+    """Paged causal GQA attention (pa_attention).  Returns (out [T_q][Hq][D], lse [T_q][Hq] float32)."""
+    _check_inputs(q, k_pool, v_pool, block_table, seq_lens, query_start_loc)
+    desc = make_desc(q, k_pool, block_table, seq_lens, scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(desc, q.device)
+    _check("pa_attention", lib().pa_attention(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                              _ptr(block_table), _ptr(seq_lens), _ptr(query_start_loc), _ptr(out),
+                                              _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def plan(desc: PaDesc, seq_lens, query_start_loc, workspace, stream=None) -> None:
+    _check("pa_plan", lib().pa_plan(ctypes.byref(desc), _ptr(seq_lens), _ptr(query_start_loc), _ptr(workspace),
+                                    workspace.numel(), _stream(stream)))
+
+
+def attention_planned(desc: PaDesc, q, k_pool, v_pool, block_table, seq_lens, query_start_loc, out, lse, workspace,
+                      stream=None) -> None:
+    _check("pa_attention_planned",
+           lib().pa_attention_planned(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                      _ptr(seq_lens), _ptr(query_start_loc), _ptr(out), _ptr(lse), _ptr(workspace),
+                                      workspace.numel(), _stream(stream)))
+
+
+def merge_planned(desc: PaDesc, query_start_loc, out, lse, workspace, stream=None) -> None:
+    _check("pa_merge_planned", lib().pa_merge_planned(ctypes.byref(desc), _ptr(query_start_loc), _ptr(out), _ptr(lse),
+                                                      _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def plan_read(desc: PaDesc, workspace, max_units: int = 1 << 20, stream=None):
+    """(header dict, list of unit dicts) of the plan in `workspace` (synchronizes)."""
+    hdr = PlanHeader()
+    units = (PlanUnit * max(1, max_units))()
+    _check("pa_plan_read", lib().pa_plan_read(ctypes.byref(desc), _ptr(workspace), workspace.numel(),
+                                              ctypes.byref(hdr), units, max_units, _stream(stream)))
+    h = {f: getattr(hdr, f) for f, _ in PlanHeader._fields_}
+    n = min(h["n_units"], max_units)
+    us = [{f: getattr(units[i], f) for f, _ in PlanUnit._fields_} for i in range(n)]
+    return h, us
+
+
+def gather_kv(desc: PaDesc, which: int, pool, block_table, seq_lens, seq: int, n_keys: int, stream=None):
+    """Dense [Hkv][n_keys][D] copy of one sequence's K (which=0) or V (which=1) rows."""
+    dense = torch.empty((desc.num_kv_heads, n_keys, desc.head_dim), dtype=pool.dtype, device=pool.device)
+    _check("pa_gather_kv", lib().pa_gather_kv(ctypes.byref(desc), int(which), _ptr(pool), _ptr(block_table),
+                                              _ptr(seq_lens), int(seq), int(n_keys), _ptr(dense), _stream(stream)))
+    return dense
+
+
+def merge(o_parts, lse_parts, out_dtype=torch.float32, stream=None):
+    """Log-sum-exp merge (pa_merge) of o_parts [P][rows][D] f32 and lse_parts [P][rows] f32."""
+    P, rows, D = o_parts.shape
+    out = torch.empty((rows, D), dtype=out_dtype, device=o_parts.device)
+    lse = torch.empty((rows,), dtype=torch.float32, device=o_parts.device)
+    _check("pa_merge", lib().pa_merge(P, rows, D, _ptr(o_parts.contiguous()), _ptr(lse_parts.contiguous()),
+                                      _DTYPES[out_dtype], _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def validate(desc: PaDesc, block_table, seq_lens, query_start_loc, workspace, stream=None) -> int:
+    """pa_validate status (0 = OK, 6 = invalid content); synchronizes."""
+    st = lib().pa_validate(ctypes.byref(desc), _ptr(block_table), _ptr(seq_lens), _ptr(query_start_loc),
+                           _ptr(workspace), workspace.numel(), _stream(stream))
+    if st not in (0, 6):
+        _check("pa_validate", st)
+    return int(st)
+
+
+def to_device(w, device="cuda"):
+    """Device tensors of a ``workloads.Workload`` (bf16 bit patterns are reinterpreted, not converted)."""
+    import numpy as np
+
+    def arr(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+    return {"q": arr(w.q), "k_pool": arr(w.k_pool), "v_pool": arr(w.v_pool),
+            "block_table": torch.from_numpy(np.ascontiguousarray(w.block_table, dtype=np.int32)).to(device),
+            "seq_lens": torch.from_numpy(np.ascontiguousarray(w.seq_lens, dtype=np.int32)).to(device),
+            "query_start_loc": torch.from_numpy(np.ascontiguousarray(w.query_start_loc, dtype=np.int32)).to(device)}

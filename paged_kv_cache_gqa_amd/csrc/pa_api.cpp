@@ -1,0 +1,297 @@
+// pa_api.cpp -- host side of the C ABI declared in include/pa.h: descriptor
+// checks, workspace sizing, and the launches of the gfx950 kernels.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "pa_internal.h"
+
+namespace {
+
+using pa::WsLayout;
+
+struct DeviceInfo {
+  bool ready = false;
+  int cus = 0;
+  int blocks_per_cu[2][2] = {{0, 0}, {0, 0}};  // [dtype][D == 128]
+};
+
+constexpr int kMaxDevices = 64;
+std::mutex g_mu;
+DeviceInfo g_dev[kMaxDevices];
+
+// Compute units of the current device and how many attention workgroups each holds.
+pa_status device_grid(const pa_desc& d, int* grid) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceInfo& info = g_dev[dev];
+  if (!info.ready) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return PA_ERR_HIP;
+    for (int dt = 0; dt < 2; ++dt)
+      for (int big = 0; big < 2; ++big) {
+        const int n = pa::attention_blocks_per_cu(dt, big ? 128 : 64);
+        if (n <= 0) return PA_ERR_HIP;
+        info.blocks_per_cu[dt][big] = n;
+      }
+    info.cus = cus;
+    info.ready = true;
+  }
+  *grid = info.cus * info.blocks_per_cu[d.dtype == PA_BF16 ? 1 : 0][d.head_dim == 128 ? 1 : 0];
+  return PA_OK;
+}
+
+struct Ws {
+  WsLayout L;
+  pa_plan_header* hdr;
+  int64_t* seq_cost;
+  int32_t* seq_unit;
+  pa_plan_unit* units;
+  int32_t* split;
+  float* part_lse;
+  float* part_o;
+};
+
+Ws carve(void* base, const WsLayout& L) {
+  char* b = static_cast<char*>(base);
+  Ws w;
+  w.L = L;
+  w.hdr = reinterpret_cast<pa_plan_header*>(b + L.header);
+  w.seq_cost = reinterpret_cast<int64_t*>(b + L.seq_cost);
+  w.seq_unit = reinterpret_cast<int32_t*>(b + L.seq_unit);
+  w.units = reinterpret_cast<pa_plan_unit*>(b + L.units);
+  w.split = reinterpret_cast<int32_t*>(b + L.split);
+  w.part_lse = reinterpret_cast<float*>(b + L.part_lse);
+  w.part_o = reinterpret_cast<float*>(b + L.part_o);
+  return w;
+}
+
+// Descriptor + workspace checks shared by the staged entry points.
+pa_status prepare(const pa_desc* desc, void* workspace, size_t workspace_bytes, int* grid, Ws* ws) {
+  if (!desc) return PA_ERR_NULL_POINTER;
+  const pa_status st = pa_check_desc(desc);
+  if (st != PA_OK) return st;
+  if (!workspace) return PA_ERR_NULL_POINTER;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return PA_ERR_BAD_SHAPE;
+  const pa_status gs = device_grid(*desc, grid);
+  if (gs != PA_OK) return gs;
+  const WsLayout L = pa::ws_layout(*desc, *grid);
+  if (workspace_bytes < L.total) return PA_ERR_WORKSPACE_TOO_SMALL;
+  *ws = carve(workspace, L);
+  return PA_OK;
+}
+
+pa::AttnArgs attn_args(const pa_desc& d, const void* q, const void* k, const void* v, const int32_t* bt,
+                       const int32_t* sl, const int32_t* qsl, void* out, float* lse, const Ws& ws) {
+  pa::AttnArgs a;
+  a.q = q;
+  a.k_pool = k;
+  a.v_pool = v;
+  a.block_table = bt;
+  a.seq_lens = sl;
+  a.qsl = qsl;
+  a.out = out;
+  a.lse = lse;
+  a.hdr = ws.hdr;
+  a.units = ws.units;
+  a.part_o = ws.part_o;
+  a.part_lse = ws.part_lse;
+  a.num_q_heads = d.num_q_heads;
+  a.num_kv_heads = d.num_kv_heads;
+  a.group = d.num_q_heads / d.num_kv_heads;
+  a.max_pages = d.max_pages_per_seq;
+  a.scale_log2 = d.scale * 1.44269504088896340736f;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL_POINTER: return "PA_ERR_NULL_POINTER: a required pointer is NULL";
+    case PA_ERR_BAD_SHAPE: return "PA_ERR_BAD_SHAPE: inconsistent sizes in the descriptor";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: head_dim must be 64 or 128, page_size 16, dtype f32 or bf16";
+    case PA_ERR_WORKSPACE_TOO_SMALL: return "PA_ERR_WORKSPACE_TOO_SMALL: workspace smaller than pa_workspace_size";
+    case PA_ERR_HIP: return "PA_ERR_HIP: a HIP runtime call or kernel launch failed";
+    case PA_ERR_INVALID_CONTENT: return "PA_ERR_INVALID_CONTENT: seq_lens / query_start_loc / block_table inconsistent";
+  }
+  return "unknown pa_status";
+}
+
+pa_status pa_check_desc(const pa_desc* d) {
+  if (!d) return PA_ERR_NULL_POINTER;
+  if (d->num_seqs < 0 || d->num_q_tokens < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1) return PA_ERR_BAD_SHAPE;
+  if (d->num_q_heads % d->num_kv_heads != 0) return PA_ERR_BAD_SHAPE;
+  if (d->num_pages < 1 || d->max_pages_per_seq < 1) return PA_ERR_BAD_SHAPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (d->page_size != PA_PAGE_SIZE) return PA_ERR_UNSUPPORTED;
+  if (d->dtype != PA_F32 && d->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (!std::isfinite(d->scale)) return PA_ERR_BAD_SHAPE;
+  // row and offset arithmetic in the kernels is 32-bit per sequence / 64-bit for addresses
+  if (int64_t(d->num_q_tokens) * d->num_q_heads > (int64_t(1) << 31) - 1) return PA_ERR_BAD_SHAPE;
+  if (int64_t(d->max_pages_per_seq) * PA_PAGE_SIZE > (int64_t(1) << 30)) return PA_ERR_BAD_SHAPE;
+  return PA_OK;
+}
+
+pa_status pa_workspace_size(const pa_desc* desc, size_t* bytes) {
+  if (!desc || !bytes) return PA_ERR_NULL_POINTER;
+  const pa_status st = pa_check_desc(desc);
+  if (st != PA_OK) return st;
+  int grid = 0;
+  const pa_status gs = device_grid(*desc, &grid);
+  if (gs != PA_OK) return gs;
+  *bytes = pa::ws_layout(*desc, grid).total;
+  return PA_OK;
+}
+
+pa_status pa_plan(const pa_desc* desc, const int32_t* seq_lens, const int32_t* qsl, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  int grid = 0;
+  Ws ws;
+  const pa_status st = prepare(desc, workspace, workspace_bytes, &grid, &ws);
+  if (st != PA_OK) return st;
+  if (desc->num_seqs > 0 && (!seq_lens || !qsl)) return PA_ERR_NULL_POINTER;
+  pa::PlanArgs a;
+  a.seq_lens = seq_lens;
+  a.qsl = qsl;
+  a.hdr = ws.hdr;
+  a.units = ws.units;
+  a.split = ws.split;
+  a.seq_cost = ws.seq_cost;
+  a.seq_unit = ws.seq_unit;
+  a.num_seqs = desc->num_seqs;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.group = desc->num_q_heads / desc->num_kv_heads;
+  a.grid = grid;
+  a.max_units = ws.L.max_units;
+  a.max_partial_rows = ws.L.max_partial_rows;
+  return pa::launch_plan(a, stream) == 0 ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_attention_planned(const pa_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* block_table, const int32_t* seq_lens, const int32_t* qsl, void* out,
+                               float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  int grid = 0;
+  Ws ws;
+  const pa_status st = prepare(desc, workspace, workspace_bytes, &grid, &ws);
+  if (st != PA_OK) return st;
+  if (desc->num_q_tokens == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !qsl || !out || !lse) return PA_ERR_NULL_POINTER;
+  const pa::AttnArgs a = attn_args(*desc, q, k_pool, v_pool, block_table, seq_lens, qsl, out, lse, ws);
+  return pa::launch_attention(a, desc->dtype, desc->head_dim, grid, stream) == 0 ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_merge_planned(const pa_desc* desc, const int32_t* qsl, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  int grid = 0;
+  Ws ws;
+  const pa_status st = prepare(desc, workspace, workspace_bytes, &grid, &ws);
+  if (st != PA_OK) return st;
+  if (desc->num_q_tokens == 0) return PA_OK;
+  if (!qsl || !out || !lse) return PA_ERR_NULL_POINTER;
+  pa::MergeArgs m;
+  m.qsl = qsl;
+  m.hdr = ws.hdr;
+  m.units = ws.units;
+  m.split = ws.split;
+  m.part_o = ws.part_o;
+  m.part_lse = ws.part_lse;
+  m.out = out;
+  m.lse = lse;
+  m.num_q_heads = desc->num_q_heads;
+  m.group = desc->num_q_heads / desc->num_kv_heads;
+  // split units <= slice boundaries (grid); one workgroup per split unit, grid-stride
+  const int mgrid = grid > 0 ? grid : 1;
+  return pa::launch_merge_planned(m, desc->dtype, desc->head_dim, mgrid, stream) == 0 ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_attention(const pa_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_table, const int32_t* seq_lens, const int32_t* qsl, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (!desc) return PA_ERR_NULL_POINTER;
+  const pa_status st = pa_check_desc(desc);
+  if (st != PA_OK) return st;
+  if (desc->num_q_tokens == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !qsl || !out || !lse || !workspace)
+    return PA_ERR_NULL_POINTER;
+  pa_status r = pa_plan(desc, seq_lens, qsl, workspace, workspace_bytes, stream);
+  if (r != PA_OK) return r;
+  r = pa_attention_planned(desc, q, k_pool, v_pool, block_table, seq_lens, qsl, out, lse, workspace,
+                           workspace_bytes, stream);
+  if (r != PA_OK) return r;
+  return pa_merge_planned(desc, qsl, out, lse, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_plan_read(const pa_desc* desc, const void* workspace, size_t workspace_bytes, pa_plan_header* header,
+                       pa_plan_unit* units, int32_t max_units, void* stream) {
+  int grid = 0;
+  Ws ws;
+  if (!header) return PA_ERR_NULL_POINTER;
+  const pa_status st = prepare(desc, const_cast<void*>(workspace), workspace_bytes, &grid, &ws);
+  if (st != PA_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(header, ws.hdr, sizeof(pa_plan_header), hipMemcpyDeviceToHost, s) != hipSuccess) return PA_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return PA_ERR_HIP;
+  int32_t n = header->n_units < max_units ? header->n_units : max_units;
+  if (n > 0 && units) {
+    if (hipMemcpyAsync(units, ws.units, sizeof(pa_plan_unit) * size_t(n), hipMemcpyDeviceToHost, s) != hipSuccess)
+      return PA_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+pa_status pa_gather_kv(const pa_desc* desc, int32_t which, const void* pool, const int32_t* block_table,
+                       const int32_t* seq_lens, int32_t seq, int32_t n_keys, void* dense_out, void* stream) {
+  if (!desc) return PA_ERR_NULL_POINTER;
+  const pa_status st = pa_check_desc(desc);
+  if (st != PA_OK) return st;
+  if (which != 0 && which != 1) return PA_ERR_BAD_SHAPE;
+  if (seq < 0 || seq >= desc->num_seqs || n_keys < 0 || n_keys > desc->max_pages_per_seq * PA_PAGE_SIZE)
+    return PA_ERR_BAD_SHAPE;
+  if (n_keys == 0) return PA_OK;
+  if (!pool || !block_table || !seq_lens || !dense_out) return PA_ERR_NULL_POINTER;
+  return pa::launch_gather(which, desc->dtype, desc->num_kv_heads, desc->head_dim, desc->max_pages_per_seq, pool,
+                           block_table, seq_lens, seq, n_keys, dense_out, stream) == 0
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+pa_status pa_merge(int32_t n_parts, int64_t rows, int32_t head_dim, const float* o_parts, const float* lse_parts,
+                   int32_t out_dtype, void* out, float* lse, void* stream) {
+  if (n_parts < 1 || rows < 0) return PA_ERR_BAD_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (out_dtype != PA_F32 && out_dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (rows == 0) return PA_OK;
+  if (!o_parts || !lse_parts || !out || !lse) return PA_ERR_NULL_POINTER;
+  return pa::launch_merge(n_parts, rows, head_dim, o_parts, lse_parts, out_dtype, out, lse, stream) == 0 ? PA_OK
+                                                                                                        : PA_ERR_HIP;
+}
+
+pa_status pa_validate(const pa_desc* desc, const int32_t* block_table, const int32_t* seq_lens, const int32_t* qsl,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!desc) return PA_ERR_NULL_POINTER;
+  const pa_status st = pa_check_desc(desc);
+  if (st != PA_OK) return st;
+  if (!workspace || !qsl || (desc->num_seqs > 0 && (!block_table || !seq_lens))) return PA_ERR_NULL_POINTER;
+  if (workspace_bytes < 256) return PA_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int32_t* flag = static_cast<int32_t*>(workspace);
+  if (hipMemsetAsync(flag, 0, sizeof(int32_t), s) != hipSuccess) return PA_ERR_HIP;
+  if (pa::launch_validate(*desc, block_table, seq_lens, qsl, flag, stream) != 0) return PA_ERR_HIP;
+  int32_t host = 0;
+  if (hipMemcpyAsync(&host, flag, sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess) return PA_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return PA_ERR_HIP;
+  return host ? PA_ERR_INVALID_CONTENT : PA_OK;
+}
+
+}  // extern "C"

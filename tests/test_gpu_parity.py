@@ -1,0 +1,259 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.  Tolerances: float32 inputs 1e-5 max-abs; bf16 inputs
+2e-2 max-abs and 2e-3 mean-abs (fp32 accumulation), for both out and lse.
+Indexing outputs (gather, plan coverage) are compared bit-exactly."""
+import bisect
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_cache_gqa_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU-only container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import paged_kv_cache_gqa_amd as pa  # noqa: E402
+
+TOL = {"f32": (1e-5, 1e-5), "bf16": (2e-2, 2e-3)}
+
+
+def run_gpu(w, **kw):
+    t = pa.to_device(w)
+    out, lse = pa.attention(t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                            t["query_start_loc"], w.scale, **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def check(w, out, lse, ref=None, rows=None):
+    ref_o, ref_l = ref if ref is not None else oracle.attention_workload(w)
+    o = out.float().cpu().numpy()
+    l = lse.cpu().numpy()
+    if rows is not None:
+        o, l = o[rows], l[rows]
+    mx, mean = TOL[w.dtype]
+    eo, el = np.abs(o - ref_o), np.abs(l - ref_l)
+    msg = (f"{w.name}: max|dout|={eo.max() if eo.size else 0:.3e} mean={eo.mean() if eo.size else 0:.3e} "
+           f"max|dlse|={el.max() if el.size else 0:.3e} mean={el.mean() if el.size else 0:.3e}")
+    print(msg, flush=True)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l)), msg
+    if eo.size:
+        assert eo.max() <= mx and el.max() <= mx, msg
+        if w.dtype == "bf16":
+            assert eo.mean() <= mean and el.mean() <= mean, msg
+
+
+# ---------------------------------------------------------------------------
+# small shapes: several tiles, ragged tails, windows, both dtypes and head dims
+# ---------------------------------------------------------------------------
+SMALL = [
+    # seed, B, max_len, Hq, Hkv, D, dtype, max_q
+    (1, 5, 100, 8, 2, 64, "f32", 1),
+    (2, 7, 300, 8, 2, 128, "bf16", 1),
+    (3, 6, 257, 32, 8, 128, "bf16", 5),
+    (4, 4, 700, 8, 1, 128, "bf16", 200),
+    (5, 9, 90, 4, 4, 64, "bf16", 3),
+    (6, 3, 520, 16, 1, 64, "f32", 40),
+    (7, 5, 1200, 64, 8, 128, "bf16", 1),
+    (8, 4, 400, 64, 1, 128, "bf16", 2),
+    (9, 6, 333, 8, 2, 128, "f32", 17),
+    (10, 8, 64, 12, 3, 64, "bf16", 64),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"s{c[0]}-{c[6]}-D{c[5]}-G{c[3] // c[4]}-q{c[7]}" for c in SMALL])
+def test_small_random(case):
+    seed, B, maxlen, Hq, Hkv, D, dt, maxq = case
+    w = W.make_random(seed, B, maxlen, Hq, Hkv, D, dt, max_q=maxq)
+    out, lse = run_gpu(w)
+    check(w, out, lse)
+
+
+def test_config1_tiny_decode_f32():
+    w = W.make_config(1)
+    out, lse = run_gpu(w)
+    check(w, out, lse)
+
+
+@pytest.mark.parametrize("c", [2, 3, 4])
+def test_full_config(c):
+    w = W.make_config(c)
+    out, lse = run_gpu(w)
+    check(w, out, lse)
+
+
+def test_config5_sampled_sequences():
+    """Full-size long-context batch on the GPU; the oracle recomputes a sample of whole sequences."""
+    w = W.make_config(5)
+    out, lse = run_gpu(w)
+    n = w.seq_lens
+    order = np.argsort(n)
+    pick = sorted(set(order[:3].tolist() + order[-4:].tolist() + list(range(0, 256, 37))))
+    sub = W.subset(w, pick)
+    ref = oracle.attention_workload(sub)
+    rows = np.concatenate([np.arange(w.query_start_loc[s], w.query_start_loc[s + 1]) for s in pick])
+    check(sub, out, lse, ref=ref, rows=rows)
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+def test_edge_lengths_and_empty_windows():
+    # n = 1, n = 16, 17, 31, 32, 33 (page and chunk boundaries), zero-query sequences, a full prefill (q = n)
+    n = [1, 16, 17, 31, 32, 33, 48, 5, 64, 97]
+    q = [1, 1, 0, 3, 32, 1, 0, 5, 64, 1]
+    for dt, D in (("bf16", 128), ("f32", 64), ("bf16", 64)):
+        w = W.build(f"edges-{dt}-{D}", 42, n, q, 8, 2, D, dt, num_pages=40)
+        out, lse = run_gpu(w)
+        check(w, out, lse)
+
+
+def test_empty_batch():
+    w = W.build("empty", 3, [5, 9], [0, 0], 8, 2, 128, "bf16", num_pages=4)
+    out, lse = run_gpu(w)
+    assert out.shape == (0, 8, 128)
+
+
+def test_single_long_sequence_max_length():
+    w = W.build("long", 5, [32768], [1], 64, 8, 128, "bf16", num_pages=2048)
+    out, lse = run_gpu(w)
+    check(w, out, lse)
+
+
+# ---------------------------------------------------------------------------
+# invariants of the GPU result
+# ---------------------------------------------------------------------------
+def _poison(w):
+    import oracle_pins as P
+    return P.poison_unused(w)
+
+
+def _permute(w, seed):
+    import oracle_pins as P
+    return P.permute_pages(w, seed)
+
+
+@pytest.mark.parametrize("case", [(21, 6, 300, 32, 8, 128, "bf16", 5), (22, 3, 600, 8, 1, 128, "bf16", 100),
+                                  (23, 5, 200, 8, 2, 64, "f32", 3)])
+def test_bitwise_invariance_poison_permutation(case):
+    seed, B, maxlen, Hq, Hkv, D, dt, maxq = case
+    w = W.make_random(seed, B, maxlen, Hq, Hkv, D, dt, max_q=maxq, slack_pages=5)
+    o1, l1 = run_gpu(w)
+    o2, l2 = run_gpu(_poison(w))
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "NaN in unused slots reached the result"
+    o3, l3 = run_gpu(_permute(w, 9))
+    assert torch.equal(o1, o3) and torch.equal(l1, l3), "physical page placement changed the result"
+
+
+def test_deterministic_and_staged_equals_one_shot():
+    w = W.make_config(3)
+    t = pa.to_device(w)
+    o1, l1 = run_gpu(w)
+    o2, l2 = run_gpu(w)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    desc = pa.make_desc(t["q"], t["k_pool"], t["block_table"], t["seq_lens"], w.scale)
+    ws = pa.alloc_workspace(desc)
+    out = torch.empty_like(t["q"])
+    lse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device="cuda")
+    pa.plan(desc, t["seq_lens"], t["query_start_loc"], ws)
+    pa.attention_planned(desc, t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                         t["query_start_loc"], out, lse, ws)
+    pa.merge_planned(desc, t["query_start_loc"], out, lse, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, out) and torch.equal(l1, lse)
+
+
+# ---------------------------------------------------------------------------
+# integer / indexing outputs (bit-exact)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("f32", 64)])
+def test_gather_kv_bit_exact(dt, D):
+    w = W.make_random(31, 4, 200, 8, 2, D, dt, max_q=2)
+    t = pa.to_device(w)
+    desc = pa.make_desc(t["q"], t["k_pool"], t["block_table"], t["seq_lens"], w.scale)
+    for s in range(w.num_seqs):
+        n = int(w.seq_lens[s])
+        for which, pool, key in ((0, t["k_pool"], "k"), (1, t["v_pool"], "v")):
+            nk = min(n + 3, w.max_pages_per_seq * 16)
+            g = pa.gather_kv(desc, which, pool, t["block_table"], t["seq_lens"], s, nk)
+            ref = oracle.gather(w.k_pool if key == "k" else w.v_pool, w.block_table, w.seq_lens, s, key)
+            got = g.cpu()
+            got = got.view(torch.int16).numpy().view(np.uint16) if dt == "bf16" else got.numpy()
+            assert got[:, :n].tobytes() == np.ascontiguousarray(ref).tobytes()
+            assert not np.any(got[:, n:].view(np.uint8))  # keys past the end are zero bits
+
+
+def test_plan_covers_every_row_and_chunk_once():
+    for c in (2, 3, 4):
+        w = W.make_config(c)
+        t = pa.to_device(w)
+        desc = pa.make_desc(t["q"], t["k_pool"], t["block_table"], t["seq_lens"], w.scale)
+        ws = pa.alloc_workspace(desc)
+        pa.plan(desc, t["seq_lens"], t["query_start_loc"], ws)
+        hdr, units = pa.plan_read(desc, ws)
+        G = w.num_q_heads // w.num_kv_heads
+        ql = w.q_lens()
+        # rows: every (sequence, kv head, window row) exactly once
+        seen = set()
+        cost = 0
+        for u in units:
+            assert u["cost0"] == cost
+            cost += u["n_chunks"] * u["cost_weight"]
+            for r in range(u["row0"], u["row0"] + u["n_rows"]):
+                key = (u["seq"], u["kv_head"], r)
+                assert key not in seen
+                seen.add(key)
+            n = int(w.seq_lens[u["seq"]])
+            last_tok = (u["row0"] + u["n_rows"] - 1) // G
+            assert u["n_keys"] == n - int(ql[u["seq"]]) + last_tok + 1  # causal tile skip
+            assert u["n_chunks"] == math.ceil(u["n_keys"] / 32)
+        assert len(seen) == int((ql * G).sum()) * w.num_kv_heads
+        assert cost == hdr["total_cost"]
+        # slices: the chunks of every unit split into contiguous pieces, one per slice boundary crossed
+        S, C = hdr["n_slots"], hdr["total_cost"]
+        assert 1 <= S <= hdr["grid"]
+        bounds = [k * C // S for k in range(S + 1)]
+        slot_of = lambda x: bisect.bisect_right(bounds, x) - 1  # noqa: E731
+        split_rows = 0
+        for u in units:
+            owners = [slot_of(u["cost0"] + i * u["cost_weight"]) for i in range(u["n_chunks"])]
+            distinct = sorted(set(owners))
+            assert distinct == list(range(distinct[0], distinct[-1] + 1))
+            assert u["n_pieces"] == len(distinct)
+            if u["n_pieces"] > 1:
+                assert u["piece_base"] == split_rows
+                split_rows += u["n_pieces"] * u["n_rows"]
+        assert split_rows == hdr["partial_rows"]
+
+
+def test_validate_reports_bad_content():
+    w = W.make_random(41, 5, 100, 8, 2, 64, "bf16", max_q=3)
+    t = pa.to_device(w)
+    desc = pa.make_desc(t["q"], t["k_pool"], t["block_table"], t["seq_lens"], w.scale)
+    ws = pa.alloc_workspace(desc)
+    assert pa.validate(desc, t["block_table"], t["seq_lens"], t["query_start_loc"], ws) == 0
+    bad = t["block_table"].clone()
+    bad[1, 0] = w.num_pages
+    assert pa.validate(desc, bad, t["seq_lens"], t["query_start_loc"], ws) == 6
+    sl = t["seq_lens"].clone()
+    sl[2] = 0 if int(w.q_lens()[2]) > 0 else -1
+    assert pa.validate(desc, t["block_table"], sl, t["query_start_loc"], ws) == 6
+
+
+def test_merge_op_against_oracle_merge():
+    rng = np.random.default_rng(5)
+    for D in (64, 128):
+        P_, rows = 5, 77
+        o = rng.standard_normal((P_, rows, D)).astype(np.float32)
+        l = (rng.standard_normal((P_, rows)) * 3).astype(np.float32)
+        l[1, :10] = -np.inf
+        ro, rl = oracle.merge(o.astype(np.float64), l.astype(np.float64))
+        go, gl = pa.merge(torch.from_numpy(o).cuda(), torch.from_numpy(l).cuda())
+        torch.cuda.synchronize()
+        assert np.abs(go.cpu().numpy() - ro).max() <= 1e-5
+        assert np.abs(gl.cpu().numpy() - rl).max() <= 1e-5
