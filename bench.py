@@ -1,0 +1,208 @@
+"""Benchmark of paged-KV GQA attention on one MI355X.
+
+A step is one full pass of the path over one batch: pa_plan (work list),
+pa_attention_planned (the persistent attention kernel) and pa_merge_planned
+(log-sum-exp merge of key-split rows) -- exactly what pa_attention enqueues.
+Inputs are resident in HBM before the timed region.  The K/V pools are held in
+several copies and step i reads copy i % n_copies, so that every step's K/V
+were last touched more than 1 GiB of traffic earlier (the 256 MB MALL cannot
+serve them); no flush kernel runs inside the timed region.
+
+Default workload: Llama-3-8B-shaped decode (64 sequences, context uniform in
+[512, 4096], 32 query / 8 KV heads, head dim 128, bf16, 16-slot pages).
+`value` is algorithmic bytes (every valid K/V row once per KV head, Q, out,
+LSE, block-table entries) divided by the wall time per step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6  # dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+FP32_PEAK_TFLOPS = 157.3
+METRIC = "decode KV-read HBM GB/s (% of peak) + prefill/verify TFLOP/s, 1 MI355X"
+KERNEL_SOURCES = ["paged_kv_cache_gqa_amd/csrc/pa_kernels.hip", "paged_kv_cache_gqa_amd/csrc/pa_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_kernel_hbm_traffic.json")
+
+DESCRIPTIONS = {
+    1: dict(batch=4, q_heads=8, kv_heads=2, head_dim=64, context="{17,64,100,256}", queries_per_seq="1"),
+    2: dict(batch=64, q_heads=32, kv_heads=8, head_dim=128, context="uniform[512,4096]", queries_per_seq="1"),
+    3: dict(batch=132, q_heads=8, kv_heads=1, head_dim=128,
+            context="4 x (prior uniform[0,2048] + 512 new) + 128 x uniform[1024,8192]",
+            queries_per_seq="512 (4 prefill chunks) / 1 (128 decodes)"),
+    4: dict(batch=32, q_heads=32, kv_heads=8, head_dim=128, context="prior uniform[2048,16384] + 5",
+            queries_per_seq="5"),
+    5: dict(batch=256, q_heads=64, kv_heads=8, head_dim=128, context="lognormal(median 8192, sigma 1) in [1024,32768]",
+            queries_per_seq="1"),
+}
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the attention kernel from the committed counter runs,
+    or None when the counters were taken on other kernel sources or another workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get("workloads", {}).get(workload)
+    if not entry or entry.get("kernel_sha") != kernel_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, alg_bytes: int, min_seconds: float = 10.0, max_runs: int = 5):
+    """The oracle (plain fp64 C, OpenMP) on the host cores over the whole batch."""
+    import oracle
+    oracle.attention_workload(w)  # warm (and build) once, untimed
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < max_runs and (len(times) < 1 or time.perf_counter() - t_start < min_seconds):
+        t0 = time.perf_counter()
+        oracle.attention_workload(w)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {"value": round(alg_bytes / t / 1e9, 4), "unit": "GB/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"the whole batch (all sequences, all heads), median of {len(times)} runs of "
+                      f"{t:.3f} s each; fp64 two-pass softmax"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (for HBM counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported: "
+              "the attention call shards by KV head with no exchange, so N GPUs run N independent copies.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_gqa_amd as pa
+    from paged_kv_cache_gqa_amd import binding as B
+    from paged_kv_cache_gqa_amd import workloads as W
+
+    torch.cuda.set_device(0)
+    w = W.make_config(args.config)
+    alg_bytes = w.algorithmic_bytes()
+    alg_flops = w.algorithmic_flops()
+    t = pa.to_device(w)
+    kv_bytes = t["k_pool"].numel() * t["k_pool"].element_size() * 2
+    n_copies = max(1, min(8, int(np.ceil(3 * 256e6 / kv_bytes)) + 1)) if kv_bytes < 2e9 else 1
+    pools = [(t["k_pool"], t["v_pool"])] + [(t["k_pool"].clone(), t["v_pool"].clone()) for _ in range(n_copies - 1)]
+    desc = pa.make_desc(t["q"], t["k_pool"], t["block_table"], t["seq_lens"], w.scale)
+    ws = pa.alloc_workspace(desc)
+    out = torch.empty_like(t["q"])
+    lse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    # pre-marshalled arguments: the host enqueues three calls per step
+    L = B.lib()
+    import ctypes
+    dref = ctypes.byref(desc)
+    vp = ctypes.c_void_p
+    sp = vp(stream.cuda_stream)
+    wsn = ws.numel()
+    plan_args = (dref, vp(t["seq_lens"].data_ptr()), vp(t["query_start_loc"].data_ptr()), vp(ws.data_ptr()), wsn, sp)
+    attn_args = [(dref, vp(t["q"].data_ptr()), vp(k.data_ptr()), vp(v.data_ptr()), vp(t["block_table"].data_ptr()),
+                  vp(t["seq_lens"].data_ptr()), vp(t["query_start_loc"].data_ptr()), vp(out.data_ptr()),
+                  vp(lse.data_ptr()), vp(ws.data_ptr()), wsn, sp) for k, v in pools]
+    merge_args = (dref, vp(t["query_start_loc"].data_ptr()), vp(out.data_ptr()), vp(lse.data_ptr()),
+                  vp(ws.data_ptr()), wsn, sp)
+
+    def step(i, ev=None):
+        rc = L.pa_plan(*plan_args)
+        if ev is not None:
+            ev[0].record(stream)
+        rc |= L.pa_attention_planned(*attn_args[i % n_copies])
+        if ev is not None:
+            ev[1].record(stream)
+        rc |= L.pa_merge_planned(*merge_args)
+        if rc:
+            raise RuntimeError(f"launch failed: {B.status_string(rc)}")
+
+    print(f"[bench] {w.name}: B={w.num_seqs} T_q={w.num_q_tokens} pages={w.num_pages} copies={n_copies} "
+          f"alg_bytes={alg_bytes / 1e6:.1f} MB alg_flops={alg_flops / 1e9:.2f} GF", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in events]
+    attn_mean = statistics.fmean(attn_ms)
+
+    if args.copy_calibration:  # a plain copy of known size, for scaling the HBM counters
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    # correctness spot check of the timed result (outputs are the same for every pool copy)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+
+    value = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = alg_bytes / (attn_mean * 1e-3) / 1e9
+    tflops = alg_flops / (ms_per_step * 1e-3) / 1e12
+    peak_tf = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+    config = {"workload": f"{w.name} (configuration {args.config})", **DESCRIPTIONS[args.config],
+              "page_size": 16, "seed": 1000 + args.config, "kv_pool_copies": n_copies,
+              "algorithmic_bytes": alg_bytes, "algorithmic_flops": alg_flops}
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded; shapes of the named configuration)",
+        "config": config,
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "tflops": round(tflops, 3), "frac_of_mfma_peak": round(tflops / peak_tf, 5),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
+                     "kernel": "pa::attention_kernel", "kernel_ms_mean": round(attn_mean, 5),
+                     "kernel_ms_p10_p90": [round(float(np.percentile(attn_ms, 10)), 5),
+                                           round(float(np.percentile(attn_ms, 90)), 5)],
+                     "per_launch": "algorithmic bytes of the whole batch (one launch covers the batch)"},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, alg_bytes)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
