@@ -92,6 +92,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--part", default="all", choices=["all", "prefill", "decode"],
+                    help="configuration 3 only: time its prefill chunks or its decode rows alone")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for HBM counter calibration)")
@@ -113,6 +115,11 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     w = W.make_config(args.config)
+    if args.part != "all":
+        ql = w.q_lens()
+        keep = np.nonzero(ql > 1 if args.part == "prefill" else ql == 1)[0]
+        w = W.subset(w, keep)
+        w.name = f"{W.CONFIG_NAMES[args.config]}-{args.part}-part"
     alg_bytes = w.algorithmic_bytes()
     alg_flops = w.algorithmic_flops()
     t = pa.to_device(w)
@@ -136,8 +143,8 @@ def main() -> int:
     attn_args = [(dref, vp(t["q"].data_ptr()), vp(k.data_ptr()), vp(v.data_ptr()), vp(t["block_table"].data_ptr()),
                   vp(t["seq_lens"].data_ptr()), vp(t["query_start_loc"].data_ptr()), vp(out.data_ptr()),
                   vp(lse.data_ptr()), vp(ws.data_ptr()), wsn, sp) for k, v in pools]
-    merge_args = (dref, vp(t["query_start_loc"].data_ptr()), vp(out.data_ptr()), vp(lse.data_ptr()),
-                  vp(ws.data_ptr()), wsn, sp)
+    merge_args = (dref, vp(t["seq_lens"].data_ptr()), vp(t["query_start_loc"].data_ptr()), vp(out.data_ptr()),
+                  vp(lse.data_ptr()), vp(ws.data_ptr()), wsn, sp)
 
     def step(i, ev=None):
         rc = L.pa_plan(*plan_args)
@@ -182,6 +189,7 @@ def main() -> int:
     tflops = alg_flops / (ms_per_step * 1e-3) / 1e12
     peak_tf = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
     config = {"workload": f"{w.name} (configuration {args.config})", **DESCRIPTIONS[args.config],
+              "part": args.part,
               "page_size": 16, "seed": 1000 + args.config, "kv_pool_copies": n_copies,
               "algorithmic_bytes": alg_bytes, "algorithmic_flops": alg_flops}
     line = {

@@ -103,8 +103,9 @@ pa_status pa_check_desc(const pa_desc* desc);
 
 /*
  * Bytes of device workspace pa_attention needs for `desc` on the current HIP
- * device (the plan, the work list and the split-key partial results).  The
- * size depends only on the descriptor and on the device's compute-unit count.
+ * device (the per-sequence cost prefix and, per workgroup of the persistent
+ * launch, room for two partial results of up to 128 rows).  The size depends
+ * only on the descriptor and on the device's compute-unit count.
  * Writes *bytes; returns PA_ERR_NULL_POINTER, a descriptor error or PA_ERR_HIP.
  */
 pa_status pa_workspace_size(const pa_desc* desc, size_t* bytes);
@@ -126,7 +127,7 @@ pa_status pa_attention(const pa_desc* desc, const void* q, const void* k_pool, c
 
 /*
  * The three stages of pa_attention, for callers that time or reuse them.
- * pa_plan writes the work list into the workspace (it reads only seq_lens and
+ * pa_plan writes the plan into the workspace (it reads only seq_lens and
  * query_start_loc; a plan stays valid while those and desc are unchanged).
  * pa_attention_planned runs the attention kernel on a planned workspace:
  * unsplit rows get their final out/lse, split rows leave partial results in
@@ -139,39 +140,45 @@ pa_status pa_attention_planned(const pa_desc* desc, const void* q, const void* k
                                const void* v_pool, const int32_t* block_table,
                                const int32_t* seq_lens, const int32_t* query_start_loc, void* out,
                                float* lse, void* workspace, size_t workspace_bytes, void* stream);
-pa_status pa_merge_planned(const pa_desc* desc, const int32_t* query_start_loc, void* out, float* lse,
-                           void* workspace, size_t workspace_bytes, void* stream);
+pa_status pa_merge_planned(const pa_desc* desc, const int32_t* seq_lens, const int32_t* query_start_loc,
+                           void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Plan inspection (debug / tests).  A plan is a list of work units; unit u
- * covers query rows [row0, row0 + n_rows) of sequence `seq` for K/V head
+ * Plan inspection (debug / tests).  The planner (pa_plan) writes only the
+ * per-sequence cost prefix; work units are derived from it on the fly.  Unit
+ * u covers query rows [row0, row0 + n_rows) of sequence `seq` for K/V head
  * `kv_head` (row index = window token * (Hq/Hkv) + head within the group)
  * against keys [0, n_keys), cut into ceil(n_keys / 32) chunks of 32 keys.
- * Units are laid out on one cost axis (cost0 = prefix of n_chunks * cost
- * weight); the persistent launch's workgroup k takes the chunks whose start
- * lies in [floor(k*C/S), floor((k+1)*C/S)), C = total cost, S = n_slots.
- * kind 0: rows <= 32, the four waves of a workgroup split the chunks;
- * kind 1: rows <= 128, each wave takes 32 rows and the chunks are shared.
- * n_pieces > 1 means the unit's keys were split between workgroups and merged.
+ * Units lie on one cost axis in (sequence, kv head, row block) order (cost0 =
+ * prefix of n_chunks * cost_weight); the persistent launch's workgroup k takes
+ * the chunks whose start lies in [floor(k*C/S), floor((k+1)*C/S)), C =
+ * total_cost, S = n_slots.  kind 0: rows <= 32, the four waves of a workgroup
+ * split the chunks; kind 1: rows <= 128, each wave takes 32 rows and the
+ * chunks are shared.  n_pieces > 1 means the unit's chunks fall into slots
+ * first_slot .. first_slot + n_pieces - 1 and their partial results are merged.
  */
 typedef struct pa_plan_unit {
   int32_t seq, kv_head, row0, n_rows;
   int32_t n_keys, n_chunks, kind, cost_weight;
   int64_t cost0;
-  int32_t piece_base, n_pieces;
+  int32_t first_slot, n_pieces;
 } pa_plan_unit;
 
 typedef struct pa_plan_header {
-  int32_t n_units, n_split, n_slots, grid;
-  int64_t total_cost, partial_rows;
+  int32_t n_units, n_slots, grid, num_seqs;
+  int64_t total_cost;
+  int32_t grains_per_workgroup; /* n_slots = max(1, min(grid * this, total_cost / 5)) */
+  int32_t reserved;
 } pa_plan_header;
 
 /*
- * Copy the plan held in `workspace` to host memory: *header, and up to
- * max_units units.  Synchronizes `stream`.
+ * Enumerate the plan held in `workspace` (after pa_plan) and copy it to host
+ * memory: *header, and the first min(n_units, max_units) units into `units`
+ * (host memory; may be NULL when max_units is 0).  Synchronizes `stream`.
  */
-pa_status pa_plan_read(const pa_desc* desc, const void* workspace, size_t workspace_bytes,
-                       pa_plan_header* header, pa_plan_unit* units, int32_t max_units, void* stream);
+pa_status pa_plan_read(const pa_desc* desc, const int32_t* seq_lens, const int32_t* query_start_loc,
+                       void* workspace, size_t workspace_bytes, pa_plan_header* header, pa_plan_unit* units,
+                       int32_t max_units, void* stream);
 
 /*
  * Gather keys [0, n_keys) of sequence `seq` from one pool into dense

@@ -40,12 +40,13 @@ class PlanUnit(ctypes.Structure):
     _fields_ = [("seq", ctypes.c_int32), ("kv_head", ctypes.c_int32), ("row0", ctypes.c_int32),
                 ("n_rows", ctypes.c_int32), ("n_keys", ctypes.c_int32), ("n_chunks", ctypes.c_int32),
                 ("kind", ctypes.c_int32), ("cost_weight", ctypes.c_int32), ("cost0", ctypes.c_int64),
-                ("piece_base", ctypes.c_int32), ("n_pieces", ctypes.c_int32)]
+                ("first_slot", ctypes.c_int32), ("n_pieces", ctypes.c_int32)]
 
 
 class PlanHeader(ctypes.Structure):
-    _fields_ = [("n_units", ctypes.c_int32), ("n_split", ctypes.c_int32), ("n_slots", ctypes.c_int32),
-                ("grid", ctypes.c_int32), ("total_cost", ctypes.c_int64), ("partial_rows", ctypes.c_int64)]
+    _fields_ = [("n_units", ctypes.c_int32), ("n_slots", ctypes.c_int32), ("grid", ctypes.c_int32),
+                ("num_seqs", ctypes.c_int32), ("total_cost", ctypes.c_int64), ("grains_per_workgroup", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _lib = None
@@ -72,8 +73,9 @@ def lib():
         L.pa_attention.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.pa_plan.argtypes = [dp, vp, vp, vp, sz, vp]
         L.pa_attention_planned.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        L.pa_merge_planned.argtypes = [dp, vp, vp, vp, vp, sz, vp]
-        L.pa_plan_read.argtypes = [dp, vp, sz, ctypes.POINTER(PlanHeader), ctypes.POINTER(PlanUnit), i32, vp]
+        L.pa_merge_planned.argtypes = [dp, vp, vp, vp, vp, vp, sz, vp]
+        L.pa_plan_read.argtypes = [dp, vp, vp, vp, sz, ctypes.POINTER(PlanHeader), ctypes.POINTER(PlanUnit), i32,
+                                   vp]
         L.pa_gather_kv.argtypes = [dp, i32, vp, vp, vp, i32, i32, vp, vp]
         L.pa_merge.argtypes = [i32, i64, i32, vp, vp, i32, vp, vp, vp]
         L.pa_validate.argtypes = [dp, vp, vp, vp, vp, sz, vp]
@@ -186,17 +188,19 @@ def attention_planned(desc: PaDesc, q, k_pool, v_pool, block_table, seq_lens, qu
                                       workspace.numel(), _stream(stream)))
 
 
-def merge_planned(desc: PaDesc, query_start_loc, out, lse, workspace, stream=None) -> None:
-    _check("pa_merge_planned", lib().pa_merge_planned(ctypes.byref(desc), _ptr(query_start_loc), _ptr(out), _ptr(lse),
-                                                      _ptr(workspace), workspace.numel(), _stream(stream)))
+def merge_planned(desc: PaDesc, seq_lens, query_start_loc, out, lse, workspace, stream=None) -> None:
+    _check("pa_merge_planned", lib().pa_merge_planned(ctypes.byref(desc), _ptr(seq_lens), _ptr(query_start_loc),
+                                                      _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                                      _stream(stream)))
 
 
-def plan_read(desc: PaDesc, workspace, max_units: int = 1 << 20, stream=None):
+def plan_read(desc: PaDesc, seq_lens, query_start_loc, workspace, max_units: int = 1 << 20, stream=None):
     """(header dict, list of unit dicts) of the plan in `workspace` (synchronizes)."""
     hdr = PlanHeader()
     units = (PlanUnit * max(1, max_units))()
-    _check("pa_plan_read", lib().pa_plan_read(ctypes.byref(desc), _ptr(workspace), workspace.numel(),
-                                              ctypes.byref(hdr), units, max_units, _stream(stream)))
+    _check("pa_plan_read", lib().pa_plan_read(ctypes.byref(desc), _ptr(seq_lens), _ptr(query_start_loc),
+                                              _ptr(workspace), workspace.numel(), ctypes.byref(hdr), units,
+                                              max_units, _stream(stream)))
     h = {f: getattr(hdr, f) for f, _ in PlanHeader._fields_}
     n = min(h["n_units"], max_units)
     us = [{f: getattr(units[i], f) for f, _ in PlanUnit._fields_} for i in range(n)]

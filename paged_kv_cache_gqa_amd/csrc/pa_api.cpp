@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 
 #include "pa_internal.h"
@@ -13,7 +14,7 @@ namespace {
 using pa::WsLayout;
 
 struct DeviceInfo {
-  bool ready = false;
+  std::atomic<bool> ready{false};
   int cus = 0;
   int blocks_per_cu[2][2] = {{0, 0}, {0, 0}};  // [dtype][D == 128]
 };
@@ -26,9 +27,13 @@ DeviceInfo g_dev[kMaxDevices];
 pa_status device_grid(const pa_desc& d, int* grid) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_ERR_HIP;
-  std::lock_guard<std::mutex> lock(g_mu);
   DeviceInfo& info = g_dev[dev];
-  if (!info.ready) {
+  if (info.ready.load(std::memory_order_acquire)) {
+    *grid = info.cus * info.blocks_per_cu[d.dtype == PA_BF16 ? 1 : 0][d.head_dim == 128 ? 1 : 0];
+    return PA_OK;
+  }
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!info.ready.load(std::memory_order_relaxed)) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       return PA_ERR_HIP;
@@ -39,7 +44,7 @@ pa_status device_grid(const pa_desc& d, int* grid) {
         info.blocks_per_cu[dt][big] = n;
       }
     info.cus = cus;
-    info.ready = true;
+    info.ready.store(true, std::memory_order_release);
   }
   *grid = info.cus * info.blocks_per_cu[d.dtype == PA_BF16 ? 1 : 0][d.head_dim == 128 ? 1 : 0];
   return PA_OK;
@@ -48,12 +53,12 @@ pa_status device_grid(const pa_desc& d, int* grid) {
 struct Ws {
   WsLayout L;
   pa_plan_header* hdr;
+  int32_t* grab;
   int64_t* seq_cost;
-  int32_t* seq_unit;
-  pa_plan_unit* units;
-  int32_t* split;
+  pa::SlotStart* slots;
   float* part_lse;
   float* part_o;
+  pa_plan_unit* units;
 };
 
 Ws carve(void* base, const WsLayout& L) {
@@ -61,12 +66,12 @@ Ws carve(void* base, const WsLayout& L) {
   Ws w;
   w.L = L;
   w.hdr = reinterpret_cast<pa_plan_header*>(b + L.header);
+  w.grab = reinterpret_cast<int32_t*>(b + L.grab);
   w.seq_cost = reinterpret_cast<int64_t*>(b + L.seq_cost);
-  w.seq_unit = reinterpret_cast<int32_t*>(b + L.seq_unit);
-  w.units = reinterpret_cast<pa_plan_unit*>(b + L.units);
-  w.split = reinterpret_cast<int32_t*>(b + L.split);
+  w.slots = reinterpret_cast<pa::SlotStart*>(b + L.slots);
   w.part_lse = reinterpret_cast<float*>(b + L.part_lse);
   w.part_o = reinterpret_cast<float*>(b + L.part_o);
+  w.units = reinterpret_cast<pa_plan_unit*>(b + L.units);
   return w;
 }
 
@@ -85,26 +90,36 @@ pa_status prepare(const pa_desc* desc, void* workspace, size_t workspace_bytes, 
   return PA_OK;
 }
 
+pa::PlanView plan_view(const pa_desc& d, const int32_t* seq_lens, const int32_t* qsl, const Ws& ws) {
+  pa::PlanView v;
+  v.seq_lens = seq_lens;
+  v.qsl = qsl;
+  v.hdr = ws.hdr;
+  v.seq_cost = ws.seq_cost;
+  v.slots = ws.slots;
+  v.num_seqs = d.num_seqs;
+  v.num_kv_heads = d.num_kv_heads;
+  v.group = d.num_q_heads / d.num_kv_heads;
+  return v;
+}
+
 pa::AttnArgs attn_args(const pa_desc& d, const void* q, const void* k, const void* v, const int32_t* bt,
                        const int32_t* sl, const int32_t* qsl, void* out, float* lse, const Ws& ws) {
   pa::AttnArgs a;
+  a.plan = plan_view(d, sl, qsl, ws);
   a.q = q;
   a.k_pool = k;
   a.v_pool = v;
   a.block_table = bt;
-  a.seq_lens = sl;
-  a.qsl = qsl;
   a.out = out;
   a.lse = lse;
-  a.hdr = ws.hdr;
-  a.units = ws.units;
   a.part_o = ws.part_o;
   a.part_lse = ws.part_lse;
+  a.grab = ws.grab;
   a.num_q_heads = d.num_q_heads;
-  a.num_kv_heads = d.num_kv_heads;
-  a.group = d.num_q_heads / d.num_kv_heads;
   a.max_pages = d.max_pages_per_seq;
-  a.scale_log2 = d.scale * 1.44269504088896340736f;
+  a.scale_log2 = std::fabs(d.scale) * 1.44269504088896340736f;
+  a.q_sign = d.scale < 0.f ? (d.dtype == PA_BF16 ? 0x80008000u : 0x80000000u) : 0u;
   return a;
 }
 
@@ -164,16 +179,13 @@ pa_status pa_plan(const pa_desc* desc, const int32_t* seq_lens, const int32_t* q
   a.seq_lens = seq_lens;
   a.qsl = qsl;
   a.hdr = ws.hdr;
-  a.units = ws.units;
-  a.split = ws.split;
   a.seq_cost = ws.seq_cost;
-  a.seq_unit = ws.seq_unit;
+  a.slots = ws.slots;
+  a.grab = ws.grab;
   a.num_seqs = desc->num_seqs;
   a.num_kv_heads = desc->num_kv_heads;
   a.group = desc->num_q_heads / desc->num_kv_heads;
   a.grid = grid;
-  a.max_units = ws.L.max_units;
-  a.max_partial_rows = ws.L.max_partial_rows;
   return pa::launch_plan(a, stream) == 0 ? PA_OK : PA_ERR_HIP;
 }
 
@@ -190,28 +202,26 @@ pa_status pa_attention_planned(const pa_desc* desc, const void* q, const void* k
   return pa::launch_attention(a, desc->dtype, desc->head_dim, grid, stream) == 0 ? PA_OK : PA_ERR_HIP;
 }
 
-pa_status pa_merge_planned(const pa_desc* desc, const int32_t* qsl, void* out, float* lse, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+pa_status pa_merge_planned(const pa_desc* desc, const int32_t* seq_lens, const int32_t* qsl, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream) {
   int grid = 0;
   Ws ws;
   const pa_status st = prepare(desc, workspace, workspace_bytes, &grid, &ws);
   if (st != PA_OK) return st;
   if (desc->num_q_tokens == 0) return PA_OK;
-  if (!qsl || !out || !lse) return PA_ERR_NULL_POINTER;
+  if (!seq_lens || !qsl || !out || !lse) return PA_ERR_NULL_POINTER;
   pa::MergeArgs m;
-  m.qsl = qsl;
-  m.hdr = ws.hdr;
-  m.units = ws.units;
-  m.split = ws.split;
+  m.plan = plan_view(*desc, seq_lens, qsl, ws);
+  m.grab = ws.grab;
   m.part_o = ws.part_o;
   m.part_lse = ws.part_lse;
   m.out = out;
   m.lse = lse;
   m.num_q_heads = desc->num_q_heads;
-  m.group = desc->num_q_heads / desc->num_kv_heads;
-  // split units <= slice boundaries (grid); one workgroup per split unit, grid-stride
-  const int mgrid = grid > 0 ? grid : 1;
-  return pa::launch_merge_planned(m, desc->dtype, desc->head_dim, mgrid, stream) == 0 ? PA_OK : PA_ERR_HIP;
+  // one workgroup per grain boundary
+  return pa::launch_merge_planned(m, desc->dtype, desc->head_dim, grid * pa::kGrainsPerWorkgroup, stream) == 0
+             ? PA_OK
+             : PA_ERR_HIP;
 }
 
 pa_status pa_attention(const pa_desc* desc, const void* q, const void* k_pool, const void* v_pool,
@@ -228,21 +238,27 @@ pa_status pa_attention(const pa_desc* desc, const void* q, const void* k_pool, c
   r = pa_attention_planned(desc, q, k_pool, v_pool, block_table, seq_lens, qsl, out, lse, workspace,
                            workspace_bytes, stream);
   if (r != PA_OK) return r;
-  return pa_merge_planned(desc, qsl, out, lse, workspace, workspace_bytes, stream);
+  return pa_merge_planned(desc, seq_lens, qsl, out, lse, workspace, workspace_bytes, stream);
 }
 
-pa_status pa_plan_read(const pa_desc* desc, const void* workspace, size_t workspace_bytes, pa_plan_header* header,
-                       pa_plan_unit* units, int32_t max_units, void* stream) {
+pa_status pa_plan_read(const pa_desc* desc, const int32_t* seq_lens, const int32_t* qsl, void* workspace,
+                       size_t workspace_bytes, pa_plan_header* header, pa_plan_unit* units, int32_t max_units,
+                       void* stream) {
   int grid = 0;
   Ws ws;
   if (!header) return PA_ERR_NULL_POINTER;
-  const pa_status st = prepare(desc, const_cast<void*>(workspace), workspace_bytes, &grid, &ws);
+  if (max_units > 0 && !units) return PA_ERR_NULL_POINTER;
+  const pa_status st = prepare(desc, workspace, workspace_bytes, &grid, &ws);
   if (st != PA_OK) return st;
+  if (desc->num_seqs > 0 && (!seq_lens || !qsl)) return PA_ERR_NULL_POINTER;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (hipMemcpyAsync(header, ws.hdr, sizeof(pa_plan_header), hipMemcpyDeviceToHost, s) != hipSuccess) return PA_ERR_HIP;
   if (hipStreamSynchronize(s) != hipSuccess) return PA_ERR_HIP;
-  int32_t n = header->n_units < max_units ? header->n_units : max_units;
-  if (n > 0 && units) {
+  const int64_t cap = ws.L.max_units;
+  int64_t n = header->n_units < max_units ? header->n_units : max_units;
+  if (n > cap) n = cap;
+  if (n > 0) {
+    if (pa::launch_plan_units(plan_view(*desc, seq_lens, qsl, ws), ws.units, cap, stream) != 0) return PA_ERR_HIP;
     if (hipMemcpyAsync(units, ws.units, sizeof(pa_plan_unit) * size_t(n), hipMemcpyDeviceToHost, s) != hipSuccess)
       return PA_ERR_HIP;
     if (hipStreamSynchronize(s) != hipSuccess) return PA_ERR_HIP;

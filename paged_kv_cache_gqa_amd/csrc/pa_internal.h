@@ -22,66 +22,98 @@ constexpr int kPlanThreads = 1024;
 // from HBM) costs more wall time than a chunk of a row-split unit (prefill: the
 // workgroup reads the chunk once and four waves spend MFMA time on it).
 constexpr int kCostKeySplit = 4;
-constexpr int kCostRowSplit = 1;
+constexpr int kCostRowSplit = 5;
 constexpr int kCostMax = kCostKeySplit > kCostRowSplit ? kCostKeySplit : kCostRowSplit;
+// Fixed cost charged at the start of every unit (row and page-table loads, the
+// pipeline fill), so that slices that start many units get fewer chunks.
+constexpr int kCostUnitStart = 12;
+
+// The cost axis is cut into up to kGrainsPerWorkgroup * grid equal grains.  Grain
+// boundaries (and so every split of a unit's keys and its partial-result slots)
+// are fixed by the plan; which workgroup runs which grain is decided at run time
+// through an atomic counter, so faster workgroups take more grains.
+// bf16 decode: K of a chunk by global->LDS DMA (1) or straight to registers (0)
+#ifndef PA_K_VIA_LDS
+#define PA_K_VIA_LDS 1
+#endif
+#ifndef PA_GRAINS_PER_WORKGROUP
+#define PA_GRAINS_PER_WORKGROUP 1
+#endif
+constexpr int kGrainsPerWorkgroup = PA_GRAINS_PER_WORKGROUP;
+
+// Where grain k starts: its cost range and the unit holding cost c0, as written by the planner.
+struct SlotStart {
+  int64_t c0, c1;
+  int64_t seq_base;    // cost at which sequence s starts
+  int64_t unit_cost0;  // cost at which unit (s, g, rb) starts
+  int32_t s, g, rb;
+  int32_t n, qn;       // seq_lens[s], query count of s
+  int32_t pad[3];
+};
+
+// Arguments shared by the kernels that walk the plan.
+struct PlanView {
+  const int32_t* seq_lens;
+  const int32_t* qsl;
+  const pa_plan_header* hdr;
+  const int64_t* seq_cost;  // [B+1]: cost at which sequence s's units start; seq_cost[B] = total
+  const SlotStart* slots;   // [max grains]
+  int32_t num_seqs;
+  int32_t num_kv_heads;
+  int32_t group;  // Hq / Hkv
+};
 
 struct AttnArgs {
+  PlanView plan;
   const void* q;
   const void* k_pool;
   const void* v_pool;
   const int32_t* block_table;
-  const int32_t* seq_lens;
-  const int32_t* qsl;
   void* out;
   float* lse;
-  const pa_plan_header* hdr;
-  const pa_plan_unit* units;
-  float* part_o;    // [partial rows][D]
-  float* part_lse;  // [partial rows]
+  float* part_o;    // [grains][2][128][D]: per grain, the piece of its first and of its last unit
+  float* part_lse;  // [grains][2][128]
+  int32_t* grab;    // grain counter (zeroed by the planner and by the merge)
   int32_t num_q_heads;
-  int32_t num_kv_heads;
-  int32_t group;  // Hq / Hkv
   int32_t max_pages;
-  float scale_log2;  // scale * log2(e): scores live in the base-2 domain
+  float scale_log2;  // |scale| * log2(e): scores live in the base-2 domain
+  uint32_t q_sign;   // xor applied to Q's bits: the sign bits when scale < 0, else 0
 };
 
 struct PlanArgs {
   const int32_t* seq_lens;
   const int32_t* qsl;
   pa_plan_header* hdr;
-  pa_plan_unit* units;
-  int32_t* split;      // indices of units with n_pieces > 1
-  int64_t* seq_cost;   // per-sequence exclusive cost prefix (scratch)
-  int32_t* seq_unit;   // per-sequence exclusive unit prefix (scratch)
+  int64_t* seq_cost;
+  SlotStart* slots;
   int32_t num_seqs;
   int32_t num_kv_heads;
   int32_t group;
-  int32_t grid;        // workgroups of the persistent attention launch
-  int64_t max_units;         // capacity of `units` / `split`
-  int64_t max_partial_rows;  // capacity of the partial-result arrays
+  int32_t grid;  // workgroups of the persistent attention launch
+  int32_t* grab;
 };
 
 struct MergeArgs {
-  const int32_t* qsl;
-  const pa_plan_header* hdr;
-  const pa_plan_unit* units;
-  const int32_t* split;
+  PlanView plan;
+  int32_t* grab;
   const float* part_o;
   const float* part_lse;
   void* out;
   float* lse;
   int32_t num_q_heads;
-  int32_t group;
 };
 
-// Workspace: [header | seq scratch | units | split list | partial lse | partial o],
-// every region 256-byte aligned.
+// Workspace: [header | grain counter | per-sequence cost prefix | grain starts | partial lse |
+// partial o | unit list (plan inspection only)], every region 256-byte aligned.
 struct WsLayout {
-  size_t header, seq_cost, seq_unit, units, split, part_lse, part_o, total;
-  int64_t max_units, max_partial_rows;
+  size_t header, grab, seq_cost, slots, part_lse, part_o, units, total;
+  int64_t partial_rows, max_units;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Rows of one partial position: the largest unit.
+constexpr int kPartRows = kBlockRows;
 
 inline WsLayout ws_layout(const pa_desc& d, int grid) {
   WsLayout L{};
@@ -90,16 +122,16 @@ inline WsLayout ws_layout(const pa_desc& d, int grid) {
   const int64_t G = d.num_kv_heads > 0 ? d.num_q_heads / d.num_kv_heads : 1;
   // units per sequence = Hkv * (1 if q_len*G <= 32 else ceil(q_len*G/128))
   L.max_units = int64_t(d.num_kv_heads) * (B + (T * G + kBlockRows - 1) / kBlockRows);
-  // every (row, head) once, plus one extra piece of <= 128 rows per slot boundary
-  L.max_partial_rows = T * d.num_q_heads + int64_t(grid) * kBlockRows;
+  const int64_t grains = int64_t(grid) * kGrainsPerWorkgroup;
+  L.partial_rows = grains * 2 * kPartRows;
   size_t off = 0;
   L.header = off;   off += align256(sizeof(pa_plan_header));
+  L.grab = off;     off += 256;
   L.seq_cost = off; off += align256(sizeof(int64_t) * size_t(B + 1));
-  L.seq_unit = off; off += align256(sizeof(int32_t) * size_t(B + 1));
+  L.slots = off;    off += align256(sizeof(SlotStart) * size_t(grains > 0 ? grains : 1));
+  L.part_lse = off; off += align256(sizeof(float) * size_t(L.partial_rows));
+  L.part_o = off;   off += align256(sizeof(float) * size_t(L.partial_rows) * size_t(d.head_dim));
   L.units = off;    off += align256(sizeof(pa_plan_unit) * size_t(L.max_units > 0 ? L.max_units : 1));
-  L.split = off;    off += align256(sizeof(int32_t) * size_t(L.max_units > 0 ? L.max_units : 1));
-  L.part_lse = off; off += align256(sizeof(float) * size_t(L.max_partial_rows));
-  L.part_o = off;   off += align256(sizeof(float) * size_t(L.max_partial_rows) * size_t(d.head_dim));
   L.total = off;
   return L;
 }
@@ -111,6 +143,7 @@ namespace pa {
 int launch_plan(const PlanArgs& a, void* stream);
 int launch_attention(const AttnArgs& a, int dtype, int head_dim, int grid, void* stream);
 int launch_merge_planned(const MergeArgs& a, int dtype, int head_dim, int grid, void* stream);
+int launch_plan_units(const PlanView& v, pa_plan_unit* units, int64_t max_units, void* stream);
 int launch_gather(int which, int dtype, int Hkv, int D, int max_pages, const void* pool,
                   const int32_t* block_table, const int32_t* seq_lens, int seq, int n_keys, void* dense,
                   void* stream);

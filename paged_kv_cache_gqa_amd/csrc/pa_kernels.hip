@@ -13,29 +13,28 @@
 // Design for CDNA4 (what differs from the Ascend design on the XY-Serve page):
 //  * A chunk is 32 keys = two 16-slot pages.  QK^T runs as S^T = K . Q^T on
 //    v_mfma_f32_16x16x32_bf16 (16 keys x 16 query rows per MFMA, D in steps of
-//    32) and PV as O^T = V^T . P^T (16 d x 16 rows, 32 keys per MFMA).  Every
-//    MFMA operand is one 16-byte load per lane straight from the pool: K pages
+//    32) and PV as O^T = V^T . P^T (16 d x 16 rows, 32 keys per MFMA).  K pages
 //    are [slot][D], V pages are stored [D][slot] so the key axis that PV reduces
-//    over is contiguous.  Nothing is transposed in LDS.
-//  * QK MFMA half h takes its 16 key rows from page h of the chunk, so every
-//    load of a chunk is (uniform page base) + (one 32-bit lane offset) +
-//    (immediate).  After the C-layout write-back lane (row n, quad q) holds the
-//    scores of keys 4q..4q+3 of both pages; those 8 values are exactly the
-//    lane's B operand of the PV MFMA (element j = key 16*(j/4) + 4q + j%4), so
-//    softmax needs no cross-lane data movement beyond two xor-shuffles for the
-//    row maximum.
+//    over is contiguous; nothing is transposed on chip.
+//  * QK MFMA half h takes its 16 key rows from page h of the chunk.  After the
+//    C-layout write-back lane (row n, quad q) holds the scores of keys
+//    4q..4q+3 of both pages; those 8 values are exactly the lane's B operand of
+//    the PV MFMA (element j = key 16*(j/4) + 4q + j%4), so softmax needs no
+//    cross-lane data movement beyond two lane swaps for the row statistics.
 //  * Rows are (window token, head in group) pairs, so the G query heads that
 //    share a K/V head -- and all tokens of a verify window or prefill block --
 //    read each K/V byte once.
 //  * One persistent launch of (#CU x workgroups per CU) workgroups walks a
-//    work list on one cost axis cut into equal slices (stream-K style); a
-//    workgroup's slice can span several units and split a unit's keys, in
-//    which case it writes partial (o, lse) rows that the merge kernel combines.
-//    Decode/verify units (<= 32 rows) let the 4 waves take alternate chunks
-//    and merge in LDS; prefill units (<= 128 rows) give each wave 32 rows and
-//    stage each chunk once in LDS for all 4 waves.
-//  * Workgroup k runs on XCD k % 8; slots are renumbered so that consecutive
-//    slices (which share K/V pages of one sequence) sit on one XCD's L2.
+//    work list laid on one cost axis cut into equal grains (stream-K style); a
+//    grain can span several units and split a unit's keys, in which case it
+//    writes partial (o, lse) rows that the merge kernel combines.  Split points
+//    depend only on the batch shape, so results are bitwise reproducible.
+//  * Decode/verify units (<= 32 rows) let the 4 waves take alternate chunks and
+//    merge in LDS.  Each wave keeps one chunk in flight: V straight to
+//    registers, K (bf16) by global->LDS DMA into the wave's own slot.  Prefill
+//    units (<= 128 rows) give each wave 32 rows; the 4 waves DMA the 4 page
+//    blocks of a chunk into a ring of LDS slots shared by all of them (XOR-
+//    swizzled rows, so the MFMA fragment reads are conflict-free).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -60,21 +59,6 @@ using cptr = const __attribute__((address_space(4))) T*;
 template <typename T>
 __device__ __forceinline__ cptr<T> ro(const T* p) { return (cptr<T>)p; }
 
-__device__ __forceinline__ pa_plan_unit load_unit(cptr<pa_plan_unit> p) {
-  pa_plan_unit u;
-  u.seq = p->seq;
-  u.kv_head = p->kv_head;
-  u.row0 = p->row0;
-  u.n_rows = p->n_rows;
-  u.n_keys = p->n_keys;
-  u.n_chunks = p->n_chunks;
-  u.kind = p->kind;
-  u.cost_weight = p->cost_weight;
-  u.cost0 = p->cost0;
-  u.piece_base = p->piece_base;
-  u.n_pieces = p->n_pieces;
-  return u;
-}
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ f32x4_t as_f32x4(u32x4_t v) { return __builtin_bit_cast(f32x4_t, v); }
@@ -87,11 +71,87 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return uint32_t(__builtin_bit_cast(uint16_t, x)) | (uint32_t(__builtin_bit_cast(uint16_t, y)) << 16);
 }
 
+// Reductions over the 4 lanes (one per quad) that hold the same query row: a
+// butterfly over lane ^ 32 and lane ^ 16 with the gfx950 permlane swaps.
+__device__ __forceinline__ float quad_max(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// The running maximum that P is scaled against is only moved when a row's new
+// maximum exceeds it by more than this many powers of two; in between, P may
+// reach 2^kLazy (exact for the sums, same relative precision for bf16 P).
+constexpr float kLazy = 8.0f;
+
 // Chunk-relative key of element j (0..7) of the P operand held by a lane of quad q:
 // QK half j/4 read page j/4, and the C layout gives the lane MFMA rows 4q..4q+3.
 __device__ __forceinline__ int p_key(int j, int quad) { return 16 * (j >> 2) + 4 * quad + (j & 3); }
 
 __device__ __forceinline__ uint2 ld8(const char* p) { return *reinterpret_cast<const uint2*>(p); }
+
+// LDS reads that follow a global->LDS DMA still in flight.  The compiler treats every LDS read as
+// possibly aliasing every DMA in flight (all LDS is one object to it) and would wait for all of
+// them; these reads are written as inline asm that completes its own reads (s_waitcnt lgkmcnt(0)
+// inside the block), and the DMA data they need is waited for explicitly (vmcnt + barrier).
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return uint32_t(uintptr_t((const __attribute__((address_space(3))) char*)p));
+}
+__device__ __forceinline__ void lds_read4_b128(const uint32_t (&a)[4], u32x4_t& r0, u32x4_t& r1, u32x4_t& r2,
+                                               u32x4_t& r3) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n"
+      "ds_read_b128 %1, %5\n"
+      "ds_read_b128 %2, %6\n"
+      "ds_read_b128 %3, %7\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+}
+__device__ __forceinline__ void lds_read2_b128(uint32_t a0, uint32_t a1, u32x4_t& r0, u32x4_t& r1) {
+  asm volatile(
+      "ds_read_b128 %0, %2\n"
+      "ds_read_b128 %1, %3\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1)
+      : "v"(a0), "v"(a1));
+}
+__device__ __forceinline__ void lds_read4_b64(const uint32_t (&a)[4], u32x2_t& r0, u32x2_t& r1, u32x2_t& r2,
+                                              u32x2_t& r3) {
+  asm volatile(
+      "ds_read_b64 %0, %4\n"
+      "ds_read_b64 %1, %5\n"
+      "ds_read_b64 %2, %6\n"
+      "ds_read_b64 %3, %7\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+}
+// 16-byte LDS write that the compiler does not order behind DMAs in flight (the data it writes
+// does not overlap any DMA target; LDS operations of one wave execute in issue order).
+__device__ __forceinline__ void lds_write_b128(uint32_t a, u32x4_t v) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+// N 16-byte reads (N even), in blocks of four and two.
+template <int N>
+__device__ __forceinline__ void lds_read_b128(const uint32_t (&a)[N], u32x4_t (&r)[N]) {
+  static_assert(N % 2 == 0, "even count");
+#pragma unroll
+  for (int i = 0; i + 4 <= N; i += 4) {
+    const uint32_t b[4] = {a[i], a[i + 1], a[i + 2], a[i + 3]};
+    lds_read4_b128(b, r[i], r[i + 1], r[i + 2], r[i + 3]);
+  }
+  if constexpr (N % 4 == 2) lds_read2_b128(a[N - 2], a[N - 1], r[N - 2], r[N - 1]);
+}
 
 // ---------------------------------------------------------------------------
 // Element types.  A "fragment" is the 16 bytes one lane feeds to one MFMA
@@ -108,6 +168,7 @@ struct Bf16 {
   static constexpr int kNF = kKF + kVF;
   static constexpr int kTiles = D / 16;
   static constexpr bool kBf16 = true;
+  static constexpr int kVLoads = 2 * kVF;  // global load instructions per chunk of V (two pages per tile)
 
   __device__ static int q_off(int f, int quad) { return (32 * f + 8 * quad) * kEb; }
   // lane offsets within a (page, head) block: K row = lane%16, d = 8*quad (+32*kk)
@@ -153,6 +214,38 @@ struct Bf16 {
   __device__ static f32x4_t pv(const u32x4_t* vf, int t, const PFrag& p, f32x4_t acc) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf[t]), as_bf16x8(p.v), acc, 0, 0, 0);
   }
+  // K and V fragments of a chunk held in LDS (block images of Ring<Bf16<D>>: K page 0, K page 1,
+  // V page 0, V page 1, rows XOR-swizzled by 16-byte column)
+  template <class RG>
+  __device__ static void lds_read_k(const char* slot, int lane, u32x4_t (&kf)[kKF]) {
+    const int m = lane & 15, quad = lane >> 4;
+    uint32_t a[kKF];
+#pragma unroll
+    for (int f = 0; f < kKF; ++f) {
+      const int h = f / (D / 32), kk = f % (D / 32);
+      a[f] = lds_addr(slot + h * RG::kBlk + m * RG::kPitchK + RG::swz_k(m, 4 * kk + quad) * 16);
+    }
+    lds_read_b128<kKF>(a, kf);
+  }
+  template <class RG>
+  __device__ static void lds_read_v(const char* slot, int lane, u32x4_t (&vf)[kVF]) {
+    const int m = lane & 15, quad = lane >> 4;
+#pragma unroll
+    for (int t0 = 0; t0 < kVF; t0 += 2) {
+      uint32_t a[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int d = 16 * (t0 + i) + m;
+        const int off = d * RG::kPitchV + RG::swz_v(d, quad >> 1) * 16 + 8 * (quad & 1);
+        a[2 * i] = lds_addr(slot + 2 * RG::kBlk + off);
+        a[2 * i + 1] = lds_addr(slot + 3 * RG::kBlk + off);
+      }
+      u32x2_t x0, x1, x2, x3;
+      lds_read4_b64(a, x0, x1, x2, x3);
+      vf[t0] = u32x4_t{x0[0], x0[1], x1[0], x1[1]};
+      vf[t0 + 1] = u32x4_t{x2[0], x2[1], x3[0], x3[1]};
+    }
+  }
   __device__ static void store_out(char* dst, f32x4_t o) {  // 4 consecutive d
     uint2 v;
     v.x = pack_bf16x2(o[0], o[1]);
@@ -171,6 +264,7 @@ struct F32 {
   static constexpr int kNF = kKF + kVF;
   static constexpr int kTiles = D / 16;
   static constexpr bool kBf16 = false;
+  static constexpr int kVLoads = kVF;
 
   __device__ static int q_off(int f, int quad) { return (16 * f + 4 * quad) * kEb; }
   __device__ static uint32_t k_lane(int lane) { return uint32_t(((lane & 15) * D + 4 * (lane >> 4)) * kEb); }
@@ -211,6 +305,29 @@ struct F32 {
     for (int j = 0; j < 8; ++j)
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f32x4(vf[2 * t + (j >> 2)])[j & 3], p.p[j], acc, 0, 0, 0);
     return acc;
+  }
+  template <class RG>
+  __device__ static void lds_read_k(const char* slot, int lane, u32x4_t (&kf)[kKF]) {
+    const int m = lane & 15, quad = lane >> 4;
+    uint32_t a[kKF];
+#pragma unroll
+    for (int f = 0; f < kKF; ++f) {
+      const int h = f / (D / 16), jj = f % (D / 16);
+      a[f] = lds_addr(slot + h * RG::kBlk + m * RG::kPitchK + RG::swz_k(m, 4 * jj + quad) * 16);
+    }
+    lds_read_b128<kKF>(a, kf);
+  }
+  template <class RG>
+  __device__ static void lds_read_v(const char* slot, int lane, u32x4_t (&vf)[kVF]) {
+    const int m = lane & 15, quad = lane >> 4;
+    uint32_t a[kVF];
+#pragma unroll
+    for (int g = 0; g < kVF; ++g) {
+      const int t = g >> 1, h = g & 1;
+      const int d = 16 * t + m;
+      a[g] = lds_addr(slot + (2 + h) * RG::kBlk + d * RG::kPitchV + RG::swz_v(d, quad) * 16);
+    }
+    lds_read_b128<kVF>(a, vf);
   }
   __device__ static void store_out(char* dst, f32x4_t o) { *reinterpret_cast<f32x4_t*>(dst) = o; }
 };
@@ -253,7 +370,7 @@ __device__ __forceinline__ ChunkPages chunk_pages(const AttnArgs& A, cptr<int32_
   const int pa = __builtin_amdgcn_readfirstlane(bt_row[2 * c]);
   const int pb = key0 + kPage < n_seq ? __builtin_amdgcn_readfirstlane(bt_row[2 * c + 1]) : pa;
   const int64_t blk = int64_t(kPage) * TR::D * TR::kEb;  // bytes of one (page, head) block
-  const int64_t hkv = A.num_kv_heads;
+  const int64_t hkv = A.plan.num_kv_heads;
   ChunkPages cp;
   cp.k0 = static_cast<const char*>(A.k_pool) + (int64_t(pa) * hkv + kvh) * blk;
   cp.k1 = static_cast<const char*>(A.k_pool) + (int64_t(pb) * hkv + kvh) * blk;
@@ -292,36 +409,37 @@ __device__ __forceinline__ void softmax_chunk(State<TR, RT>& st, GetQ getq, cons
     getq(rt, qf);
     const f32x4_t s0 = TR::qk(kf, 0, qf);
     const f32x4_t s1 = TR::qk(kf, 1, qf);
-    float x[8];
+    float x[8];  // raw scores q.k; the positive factor scale*log2(e) is applied inside exp2
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      x[e] = s0[e] * sl2;
-      x[4 + e] = s1[e] * sl2;
+      x[e] = s0[e];
+      x[4 + e] = s1[e];
     }
     if (mask) {
       const int lim = p_row[rt] - key0;  // element j visible iff its key <= lim
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[j] = p_key(j, quad) <= lim ? x[j] : -INFINITY;
     }
-    float mx = x[0];
+    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    mx = quad_max(mx);
+    const float mx2 = mx == -INFINITY ? -INFINITY : mx * sl2;  // row maximum in the base-2 domain
+    if (__any(mx2 > st.m[rt] + kLazy)) {
+      const float m_new = fmaxf(st.m[rt], mx2);
+      const float alpha = fast_exp2(st.m[rt] - (m_new == -INFINITY ? 0.f : m_new));
+      st.l[rt] *= alpha;
 #pragma unroll
-    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(st.m[rt], mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(st.m[rt] - m_use);
+      for (int t = 0; t < TR::kTiles; ++t) st.o[rt][t] *= alpha;
+      st.m[rt] = m_new;
+    }
+    const float neg_m = st.m[rt] == -INFINITY ? 0.f : -st.m[rt];
     float p[8];
     float sum = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      p[j] = fast_exp2(x[j] - m_use);
+      p[j] = fast_exp2(__builtin_fmaf(x[j], sl2, neg_m));
       sum += p[j];
     }
-    st.l[rt] = st.l[rt] * alpha + sum;
-    st.m[rt] = m_new;
-#pragma unroll
-    for (int t = 0; t < TR::kTiles; ++t) st.o[rt][t] *= alpha;
+    st.l[rt] += sum;
     pf[rt] = TR::make_p(p);
   }
 }
@@ -349,60 +467,120 @@ __device__ __forceinline__ RowInfo row_info(const AttnArgs& A, const pa_plan_uni
   RowInfo ri;
   ri.valid = r < U.n_rows;
   const int rr = U.row0 + (ri.valid ? r : 0);
-  const int t = rr / A.group;
-  const int hh = rr - t * A.group;
+  const int t = rr / A.plan.group;
+  const int hh = rr - t * A.plan.group;
   ri.tok = q0 + t;
-  ri.head = U.kv_head * A.group + hh;
+  ri.head = U.kv_head * A.plan.group + hh;
   ri.p = ri.valid ? n_seq - qn + t : -1;
   return ri;
 }
 
+// Q fragment of one row; for a negative scale the signs are flipped (exact), so that the
+// factor applied to q.k is always |scale| * log2(e) >= 0.
 template <class TR>
 __device__ __forceinline__ u32x4_t load_q_frag(const AttnArgs& A, const RowInfo& ri, int f, int quad) {
   const char* base = static_cast<const char*>(A.q) + (int64_t(ri.tok) * A.num_q_heads + ri.head) * TR::D * TR::kEb;
-  return ri.valid ? ld16(base + TR::q_off(f, quad)) : u32x4_t{0u, 0u, 0u, 0u};
+  return ri.valid ? (ld16(base + TR::q_off(f, quad)) ^ A.q_sign) : u32x4_t{0u, 0u, 0u, 0u};
 }
 
-// Final (normalised) output of one row tile's 4 d values at tile t, or a partial row.
+// Final (normalised) output of one row tile's 4 d values at tile t (part < 0), or
+// the same values as partial row r of partial position `part` (slot * 2 + 0/1).
 template <class TR>
-__device__ __forceinline__ void emit(const AttnArgs& A, const pa_plan_unit& U, const RowInfo& ri, int r, int piece,
-                                     int t, int quad, f32x4_t o, float lse_nat, bool write_lse) {
+__device__ __forceinline__ void emit(const AttnArgs& A, const RowInfo& ri, int r, int part, int t, int quad,
+                                     f32x4_t o, float lse_nat, bool write_lse) {
   if (!ri.valid) return;
   const int d = 16 * t + 4 * quad;
-  if (U.n_pieces <= 1) {
+  if (part < 0) {
     char* dst = static_cast<char*>(A.out) + ((int64_t(ri.tok) * A.num_q_heads + ri.head) * TR::D + d) * TR::kEb;
     TR::store_out(dst, o);
     if (write_lse) A.lse[int64_t(ri.tok) * A.num_q_heads + ri.head] = lse_nat;
   } else {
-    const int64_t prow = int64_t(U.piece_base) + int64_t(piece) * U.n_rows + r;
+    const int64_t prow = int64_t(part) * kPartRows + r;
     *reinterpret_cast<f32x4_t*>(A.part_o + prow * TR::D + d) = o;
     if (write_lse) A.part_lse[prow] = lse_nat;
   }
 }
 
-// LDS: staging for row-split units (2 buffers x kNF fragments x 64 lanes) and
-// the cross-wave merge of key-split units (4 waves x 2 row tiles x kTiles).
+// Geometry of the LDS ring that row-split units stream chunks through.  A
+// chunk is four (page, head) blocks -- K page 0, K page 1, V page 0, V page 1 --
+// copied by global->LDS DMA (wave w copies block w, 1 KiB per instruction).
+// Each block's LDS image is a permutation of its 16-byte columns (XOR swizzle
+// by row) so that the fragment reads are free of bank conflicts.
+template <class TR>
+struct Ring {
+  static constexpr int kBlk = kPage * TR::D * TR::kEb;  // bytes of one (page, head) block
+  static constexpr int kChunk = 4 * kBlk;
+  static constexpr int kNB = 65536 / kChunk > 4 ? 4 : (65536 / kChunk < 2 ? 2 : 65536 / kChunk);  // ring slots
+  static constexpr int kInstr = kBlk / 1024;  // DMA instructions per wave per chunk
+  static constexpr int kPitchK = TR::D * TR::kEb;  // K row (slot) pitch
+  static constexpr int kNCk = kPitchK / 16;
+  static constexpr int kPitchV = kPage * TR::kEb;  // V^T row (d) pitch: 32 or 64 bytes
+  static constexpr int kNCv = kPitchV / 16;        // 2 or 4 columns
+  static constexpr int kShV = kNCv == 2 ? 3 : 2;   // rows per 256 bytes = 1 << kShV
+  static constexpr int kBytes = kNB * kChunk;
+  // swizzled column of global column c in row r
+  __device__ static int swz_k(int r, int c) { return c ^ (r & (kNCk - 1)); }
+  __device__ static int swz_v(int r, int c) { return c ^ ((r >> kShV) & (kNCv - 1)); }
+};
+
+// LDS: the row-split ring and the key-split Q slices / cross-wave merge buffer share one region.
 template <class TR>
 struct Smem {
-  static constexpr int kStage = 2 * TR::kNF * 64;            // u32x4 slots
-  static constexpr int kMerge = kWaves * 2 * TR::kTiles * 64;  // f32x4 slots
-  static constexpr int kSlots = kStage > kMerge ? kStage : kMerge;
-  u32x4_t buf[kSlots];
+  static constexpr int kMergeBytes = kWaves * 2 * TR::kTiles * 64 * 16;
+  static constexpr int kBytes = Ring<TR>::kBytes > kMergeBytes ? Ring<TR>::kBytes : kMergeBytes;
+  u32x4_t buf[kBytes / 16];
   float stat[kWaves][2][2][16];  // [wave][row tile][m | l][row]
 };
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Global->LDS DMA of 16 bytes per lane from one (page, head) block: lane l writes LDS bytes
+// [dst + 16 l, +16) from block byte `off`.  The MUBUF form (buffer_load ... lds) is used rather
+// than the FLAT-global one: the compiler's wait analysis treats a FLAT instruction that touches
+// two address spaces as completing out of order and then drains every load with vmcnt(0) at the
+// next wait for a register load; with MUBUF its waits for the V register loads stay exact.
+// The descriptor covers exactly one block (`bytes`), so an offset past it would read zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const char* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, int(bytes), 0x00020000);
+}
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, char* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, off, 0, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmcnt_lgkm0(int n) {
+  // s_waitcnt vmcnt(n) lgkmcnt(0); expcnt left at its maximum
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0070); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0072); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0074); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0076); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0078); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x007C); break;
+    case 16: __builtin_amdgcn_s_waitcnt(0x4070); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0070); break;  // any other count: wait for everything
+  }
+}
+
+// Workgroup barrier that orders LDS accesses for the compiler without waiting on global memory.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // ---------------------------------------------------------------------------
 // Key-split unit (decode / verify, <= 32 rows): wave w takes chunks i0+w, i0+w+4, ...
 // ---------------------------------------------------------------------------
 template <class TR, int RT>
-__device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, int i0, int i1, int piece, Smem<TR>& sm) {
-  const int lane = threadIdx.x & 63;
+__device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, int i0, int i1, int part, Smem<TR>& sm) {
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));  // lane-derived values are recomputed per unit, not held across the unit loop
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int quad = lane >> 4;
   const int s = U.seq;
-  const int n_seq = ro(A.seq_lens)[s];
-  const int q0 = ro(A.qsl)[s];
-  const int qn = ro(A.qsl)[s + 1] - q0;
+  const int n_seq = ro(A.plan.seq_lens)[s];
+  const int q0 = ro(A.plan.qsl)[s];
+  const int qn = ro(A.plan.qsl)[s + 1] - q0;
   const cptr<int32_t> bt_row = ro(A.block_table) + int64_t(s) * A.max_pages;
 
   RowInfo ri[RT];
@@ -412,14 +590,17 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
     ri[rt] = row_info(A, U, 16 * rt + (lane & 15), n_seq, q0, qn);
     p_row[rt] = ri[rt].p;
   }
-  const int min_p = n_seq - qn + U.row0 / A.group;  // first row's last visible key
+  const int min_p = n_seq - qn + U.row0 / A.plan.group;  // first row's last visible key
 
-  // Q fragments live in this wave's slice of LDS (re-read every chunk; keeps VGPRs for K/V in flight)
+  // Q fragments live in this wave's slice of LDS (re-read every chunk; keeps VGPRs for K/V in flight).
+  // Order of issue at a unit start: Q loads, then the first chunk's K/V loads, then the LDS copy of Q,
+  // so the Q and K/V latencies overlap.
   u32x4_t* qlds = sm.buf + w * (RT * TR::kQF * 64);
+  u32x4_t qtmp[RT][TR::kQF];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int f = 0; f < TR::kQF; ++f) qlds[(rt * TR::kQF + f) * 64 + lane] = load_q_frag<TR>(A, ri[rt], f, quad);
+    for (int f = 0; f < TR::kQF; ++f) qtmp[rt][f] = load_q_frag<TR>(A, ri[rt], f, quad);
   auto getq = [&](int rt, u32x4_t (&qf)[TR::kQF]) {
 #pragma unroll
     for (int f = 0; f < TR::kQF; ++f) qf[f] = qlds[(rt * TR::kQF + f) * 64 + lane];
@@ -427,37 +608,86 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
   State<TR, RT> st;
   state_init(st);
 
+  // A wave keeps one chunk (16 KiB for bf16, D = 128) of K/V in flight: measured on MI355X, two
+  // chunks per wave streamed slower than one.  For bf16 the K half of a chunk travels by
+  // global->LDS DMA into this wave's 2-page slot (contiguous 1 KiB per instruction; K fragments
+  // read directly from the pool touch 16 rows x 64 B per instruction, which streams ~10% slower
+  // at this occupancy) and V goes straight to registers (512 contiguous bytes per instruction).
+  // Every load is issued unconditionally: past the wave's last chunk it re-reads the chunk it has
+  // (an L2 hit), so the number of loads in flight is the same on every path and the waits --
+  // the compiler's for V, the explicit one for the K DMA -- are exact.
+  using RG = Ring<TR>;
+  constexpr bool kKviaLds = TR::kBf16 && PA_K_VIA_LDS;
+  constexpr int kQRegion = kWaves * 2 * TR::kQF * 64;  // u32x4 slots of the Q slices (2 row tiles)
+  static_assert(!kKviaLds || (kQRegion * 16 + kWaves * 2 * RG::kBlk <= Smem<TR>::kBytes), "LDS budget");
+  char* kslot = reinterpret_cast<char*>(sm.buf + kQRegion) + w * 2 * RG::kBlk;
   const uint32_t kl = TR::k_lane(lane), vl = TR::v_lane(lane);
-  int c = i0 + w;
+  auto dma_k = [&](char* slot, const ChunkPages& cp) {
+    constexpr int kPer = RG::kBlk / 1024;  // DMA instructions per page
+    const __amdgpu_buffer_rsrc_t r0 = block_rsrc(cp.k0, RG::kBlk), r1 = block_rsrc(cp.k1, RG::kBlk);
+#pragma unroll
+    for (int i = 0; i < 2 * kPer; ++i) {
+      const int o = (i % kPer) * 1024 + 16 * lane;
+      const int r = o / RG::kPitchK, cc = (o % RG::kPitchK) / 16;
+      dma16(i < kPer ? r0 : r1, uint32_t(r * RG::kPitchK + RG::swz_k(r, cc) * 16),
+            slot + (i / kPer) * RG::kBlk + (i % kPer) * 1024);
+    }
+  };
+  const int c = i0 + w;
   u32x4_t kf[TR::kKF];
   u32x4_t vf[TR::kVF];
-  if (c < i1) {
-    const ChunkPages cp = chunk_pages<TR>(A, bt_row, U.kv_head, c, n_seq);
-    load_k<TR>(cp, kl, vl, kf);
+  ChunkPages cp = chunk_pages<TR>(A, bt_row, U.kv_head, c < i1 ? c : i0, n_seq);
+  if constexpr (kKviaLds) dma_k(kslot, cp);
+  else load_k<TR>(cp, kl, vl, kf);
+  load_v<TR>(cp, kl, vl, vf);
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int f = 0; f < TR::kQF; ++f) {
+      if constexpr (kKviaLds) lds_write_b128(lds_addr(qlds + (rt * TR::kQF + f) * 64 + lane), qtmp[rt][f]);
+      else qlds[(rt * TR::kQF + f) * 64 + lane] = qtmp[rt][f];
+    }
+
+  // The loop body has a single path.  A step past the wave's last chunk is a dummy: all its keys
+  // are masked and its V is zeroed, so it adds nothing.
+  const int mine = i1 > c ? (i1 - c + kWaves - 1) / kWaves : 0;  // chunks of this wave
+  for (int j = 0; j < mine; ++j) {
+    const int cc = c + j * kWaves;
+    const int key0 = cc * kChunkKeys;
+    const int cn = cc + kWaves;
+    if (cn < i1) cp = chunk_pages<TR>(A, bt_row, U.kv_head, cn, n_seq);
+    typename TR::PFrag pf[RT];
+    if constexpr (kKviaLds) {
+      wait_vmcnt_lgkm0(TR::kVLoads);  // the K DMA of this chunk has landed (only V was issued after it)
+      asm volatile("" ::: "memory");
+      TR::template lds_read_k<RG>(kslot, lane, kf);  // completes before the slot is refilled
+      asm volatile("" ::: "memory");
+      dma_k(kslot, cp);
+      auto getq_asm = [&](int rt, u32x4_t (&qf)[TR::kQF]) {  // Q reads behind the DMA just issued
+        uint32_t a[TR::kQF];
+#pragma unroll
+        for (int f = 0; f < TR::kQF; ++f) a[f] = lds_addr(qlds + (rt * TR::kQF + f) * 64 + lane);
+        lds_read_b128<TR::kQF>(a, qf);
+      };
+      softmax_chunk<TR, RT>(st, getq_asm, kf, key0, p_row, key0 + kChunkKeys - 1 > min_p, A.scale_log2, lane,
+                            pf);
+    } else {
+      asm volatile("" ::: "memory");  // keep the Q reads inside the loop
+      softmax_chunk<TR, RT>(st, getq, kf, key0, p_row, key0 + kChunkKeys - 1 > min_p, A.scale_log2, lane, pf);
+      load_k<TR>(cp, kl, vl, kf);
+    }
+    TR::sanitize_v(vf, quad, n_seq - key0);
+    pv_chunk<TR, RT>(st, vf, pf);
     load_v<TR>(cp, kl, vl, vf);
   }
-  for (; c < i1; c += kWaves) {
-    const int key0 = c * kChunkKeys;
-    const int cn = c + kWaves;
-    ChunkPages cpn;
-    if (cn < i1) cpn = chunk_pages<TR>(A, bt_row, U.kv_head, cn, n_seq);
-    asm volatile("" ::: "memory");  // keep the Q reads inside the loop
-    typename TR::PFrag pf[RT];
-    softmax_chunk<TR, RT>(st, getq, kf, key0, p_row, key0 + kChunkKeys - 1 > min_p, A.scale_log2, lane, pf);
-    if (cn < i1) load_k<TR>(cpn, kl, vl, kf);
-    if (key0 + kChunkKeys > n_seq) TR::sanitize_v(vf, quad, n_seq - key0);
-    pv_chunk<TR, RT>(st, vf, pf);
-    if (cn < i1) load_v<TR>(cpn, kl, vl, vf);
-  }
+  if constexpr (kKviaLds) wait_vmcnt_lgkm0(0);  // the last (unused) K DMA has landed before LDS is reused
   __syncthreads();  // every wave is done with its Q slice before the merge buffer overwrites it
 
   // merge the 4 waves' states through LDS
   f32x4_t* obuf = reinterpret_cast<f32x4_t*>(sm.buf);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    float l = st.l[rt];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = quad_sum(st.l[rt]);
     if (quad == 0) {
       sm.stat[w][rt][0][lane] = st.m[rt];
       sm.stat[w][rt][1][lane] = l;
@@ -487,27 +717,50 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
       f32x4_t o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < kWaves; ++i) o += obuf[((i * 2 + rt) * TR::kTiles + t) * 64 + lane] * sc[i];
-      emit<TR>(A, U, ri[rt], 16 * rt + n, piece, t, quad, o * inv, lse_nat, t == 0 && quad == 0);
+      emit<TR>(A, ri[rt], 16 * rt + n, part, t, quad, o * inv, lse_nat, t == 0 && quad == 0);
     }
   }
   __syncthreads();
 }
 
+// One chunk of a row-split unit: start the DMA of chunk `next` (if >= 0) into slot `fill`, then
+// compute on the chunk held in slot `cur` (a different slot, landed before the last barrier).
+template <class TR, int RT, class Issue, class GetQ>
+__device__ __forceinline__ void ring_step(char* fill, const char* cur, Issue issue, int next,
+                                          bool active, State<TR, RT>& st, GetQ getq, int key0,
+                                          const int (&p_row)[RT], int min_p, int n_seq, float sl2, int lane) {
+  using RG = Ring<TR>;
+  if (next >= 0) issue(next, fill);
+  if (active) {
+    const int quad = lane >> 4;
+    u32x4_t kf[TR::kKF];
+    TR::template lds_read_k<RG>(cur, lane, kf);
+    typename TR::PFrag pf[RT];
+    softmax_chunk<TR, RT>(st, getq, kf, key0, p_row, key0 + kChunkKeys - 1 > min_p, sl2, lane, pf);
+    u32x4_t vf[TR::kVF];
+    TR::template lds_read_v<RG>(cur, lane, vf);
+    if (key0 + kChunkKeys > n_seq) TR::sanitize_v(vf, quad, n_seq - key0);
+    pv_chunk<TR, RT>(st, vf, pf);
+  }
+}
+
 // ---------------------------------------------------------------------------
-// Row-split unit (prefill, <= 128 rows): wave w owns rows [32w, 32w+32); the
-// workgroup stages each chunk once in LDS (double-buffered) for all 4 waves.
+// Row-split unit (prefill, <= 128 rows): wave w owns rows [32w, 32w+32).  The
+// workgroup streams chunks through an LDS ring with global->LDS DMA, kNB - 1
+// chunks ahead of the one being computed; every wave issues 1/4 of each chunk.
 // ---------------------------------------------------------------------------
 template <class TR>
-__device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, int i0, int i1, int piece, Smem<TR>& sm) {
+__device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, int i0, int i1, int part, Smem<TR>& sm) {
+  using RG = Ring<TR>;
   constexpr int RT = 2;
-  constexpr int kPer = (TR::kNF + kWaves - 1) / kWaves;  // fragments each thread stages per chunk
-  const int lane = threadIdx.x & 63;
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));  // lane-derived values are recomputed per unit, not held across the unit loop
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int quad = lane >> 4;
   const int s = U.seq;
-  const int n_seq = ro(A.seq_lens)[s];
-  const int q0 = ro(A.qsl)[s];
-  const int qn = ro(A.qsl)[s + 1] - q0;
+  const int n_seq = ro(A.plan.seq_lens)[s];
+  const int q0 = ro(A.plan.qsl)[s];
+  const int qn = ro(A.plan.qsl)[s + 1] - q0;
   const cptr<int32_t> bt_row = ro(A.block_table) + int64_t(s) * A.max_pages;
   const bool active = 32 * w < U.n_rows;
 
@@ -518,7 +771,7 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
     ri[rt] = row_info(A, U, 32 * w + 16 * rt + (lane & 15), n_seq, q0, qn);
     p_row[rt] = ri[rt].p;
   }
-  const int min_p = n_seq - qn + (U.row0 + 32 * w) / A.group;
+  const int min_p = n_seq - qn + (U.row0 + 32 * w) / A.plan.group;
 
   u32x4_t qreg[RT][TR::kQF];
 #pragma unroll
@@ -532,58 +785,52 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
   State<TR, RT> st;
   state_init(st);
 
-  const uint32_t kl = TR::k_lane(lane), vl = TR::v_lane(lane);
-  u32x4_t stage[kPer];
-  auto fetch = [&](int c) {
+  // Wave w copies block w of each chunk; lane `lane` of DMA instruction i fills LDS bytes
+  // [i*1024 + 16*lane, +16) of the block image, i.e. row r, swizzled column cc.
+  char* ring = reinterpret_cast<char*>(sm.buf);
+  auto issue = [&](int c, char* slot) {
     const ChunkPages cp = chunk_pages<TR>(A, bt_row, U.kv_head, c, n_seq);
+    const __amdgpu_buffer_rsrc_t rs = block_rsrc(w == 0 ? cp.k0 : w == 1 ? cp.k1 : w == 2 ? cp.v0 : cp.v1, RG::kBlk);
+    char* dst = slot + w * RG::kBlk;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int f = w + kWaves * j;
-      if (f < TR::kNF) stage[j] = frag<TR>(cp, kl, vl, f);
-    }
-  };
-  auto deposit = [&](int b) {
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int f = w + kWaves * j;
-      if (f < TR::kNF) sm.buf[(b * TR::kNF + f) * 64 + lane] = stage[j];
+    for (int i = 0; i < RG::kInstr; ++i) {
+      const int o = i * 1024 + 16 * lane;
+      uint32_t src;
+      if (w < 2) {
+        const int r = o / RG::kPitchK, cc = (o % RG::kPitchK) / 16;
+        src = uint32_t(r * RG::kPitchK + RG::swz_k(r, cc) * 16);
+      } else {
+        const int r = o / RG::kPitchV, cc = (o % RG::kPitchV) / 16;
+        src = uint32_t(r * RG::kPitchV + RG::swz_v(r, cc) * 16);
+      }
+      dma16(rs, src, dst + i * 1024);
     }
   };
 
-  fetch(i0);
-  deposit(0);
-  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < RG::kNB - 1; ++j)
+    if (i0 + j < i1) issue(i0 + j, ring + j * RG::kChunk);
   for (int c = i0; c < i1; ++c) {
-    const int b = (c - i0) & 1;
-    const int key0 = c * kChunkKeys;
-    if (c + 1 < i1) fetch(c + 1);
-    if (active) {
-      u32x4_t kf[TR::kKF];
-#pragma unroll
-      for (int f = 0; f < TR::kKF; ++f) kf[f] = sm.buf[(b * TR::kNF + f) * 64 + lane];
-      typename TR::PFrag pf[RT];
-      softmax_chunk<TR, RT>(st, getq, kf, key0, p_row, key0 + kChunkKeys - 1 > min_p, A.scale_log2, lane, pf);
-      u32x4_t vf[TR::kVF];
-#pragma unroll
-      for (int f = 0; f < TR::kVF; ++f) vf[f] = sm.buf[(b * TR::kNF + TR::kKF + f) * 64 + lane];
-      if (key0 + kChunkKeys > n_seq) TR::sanitize_v(vf, quad, n_seq - key0);
-      pv_chunk<TR, RT>(st, vf, pf);
-    }
-    if (c + 1 < i1) deposit(b ^ 1);
-    __syncthreads();
+    const int j = c - i0;
+    const int ahead = min(RG::kNB - 2, i1 - 1 - c);  // chunks this wave issued after chunk c
+    wait_vmcnt_lgkm0(ahead * RG::kInstr);
+    lds_barrier();  // chunk c is in LDS for every wave; chunk c-1's slot is free
+    ring_step<TR, RT>(ring + ((j + RG::kNB - 1) % RG::kNB) * RG::kChunk, ring + (j % RG::kNB) * RG::kChunk,
+                      issue, c + RG::kNB - 1 < i1 ? c + RG::kNB - 1 : -1, active, st, getq, c * kChunkKeys, p_row,
+                      min_p, n_seq, A.scale_log2, lane);
   }
+  __builtin_amdgcn_s_waitcnt(0x0070);  // nothing of this unit left in flight
+  lds_barrier();                        // every wave is done with the ring before it is reused
 
   if (active) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      float l = st.l[rt];
-      l += __shfl_xor(l, 16);
-      l += __shfl_xor(l, 32);
+      const float l = quad_sum(st.l[rt]);
       const float inv = l > 0.f ? 1.f / l : 0.f;
       const float lse_nat = l > 0.f ? (st.m[rt] + fast_log2(l)) * kLn2 : -INFINITY;
 #pragma unroll
       for (int t = 0; t < TR::kTiles; ++t)
-        emit<TR>(A, U, ri[rt], 32 * w + 16 * rt + (lane & 15), piece, t, quad, st.o[rt][t] * inv, lse_nat,
+        emit<TR>(A, ri[rt], 32 * w + 16 * rt + (lane & 15), part, t, quad, st.o[rt][t] * inv, lse_nat,
                  t == 0 && quad == 0);
     }
   }
@@ -593,58 +840,12 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
 __device__ __forceinline__ int64_t slot_of(int64_t c, int64_t S, int64_t C) { return ((c + 1) * S - 1) / C; }
 __device__ __forceinline__ int64_t slice_begin(int64_t k, int64_t S, int64_t C) { return k * C / S; }
 
-// Renumber workgroups so that consecutive slots run on one XCD (workgroup b runs on XCD b % 8).
-__device__ __forceinline__ int xcd_slot(int b, int S) {
-  const int x = b & 7, k = b >> 3;
-  const int per = S >> 3, rem = S & 7;
-  return x * per + (x < rem ? x : rem) + k;
-}
-
-template <class TR>
-__global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs A) {
-  __shared__ Smem<TR> sm;
-  const cptr<pa_plan_header> hdr = ro(A.hdr);
-  const cptr<pa_plan_unit> units = ro(A.units);
-  const int S = hdr->n_slots;
-  if (int(blockIdx.x) >= S) return;
-  const int slot = xcd_slot(blockIdx.x, S);
-  const int64_t C = hdr->total_cost;
-  const int n_units = hdr->n_units;
-  const int64_t c0 = slice_begin(slot, S, C);
-  const int64_t c1 = slice_begin(slot + 1, S, C);
-  if (c0 >= c1) return;
-  // last unit whose cost0 <= c0
-  int lo = 0, hi = n_units - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (units[mid].cost0 <= c0) lo = mid; else hi = mid - 1;
-  }
-  for (int u = lo; u < n_units; ++u) {
-    const pa_plan_unit U = load_unit(units + u);
-    if (U.cost0 >= c1) break;
-    const int64_t w = U.cost_weight;
-    const int i0 = int(c0 > U.cost0 ? (c0 - U.cost0 + w - 1) / w : 0);
-    const int64_t e = (c1 - U.cost0 + w - 1) / w;
-    const int i1 = int(e < U.n_chunks ? e : U.n_chunks);
-    if (i0 >= i1) continue;
-    const int piece = int(slot - slot_of(U.cost0, S, C));
-    if (U.kind == 0) {
-      if (U.n_rows <= 16) run_keysplit<TR, 1>(A, U, i0, i1, piece, sm);
-      else run_keysplit<TR, 2>(A, U, i0, i1, piece, sm);
-    } else {
-      run_rowsplit<TR>(A, U, i0, i1, piece, sm);
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Planner: one workgroup of 1024 threads.
+// The plan.  Sequence s contributes Hkv groups of nb units (nb = 1 when its
+// q_len * G rows fit one key-split unit, else ceil(rows / 128) row blocks);
+// units are ordered (sequence, kv head, row block) on one cost axis.  Only the
+// per-sequence cost prefix is stored; units are rebuilt from it on the fly.
 // ---------------------------------------------------------------------------
-struct SeqShape {
-  int units;
-  int64_t cost;
-};
-
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // keys visible to the last row of row block rb of a sequence (n keys, qn tokens, G heads)
@@ -654,157 +855,317 @@ __device__ __forceinline__ int block_keys(int n, int qn, int G, int rb) {
   return n - qn + last + 1;
 }
 
-__device__ SeqShape seq_shape(int n, int qn, int G, int Hkv) {
-  SeqShape r{0, 0};
-  if (qn <= 0) return r;
-  const int rows = qn * G;
-  if (rows <= kSplitRows) {
-    r.units = Hkv;
-    r.cost = int64_t(Hkv) * ceil_div(n, kChunkKeys) * kCostKeySplit;
+struct SeqUnits {
+  int n, qn, rows, nb;
+  bool split;        // one key-split unit per kv head
+  int64_t per_head;  // cost of one kv head's units
+};
+
+__device__ SeqUnits seq_units(int n, int qn, int G) {
+  SeqUnits q;
+  q.n = n;
+  q.qn = qn;
+  q.rows = qn > 0 ? qn * G : 0;
+  q.split = q.rows <= kSplitRows;
+  if (qn <= 0) {
+    q.nb = 0;
+    q.per_head = 0;
+  } else if (q.split) {
+    q.nb = 1;
+    q.per_head = kCostUnitStart + int64_t(ceil_div(n, kChunkKeys)) * kCostKeySplit;
   } else {
-    const int nb = ceil_div(rows, kBlockRows);
+    q.nb = ceil_div(q.rows, kBlockRows);
     int64_t ch = 0;
-    for (int rb = 0; rb < nb; ++rb) ch += ceil_div(block_keys(n, qn, G, rb), kChunkKeys);
-    r.units = Hkv * nb;
-    r.cost = int64_t(Hkv) * ch * kCostRowSplit;
+    for (int rb = 0; rb < q.nb; ++rb) ch += ceil_div(block_keys(n, qn, G, rb), kChunkKeys);
+    q.per_head = int64_t(q.nb) * kCostUnitStart + ch * kCostRowSplit;
   }
+  return q;
+}
+
+// A unit occupies [cost0, cost0 + kCostUnitStart + n_chunks * weight) on the cost axis;
+// chunk i starts at cost0 + kCostUnitStart + i * weight.
+__device__ __forceinline__ int64_t unit_cost(const pa_plan_unit& U) {
+  return kCostUnitStart + int64_t(U.n_chunks) * U.cost_weight;
+}
+__device__ __forceinline__ int64_t chunk_start(const pa_plan_unit& U, int i) {
+  return U.cost0 + kCostUnitStart + int64_t(i) * U.cost_weight;
+}
+
+__device__ pa_plan_unit make_unit(int s, const SeqUnits& q, int G, int g, int rb, int64_t cost0) {
+  pa_plan_unit U;
+  U.seq = s;
+  U.kv_head = g;
+  U.row0 = q.split ? 0 : rb * kBlockRows;
+  U.n_rows = q.split ? q.rows : min(kBlockRows, q.rows - rb * kBlockRows);
+  U.n_keys = q.split ? q.n : block_keys(q.n, q.qn, G, rb);
+  U.n_chunks = ceil_div(U.n_keys, kChunkKeys);
+  U.kind = q.split ? 0 : 1;
+  U.cost_weight = q.split ? kCostKeySplit : kCostRowSplit;
+  U.cost0 = cost0;
+  U.first_slot = 0;
+  U.n_pieces = 0;
+  return U;
+}
+
+// Cursor over the units of the plan, in cost order.
+struct UnitCursor {
+  int s, g, rb;
+  int64_t seq_base;  // cost at which sequence s starts
+  SeqUnits q;
+  pa_plan_unit U;
+};
+
+template <class P>
+__device__ void cursor_load_seq(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl) {
+  cu.q = seq_units(seq_lens[cu.s], qsl[cu.s + 1] - qsl[cu.s], v.group);
+}
+
+// Position the cursor on the unit whose cost range holds c (0 <= c < total).
+template <class P, class Q>
+__device__ void cursor_find(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl, Q seq_cost, int64_t c) {
+  int lo = 0, hi = v.num_seqs - 1;  // last s with seq_cost[s] <= c
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (seq_cost[mid] <= c) lo = mid; else hi = mid - 1;
+  }
+  cu.s = lo;
+  cu.seq_base = seq_cost[lo];
+  cursor_load_seq(cu, v, seq_lens, qsl);
+  const int64_t off = c - cu.seq_base;
+  cu.g = int(off / cu.q.per_head);
+  int64_t acc = cu.seq_base + int64_t(cu.g) * cu.q.per_head;
+  cu.rb = 0;
+  if (!cu.q.split) {
+    for (; cu.rb < cu.q.nb - 1; ++cu.rb) {
+      const int64_t wgt =
+          kCostUnitStart + int64_t(ceil_div(block_keys(cu.q.n, cu.q.qn, v.group, cu.rb), kChunkKeys)) * kCostRowSplit;
+      if (c < acc + wgt) break;
+      acc += wgt;
+    }
+  }
+  cu.U = make_unit(cu.s, cu.q, v.group, cu.g, cu.rb, acc);
+}
+
+// Position the cursor as the planner recorded for one slot.
+__device__ __forceinline__ void cursor_from_slot(UnitCursor& cu, const PlanView& v, const SlotStart& st) {
+  cu.s = st.s;
+  cu.g = st.g;
+  cu.rb = st.rb;
+  cu.seq_base = st.seq_base;
+  cu.q = seq_units(st.n, st.qn, v.group);
+  cu.U = make_unit(st.s, cu.q, v.group, st.g, st.rb, st.unit_cost0);
+}
+
+__device__ __forceinline__ SlotStart load_slot(cptr<SlotStart> p) {
+  SlotStart r;
+  r.c0 = p->c0;
+  r.c1 = p->c1;
+  r.seq_base = p->seq_base;
+  r.unit_cost0 = p->unit_cost0;
+  r.s = p->s;
+  r.g = p->g;
+  r.rb = p->rb;
+  r.n = p->n;
+  r.qn = p->qn;
   return r;
 }
 
-// Inclusive block scan of one int64 per thread (kPlanThreads threads).
-__device__ int64_t block_scan(int64_t v, int64_t* tmp) {
-  const int t = threadIdx.x;
-  tmp[t] = v;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {
-    const int64_t add = t >= off ? tmp[t - off] : 0;
-    __syncthreads();
-    tmp[t] += add;
-    __syncthreads();
+// Advance to the next unit; returns false past the last one.
+template <class P>
+__device__ bool cursor_next(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl) {
+  const int64_t next_cost = cu.U.cost0 + unit_cost(cu.U);
+  if (++cu.rb >= cu.q.nb) {
+    cu.rb = 0;
+    if (++cu.g >= v.num_kv_heads) {
+      cu.g = 0;
+      do {
+        cu.seq_base += int64_t(v.num_kv_heads) * cu.q.per_head;
+        if (++cu.s >= v.num_seqs) return false;
+        cursor_load_seq(cu, v, seq_lens, qsl);
+      } while (cu.q.nb == 0);
+    }
   }
-  const int64_t r = tmp[t];
-  __syncthreads();
-  return r;
+  cu.U = make_unit(cu.s, cu.q, v.group, cu.g, cu.rb, next_cost);
+  return true;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
-  __shared__ int64_t tmp[kPlanThreads];
-  __shared__ int64_t tot_cost_s, tot_units_s;
-  const int t = threadIdx.x;
-  const int B = a.num_seqs;
-  // phase 1: per-sequence unit counts and costs, exclusive prefixes
-  int64_t carry_c = 0, carry_u = 0;
-  for (int base = 0; base < B; base += kPlanThreads) {
-    const int s = base + t;
-    SeqShape sh{0, 0};
-    if (s < B) sh = seq_shape(a.seq_lens[s], a.qsl[s + 1] - a.qsl[s], a.group, a.num_kv_heads);
-    const int64_t ic = block_scan(sh.cost, tmp);
-    const int64_t tc = tmp[kPlanThreads - 1 < B - base ? kPlanThreads - 1 : B - base - 1];
-    __syncthreads();
-    const int64_t iu = block_scan(sh.units, tmp);
-    const int64_t tu = tmp[kPlanThreads - 1 < B - base ? kPlanThreads - 1 : B - base - 1];
-    __syncthreads();
-    if (s < B) {
-      a.seq_cost[s] = carry_c + ic - sh.cost;
-      a.seq_unit[s] = int32_t(carry_u + iu - sh.units);
-    }
-    carry_c += tc;
-    carry_u += tu;
-  }
-  if (t == 0) {
-    tot_cost_s = carry_c;
-    tot_units_s = carry_u;
-  }
-  __syncthreads();
-  // Capacity guard: the workspace is sized from the descriptor; inconsistent
-  // seq_lens / query_start_loc contents could ask for more units -- plan nothing.
-  if (tot_units_s > a.max_units) {
-    if (t == 0) {
-      a.hdr->n_units = 0;
-      a.hdr->n_split = 0;
-      a.hdr->n_slots = 0;
-      a.hdr->grid = a.grid;
-      a.hdr->total_cost = 0;
-      a.hdr->partial_rows = 0;
-    }
-    return;
-  }
-  const int64_t C = tot_cost_s;
-  const int n_units = int(tot_units_s);
-  int64_t S = C / kCostMax;  // every slice at least one chunk of the heaviest kind wide
-  if (S > a.grid) S = a.grid;
-  if (S < 1 && C > 0) S = 1;
-  // phase 2: write units
-  for (int s = t; s < B; s += kPlanThreads) {
-    const int n = a.seq_lens[s];
-    const int qn = a.qsl[s + 1] - a.qsl[s];
-    if (qn <= 0) continue;
-    const int G = a.group;
-    const int rows = qn * G;
-    int64_t cost = a.seq_cost[s];
-    int u = a.seq_unit[s];
-    const bool split = rows <= kSplitRows;
-    const int nb = split ? 1 : ceil_div(rows, kBlockRows);
-    for (int g = 0; g < a.num_kv_heads; ++g) {
-      for (int rb = 0; rb < nb; ++rb) {
-        pa_plan_unit U;
-        U.seq = s;
-        U.kv_head = g;
-        U.row0 = split ? 0 : rb * kBlockRows;
-        U.n_rows = split ? rows : min(kBlockRows, rows - rb * kBlockRows);
-        U.n_keys = split ? n : block_keys(n, qn, G, rb);
-        U.n_chunks = ceil_div(U.n_keys, kChunkKeys);
-        U.kind = split ? 0 : 1;
-        U.cost_weight = split ? kCostKeySplit : kCostRowSplit;
-        U.cost0 = cost;
-        const int64_t last = cost + int64_t(U.n_chunks - 1) * U.cost_weight;
-        U.n_pieces = int(((last + 1) * S - 1) / C - ((cost + 1) * S - 1) / C + 1);
-        U.piece_base = 0;
-        cost += int64_t(U.n_chunks) * U.cost_weight;
-        a.units[u++] = U;
+// One grain: the chunks whose start cost lies in [c0, c1), unit by unit.
+template <class TR>
+__device__ void run_grain(const AttnArgs& A, int grain, Smem<TR>& sm) {
+  const PlanView& v = A.plan;
+  const SlotStart st = load_slot(ro(v.slots) + grain);
+  const int64_t c0 = st.c0, c1 = st.c1;
+  if (c0 >= c1) return;
+  const cptr<int32_t> seq_lens = ro(v.seq_lens);
+  const cptr<int32_t> qsl = ro(v.qsl);
+  UnitCursor cu;
+  cursor_from_slot(cu, v, st);
+  do {
+    const pa_plan_unit& U = cu.U;
+    if (U.cost0 >= c1) break;
+    const int64_t w = U.cost_weight;
+    const int64_t cs = chunk_start(U, 0);
+    const int i0 = int(c0 > cs ? (c0 - cs + w - 1) / w : 0);
+    const int64_t e = c1 > cs ? (c1 - cs + w - 1) / w : 0;
+    const int i1 = int(e < U.n_chunks ? e : U.n_chunks);
+    if (i0 < i1) {
+      // a grain holds at most two pieces of split units: the one it starts inside (position 0)
+      // and the one it ends inside (position 1)
+      const int part = (i0 > 0 || i1 < U.n_chunks) ? 2 * grain + (cs < c0 ? 0 : 1) : -1;
+      if (U.kind == 0) {
+        if (U.n_rows <= 16) run_keysplit<TR, 1>(A, U, i0, i1, part, sm);
+        else run_keysplit<TR, 2>(A, U, i0, i1, part, sm);
+      } else {
+        run_rowsplit<TR>(A, U, i0, i1, part, sm);
       }
     }
-  }
-  __syncthreads();
-  // phase 3: partial-row storage and the list of split units
-  int64_t carry_r = 0, carry_s = 0;
-  for (int base = 0; base < n_units; base += kPlanThreads) {
-    const int u = base + t;
-    int64_t rows = 0, flag = 0;
-    if (u < n_units) {
-      const pa_plan_unit& U = a.units[u];
-      if (U.n_pieces > 1) {
-        rows = int64_t(U.n_pieces) * U.n_rows;
-        flag = 1;
-      }
-    }
-    const int last_t = kPlanThreads - 1 < n_units - base ? kPlanThreads - 1 : n_units - base - 1;
-    const int64_t ir = block_scan(rows, tmp);
-    const int64_t tr = tmp[last_t];
+  } while (cursor_next(cu, v, seq_lens, qsl));
+}
+
+// Persistent launch: workgroup b runs grain b, then takes grains grid, grid+1, ... from the
+// counter until none is left; the grab for its next grain is issued when a grain starts.
+template <class TR>
+__global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs A) {
+  __shared__ Smem<TR> sm;
+  __shared__ int next_grain;
+  const int n_grains = ro(A.plan.hdr)->n_slots;
+  int g = blockIdx.x;
+  while (g < n_grains) {
+    int ahead = 0;
+    if (threadIdx.x == 0)
+      ahead = int(gridDim.x) + __hip_atomic_fetch_add(A.grab, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    run_grain<TR>(A, g, sm);
     __syncthreads();
-    const int64_t is = block_scan(flag, tmp);
-    const int64_t ts = tmp[last_t];
+    if (threadIdx.x == 0) next_grain = ahead;
     __syncthreads();
-    if (u < n_units) {
-      a.units[u].piece_base = int32_t(carry_r + ir - rows);
-      if (flag) a.split[carry_s + is - 1] = u;
-    }
-    carry_r += tr;
-    carry_s += ts;
-  }
-  if (t == 0) {
-    const bool fits = carry_r <= a.max_partial_rows;  // holds by construction; guards the workspace
-    a.hdr->n_units = fits ? n_units : 0;
-    a.hdr->n_split = fits ? int32_t(carry_s) : 0;
-    a.hdr->n_slots = fits ? int32_t(S) : 0;
-    a.hdr->grid = a.grid;
-    a.hdr->total_cost = C;
-    a.hdr->partial_rows = carry_r;
+    g = next_grain;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of partial rows: one workgroup per split unit (grid-stride).
+// Planner: one workgroup writes the per-sequence cost prefix and the header.
+// ---------------------------------------------------------------------------
+constexpr int kScanThreads = 1024;
+
+// Exclusive scan of one int64 per thread over the workgroup; *total gets the sum.
+__device__ int64_t block_exclusive_scan(int64_t x, int64_t* wave_tot, int64_t* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  constexpr int kNW = kScanThreads / 64;
+  int64_t incl = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wave_tot[wid] = incl;
+  __syncthreads();
+  if (wid == 0) {
+    int64_t t = lane < kNW ? wave_tot[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < kNW; off <<= 1) {
+      const int64_t y = __shfl_up(t, off);
+      if (lane >= off) t += y;
+    }
+    if (lane < kNW) wave_tot[lane] = t;
+  }
+  __syncthreads();
+  const int64_t excl = incl - x + (wid > 0 ? wave_tot[wid - 1] : 0);
+  *total = wave_tot[kNW - 1];
+  __syncthreads();
+  return excl;
+}
+
+constexpr int kPlanLdsSeqs = 4096;  // sequences whose cost prefix the planner keeps in LDS
+
+__global__ __launch_bounds__(kScanThreads) void plan_kernel(PlanArgs a) {
+  __shared__ int64_t wave_tot[kScanThreads / 64];
+  __shared__ int64_t lds_cost[kPlanLdsSeqs + 1];
+  int64_t carry = 0, units = 0;
+  for (int base = 0; base < a.num_seqs; base += kScanThreads) {
+    const int s = base + threadIdx.x;
+    int64_t cost = 0, nu = 0;
+    if (s < a.num_seqs) {
+      const SeqUnits q = seq_units(a.seq_lens[s], a.qsl[s + 1] - a.qsl[s], a.group);
+      cost = int64_t(a.num_kv_heads) * q.per_head;
+      nu = int64_t(a.num_kv_heads) * q.nb;
+    }
+    int64_t tot, tot_u;
+    const int64_t ex = block_exclusive_scan(cost, wave_tot, &tot);
+    block_exclusive_scan(nu, wave_tot, &tot_u);
+    if (s < a.num_seqs) {
+      a.seq_cost[s] = carry + ex;
+      if (s < kPlanLdsSeqs) lds_cost[s] = carry + ex;
+    }
+    carry += tot;
+    units += tot_u;
+  }
+  const int64_t C = carry;
+  int64_t S = C / kCostMax;  // every grain at least one chunk of the heaviest kind wide
+  if (S > int64_t(a.grid) * kGrainsPerWorkgroup) S = int64_t(a.grid) * kGrainsPerWorkgroup;
+  if (S < 1 && C > 0) S = 1;
+  if (threadIdx.x == 0) {
+    *a.grab = 0;
+    a.seq_cost[a.num_seqs] = C;
+    a.hdr->n_units = int32_t(units);
+    a.hdr->n_slots = int32_t(S);
+    a.hdr->grid = a.grid;
+    a.hdr->num_seqs = a.num_seqs;
+    a.hdr->total_cost = C;
+    a.hdr->grains_per_workgroup = kGrainsPerWorkgroup;
+    a.hdr->reserved = 0;
+  }
+  __syncthreads();  // seq_cost (global and LDS) complete
+  // where every slot starts: one binary search per slot
+  PlanView v;
+  v.seq_lens = a.seq_lens;
+  v.qsl = a.qsl;
+  v.hdr = a.hdr;
+  v.seq_cost = a.seq_cost;
+  v.slots = a.slots;
+  v.num_seqs = a.num_seqs;
+  v.num_kv_heads = a.num_kv_heads;
+  v.group = a.group;
+  for (int k = threadIdx.x; k < S; k += kScanThreads) {
+    SlotStart r;
+    r.c0 = slice_begin(k, S, C);
+    r.c1 = slice_begin(k + 1, S, C);
+    UnitCursor cu;
+    if (a.num_seqs <= kPlanLdsSeqs) cursor_find(cu, v, a.seq_lens, a.qsl, lds_cost, r.c0);
+    else cursor_find(cu, v, a.seq_lens, a.qsl, a.seq_cost, r.c0);
+    r.seq_base = cu.seq_base;
+    r.unit_cost0 = cu.U.cost0;
+    r.s = cu.s;
+    r.g = cu.g;
+    r.rb = cu.rb;
+    r.n = cu.q.n;
+    r.qn = cu.q.qn;
+    r.pad[0] = r.pad[1] = r.pad[2] = 0;
+    a.slots[k] = r;
+  }
+}
+
+// Plan inspection: one thread walks every unit in cost order (tests and debugging only).
+__global__ void plan_units_kernel(PlanView v, pa_plan_unit* out, int64_t max_units) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  const int64_t C = v.hdr->total_cost, S = v.hdr->n_slots;
+  if (C <= 0) return;
+  UnitCursor cu;
+  cursor_find(cu, v, v.seq_lens, v.qsl, v.seq_cost, 0);
+  int64_t i = 0;
+  do {
+    pa_plan_unit U = cu.U;
+    const int64_t first = slot_of(chunk_start(U, 0), S, C);
+    const int64_t last = slot_of(chunk_start(U, U.n_chunks - 1), S, C);
+    U.first_slot = int32_t(first);
+    U.n_pieces = int32_t(last - first + 1);
+    if (i < max_units) out[i] = U;
+    ++i;
+  } while (cursor_next(cu, v, v.seq_lens, v.qsl));
+}
+
+// ---------------------------------------------------------------------------
+// Log-sum-exp merge of split units.  Workgroup k looks at slice boundary k; the
+// unit that boundary cuts is merged by the workgroup of its first boundary.
 // ---------------------------------------------------------------------------
 template <class TR>
 __device__ __forceinline__ void merge_row(const float* o_parts, const float* lse_parts, int64_t stride_rows,
@@ -830,23 +1191,68 @@ template <class TR>
 __global__ __launch_bounds__(kThreads) void merge_planned_kernel(MergeArgs a) {
   constexpr int kLanesPerRow = TR::D / 4;
   constexpr int kRowsPerPass = kThreads / kLanesPerRow;
-  const int n_split = a.hdr->n_split;
+  constexpr int kMaxPass = kPartRows / kRowsPerPass;
+  const PlanView& v = a.plan;
+  const pa_plan_header* hdr = v.hdr;
+  const int64_t S = hdr->n_slots, C = hdr->total_cost;
+  const int k = blockIdx.x;
+  if (k == 0 && threadIdx.x == 0) *a.grab = 0;  // the attention launch has finished: ready for the next one
+  if (k == 0 || k >= S) return;
+  UnitCursor cu;
+  cursor_from_slot(cu, v, load_slot(ro(v.slots) + k));  // the unit holding the first cost of grain k
+  const pa_plan_unit& U = cu.U;
+  const int64_t first = slot_of(chunk_start(U, 0), S, C);
+  const int64_t last = slot_of(chunk_start(U, U.n_chunks - 1), S, C);
+  if (first != k - 1 || last < k) return;  // boundary k does not open this unit's split
+  const int n_pieces = int(last - first + 1);
+  // piece j sits in slot first + j: position 1 (the slot's last unit) for j = 0, position 0 after
+  const int q0 = ro(v.qsl)[U.seq];
   const int d4 = threadIdx.x % kLanesPerRow;
-  for (int i = blockIdx.x; i < n_split; i += gridDim.x) {
-    const pa_plan_unit U = a.units[a.split[i]];
-    const int q0 = a.qsl[U.seq];
-    for (int r = threadIdx.x / kLanesPerRow; r < U.n_rows; r += kRowsPerPass) {
-      const int64_t prow = int64_t(U.piece_base) + r;
-      float lse;
-      f32x4_t o;
-      merge_row<TR>(a.part_o + prow * TR::D, a.part_lse + prow, U.n_rows, U.n_pieces, d4, &lse, &o);
-      const int rr = U.row0 + r;
-      const int tk = rr / a.group;
-      const int head = U.kv_head * a.group + (rr - tk * a.group);
-      const int64_t orow = int64_t(q0 + tk) * a.num_q_heads + head;
-      TR::store_out(static_cast<char*>(a.out) + (orow * TR::D + 4 * d4) * TR::kEb, o);
-      if (d4 == 0) a.lse[orow] = lse;
+  const int r0 = threadIdx.x / kLanesPerRow;
+  // online merge over the pieces, all rows of this thread in flight together
+  float M[kMaxPass], L[kMaxPass];
+  f32x4_t O[kMaxPass];
+#pragma unroll
+  for (int i = 0; i < kMaxPass; ++i) {
+    M[i] = -INFINITY;
+    L[i] = 0.f;
+    O[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int j = 0; j < n_pieces; ++j) {
+    const int64_t pbase = (2 * (first + j) + (j == 0 ? 1 : 0)) * int64_t(kPartRows);
+    float lj[kMaxPass];
+    f32x4_t oj[kMaxPass];
+#pragma unroll
+    for (int i = 0; i < kMaxPass; ++i) {
+      const int r = r0 + i * kRowsPerPass;
+      if (r < U.n_rows) {
+        lj[i] = a.part_lse[pbase + r];
+        oj[i] = *reinterpret_cast<const f32x4_t*>(a.part_o + (pbase + r) * TR::D + 4 * d4);
+      }
     }
+#pragma unroll
+    for (int i = 0; i < kMaxPass; ++i) {
+      const int r = r0 + i * kRowsPerPass;
+      if (r < U.n_rows && lj[i] != -INFINITY) {  // a piece that saw no key of this row adds nothing
+        const float m_new = fmaxf(M[i], lj[i]);
+        const float a_old = fast_exp2((M[i] - m_new) * kLog2e);
+        const float a_new = fast_exp2((lj[i] - m_new) * kLog2e);
+        L[i] = L[i] * a_old + a_new;
+        O[i] = O[i] * a_old + oj[i] * a_new;
+        M[i] = m_new;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kMaxPass; ++i) {
+    const int r = r0 + i * kRowsPerPass;
+    if (r >= U.n_rows) continue;
+    const int rr = U.row0 + r;
+    const int tk = rr / v.group;
+    const int head = U.kv_head * v.group + (rr - tk * v.group);
+    const int64_t orow = int64_t(q0 + tk) * a.num_q_heads + head;
+    TR::store_out(static_cast<char*>(a.out) + (orow * TR::D + 4 * d4) * TR::kEb, O[i] * (1.f / L[i]));
+    if (d4 == 0) a.lse[orow] = M[i] + fast_log2(L[i]) * kLn2;
   }
 }
 
@@ -924,7 +1330,12 @@ __global__ void validate_kernel(int B, int T, int NP, int max_pages, const int32
 static hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 int launch_plan(const PlanArgs& a, void* stream) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, as_stream(stream), a);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kScanThreads), 0, as_stream(stream), a);
+  return int(hipGetLastError());
+}
+
+int launch_plan_units(const PlanView& v, pa_plan_unit* units, int64_t max_units, void* stream) {
+  hipLaunchKernelGGL(plan_units_kernel, dim3(1), dim3(64), 0, as_stream(stream), v, units, max_units);
   return int(hipGetLastError());
 }
 

@@ -163,7 +163,7 @@ def test_deterministic_and_staged_equals_one_shot():
     pa.plan(desc, t["seq_lens"], t["query_start_loc"], ws)
     pa.attention_planned(desc, t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
                          t["query_start_loc"], out, lse, ws)
-    pa.merge_planned(desc, t["query_start_loc"], out, lse, ws)
+    pa.merge_planned(desc, t["seq_lens"], t["query_start_loc"], out, lse, ws)
     torch.cuda.synchronize()
     assert torch.equal(o1, out) and torch.equal(l1, lse)
 
@@ -188,47 +188,57 @@ def test_gather_kv_bit_exact(dt, D):
             assert not np.any(got[:, n:].view(np.uint8))  # keys past the end are zero bits
 
 
-def test_plan_covers_every_row_and_chunk_once():
-    for c in (2, 3, 4):
-        w = W.make_config(c)
-        t = pa.to_device(w)
-        desc = pa.make_desc(t["q"], t["k_pool"], t["block_table"], t["seq_lens"], w.scale)
-        ws = pa.alloc_workspace(desc)
-        pa.plan(desc, t["seq_lens"], t["query_start_loc"], ws)
-        hdr, units = pa.plan_read(desc, ws)
-        G = w.num_q_heads // w.num_kv_heads
-        ql = w.q_lens()
-        # rows: every (sequence, kv head, window row) exactly once
-        seen = set()
-        cost = 0
-        for u in units:
-            assert u["cost0"] == cost
-            cost += u["n_chunks"] * u["cost_weight"]
-            for r in range(u["row0"], u["row0"] + u["n_rows"]):
-                key = (u["seq"], u["kv_head"], r)
-                assert key not in seen
-                seen.add(key)
-            n = int(w.seq_lens[u["seq"]])
-            last_tok = (u["row0"] + u["n_rows"] - 1) // G
-            assert u["n_keys"] == n - int(ql[u["seq"]]) + last_tok + 1  # causal tile skip
-            assert u["n_chunks"] == math.ceil(u["n_keys"] / 32)
-        assert len(seen) == int((ql * G).sum()) * w.num_kv_heads
-        assert cost == hdr["total_cost"]
-        # slices: the chunks of every unit split into contiguous pieces, one per slice boundary crossed
-        S, C = hdr["n_slots"], hdr["total_cost"]
-        assert 1 <= S <= hdr["grid"]
-        bounds = [k * C // S for k in range(S + 1)]
-        slot_of = lambda x: bisect.bisect_right(bounds, x) - 1  # noqa: E731
-        split_rows = 0
-        for u in units:
-            owners = [slot_of(u["cost0"] + i * u["cost_weight"]) for i in range(u["n_chunks"])]
-            distinct = sorted(set(owners))
-            assert distinct == list(range(distinct[0], distinct[-1] + 1))
-            assert u["n_pieces"] == len(distinct)
-            if u["n_pieces"] > 1:
-                assert u["piece_base"] == split_rows
-                split_rows += u["n_pieces"] * u["n_rows"]
-        assert split_rows == hdr["partial_rows"]
+def cpu_plan(w, grid, grains_per_workgroup):
+    """The plan's units re-derived on the CPU from the stated rules (sequence, kv head, row block order;
+    key-split units for q_len*G <= 32 rows, else 128-row blocks; a unit costs 12 + chunks * weight
+    (weight 4 key-split, 5 row-split) and its chunk i starts at cost0 + 12 + i * weight; the cost axis
+    is cut into min(grains_per_workgroup * grid, total // 5) equal grains)."""
+    G = w.num_q_heads // w.num_kv_heads
+    units, cost = [], 0
+    for s in range(w.num_seqs):
+        n, qn = int(w.seq_lens[s]), int(w.q_lens()[s])
+        if qn == 0:
+            continue
+        rows = qn * G
+        split = rows <= 32
+        nb = 1 if split else -(-rows // 128)
+        for g in range(w.num_kv_heads):
+            for rb in range(nb):
+                r0 = 0 if split else rb * 128
+                nr = rows if split else min(128, rows - r0)
+                nk = n if split else n - qn + (r0 + nr - 1) // G + 1
+                nch = -(-nk // 32)
+                wgt = 4 if split else 5
+                units.append(dict(seq=s, kv_head=g, row0=r0, n_rows=nr, n_keys=nk, n_chunks=nch,
+                                  kind=0 if split else 1, cost_weight=wgt, cost0=cost))
+                cost += 12 + nch * wgt
+    S = max(1, min(grains_per_workgroup * grid, cost // 5))
+    bounds = [k * cost // S for k in range(S + 1)]
+    for u in units:
+        owners = [bisect.bisect_right(bounds, u["cost0"] + 12 + i * u["cost_weight"]) - 1
+                  for i in range(u["n_chunks"])]
+        assert sorted(set(owners)) == list(range(owners[0], owners[-1] + 1))  # contiguous pieces, no gaps
+        u["first_slot"], u["n_pieces"] = owners[0], owners[-1] - owners[0] + 1
+    return units, cost, S
+
+
+@pytest.mark.parametrize("c", [2, 3, 4])
+def test_plan_matches_cpu_rederivation(c):
+    w = W.make_config(c)
+    t = pa.to_device(w)
+    desc = pa.make_desc(t["q"], t["k_pool"], t["block_table"], t["seq_lens"], w.scale)
+    ws = pa.alloc_workspace(desc)
+    pa.plan(desc, t["seq_lens"], t["query_start_loc"], ws)
+    hdr, units = pa.plan_read(desc, t["seq_lens"], t["query_start_loc"], ws)
+    assert 1 <= hdr["grains_per_workgroup"] <= 8
+    ref, cost, S = cpu_plan(w, hdr["grid"], hdr["grains_per_workgroup"])
+    assert hdr["total_cost"] == cost and hdr["n_slots"] == S and hdr["n_units"] == len(ref)
+    assert 1 <= S <= hdr["grains_per_workgroup"] * hdr["grid"]
+    assert units == ref  # bit-exact, field by field
+    # every (sequence, kv head, window row) exactly once
+    G = w.num_q_heads // w.num_kv_heads
+    seen = {(u["seq"], u["kv_head"], r) for u in units for r in range(u["row0"], u["row0"] + u["n_rows"])}
+    assert len(seen) == sum(u["n_rows"] for u in units) == int((w.q_lens() * G).sum()) * w.num_kv_heads
 
 
 def test_validate_reports_bad_content():
@@ -257,3 +267,40 @@ def test_merge_op_against_oracle_merge():
         torch.cuda.synchronize()
         assert np.abs(go.cpu().numpy() - ro).max() <= 1e-5
         assert np.abs(gl.cpu().numpy() - rl).max() <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# softmax numerics: extreme score gaps, negative scale
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dt,D,maxq", [("bf16", 128, 1), ("bf16", 128, 70), ("f32", 64, 5)])
+def test_peaked_rows_select_the_dominant_key(dt, D, maxq):
+    """One key per sequence scores ~500 (natural log units) above the rest: every row that can
+    see it must return that key's V row; any row-inconsistent running maximum would overflow."""
+    w = W.make_random(61, 6, 400, 8, 2, D, dt, max_q=maxq)
+    k = W.bf16_bits_to_f32(w.k_pool) if dt == "bf16" else w.k_pool.copy()
+    qf = W.bf16_bits_to_f32(w.q) if dt == "bf16" else w.q.copy()
+    rng = np.random.default_rng(3)
+    peak = []
+    for s in range(w.num_seqs):
+        n, q0, q1 = int(w.seq_lens[s]), int(w.query_start_loc[s]), int(w.query_start_loc[s + 1])
+        j = int(rng.integers(0, max(1, n - (q1 - q0) + 1)))  # visible to every row of the window
+        pg, slot = int(w.block_table[s, j // 16]), j % 16
+        for g in range(w.num_kv_heads):
+            heads = slice(g * 4, g * 4 + 4)
+            direction = qf[q0:q1, heads].sum(axis=(0, 1)) if q1 > q0 else np.ones(D, np.float32)
+            k[pg, g, slot, :] = (np.sign(direction) * 8.0).astype(np.float32)
+        peak.append((s, j))
+    k_pool = W.f32_to_bf16_bits(k) if dt == "bf16" else k
+    import oracle_pins as P
+    w2 = P._replace(w, k_pool=k_pool)
+    out, lse = run_gpu(w2)
+    check(w2, out, lse)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+
+
+def test_negative_scale():
+    w = W.make_random(71, 5, 300, 8, 2, 128, "bf16", max_q=40)
+    import oracle_pins as P
+    w2 = P._replace(w, scale=-0.07)
+    out, lse = run_gpu(w2)
+    check(w2, out, lse)
