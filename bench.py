@@ -1,8 +1,9 @@
 """Benchmark of paged-KV GQA attention on one MI355X.
 
-A step is one full pass of the path over one batch: pa_plan (work list),
-pa_attention_planned (the persistent attention kernel) and pa_merge_planned
-(log-sum-exp merge of key-split rows) -- exactly what pa_attention enqueues.
+A step is one full pass of the path over one batch: one pa_attention call, a
+single persistent kernel launch that plans its own grain, computes it and merges
+the key-split rows it completes (with --staged: pa_plan + pa_attention_planned +
+pa_merge_planned, the same result in three launches).
 Inputs are resident in HBM before the timed region.  The K/V pools are held in
 several copies and step i reads copy i % n_copies, so that every step's K/V
 were last touched more than 1 GiB of traffic earlier (the 256 MB MALL cannot
@@ -56,18 +57,60 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, kernel: str):
     """HBM bytes per launch of the attention kernel from the committed counter runs,
-    or None when the counters were taken on other kernel sources or another workload."""
+    or None when the counters were taken on other kernel sources, another kernel or another workload."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     entry = rec.get("workloads", {}).get(workload)
-    if not entry or entry.get("kernel_sha") != kernel_hash():
+    if not entry or entry.get("kernel_sha") != kernel_hash() or entry.get("kernel") != kernel:
         return None
     return entry.get("hbm_bytes_per_launch")
+
+
+CALIBRATION_BYTES = 512 << 20  # the plain device copy that --copy-calibration runs, CALIBRATION_COPIES times
+CALIBRATION_COPIES = 3
+
+
+def record_traffic(workload: str, fetch_csv: str, write_csv: str, kernel: str) -> dict:
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) of a
+    `--copy-calibration` bench run into HBM bytes per attention launch and store them in the traffic
+    record under `workload`.  Each counter is scaled by (known copy bytes) / (what it reads for the
+    calibration copy: the copy dispatches that moved 512 MiB)."""
+    import csv
+
+    def per_dispatch(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        target_rows = [r for r in rows if f"pa::{kernel}<" in r["Kernel_Name"]]
+        target = [float(r["Counter_Value"]) for r in target_rows]
+        last = max(int(r["Dispatch_Id"]) for r in target_rows)
+        # the calibration copies: the largest copies dispatched after the last attention launch
+        after = sorted(float(r["Counter_Value"]) for r in rows
+                       if "copyBuffer" in r["Kernel_Name"] and int(r["Dispatch_Id"]) > last)
+        calib_runs = after[-CALIBRATION_COPIES:]
+        factor = CALIBRATION_BYTES / 1024 / statistics.fmean(calib_runs)
+        return statistics.fmean(target) * 1024 * factor, factor, len(target)
+
+    fetch, f_fac, n_f = per_dispatch(fetch_csv, "FETCH_SIZE")
+    write, w_fac, n_w = per_dispatch(write_csv, "WRITE_SIZE")
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    rec.setdefault("workloads", {})[workload] = {
+        "kernel": kernel, "kernel_sha": kernel_hash(), "hbm_bytes_per_launch": round(fetch + write),
+        "fetch_bytes": round(fetch), "write_bytes": round(write),
+        "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4), "dispatches": [n_f, n_w]}
+    rec["method"] = ("rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE, separate runs, mean KiB per dispatch of "
+                     "the attention kernel, each scaled by 512 MiB / (the counter's reading for a 512 MiB "
+                     "device copy in the same run)")
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    return rec["workloads"][workload]
 
 
 def cpu_baseline(w, alg_bytes: int, min_seconds: float = 10.0, max_runs: int = 5):
@@ -94,9 +137,14 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--part", default="all", choices=["all", "prefill", "decode"],
                     help="configuration 3 only: time its prefill chunks or its decode rows alone")
+    ap.add_argument("--staged", action="store_true",
+                    help="time pa_plan + pa_attention_planned + pa_merge_planned instead of the single launch")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for HBM counter calibration)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="store the HBM bytes per launch from two rocprofv3 counter CSVs of this workload "
+                         "and exit (no GPU use)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -105,6 +153,13 @@ def main() -> int:
               "the attention call shards by KV head with no exchange, so N GPUs run N independent copies.",
               file=sys.stderr)
         return 2
+
+    if args.record_traffic:
+        from paged_kv_cache_gqa_amd import workloads as W
+        name = W.CONFIG_NAMES[args.config] + ("" if args.part == "all" else f"-{args.part}-part")
+        kernel = "attention_kernel" if args.staged else "attention_fused_kernel"
+        print(json.dumps(record_traffic(name, *args.record_traffic, kernel=kernel)))
+        return 0
 
     import numpy as np
     import torch
@@ -132,7 +187,7 @@ def main() -> int:
     lse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    # pre-marshalled arguments: the host enqueues three calls per step
+    # pre-marshalled arguments
     L = B.lib()
     import ctypes
     dref = ctypes.byref(desc)
@@ -147,13 +202,20 @@ def main() -> int:
                   vp(lse.data_ptr()), vp(ws.data_ptr()), wsn, sp)
 
     def step(i, ev=None):
-        rc = L.pa_plan(*plan_args)
-        if ev is not None:
-            ev[0].record(stream)
-        rc |= L.pa_attention_planned(*attn_args[i % n_copies])
-        if ev is not None:
-            ev[1].record(stream)
-        rc |= L.pa_merge_planned(*merge_args)
+        if args.staged:
+            rc = L.pa_plan(*plan_args)
+            if ev is not None:
+                ev[0].record(stream)
+            rc |= L.pa_attention_planned(*attn_args[i % n_copies])
+            if ev is not None:
+                ev[1].record(stream)
+            rc |= L.pa_merge_planned(*merge_args)
+        else:
+            if ev is not None:
+                ev[0].record(stream)
+            rc = L.pa_attention(*attn_args[i % n_copies])
+            if ev is not None:
+                ev[1].record(stream)
         if rc:
             raise RuntimeError(f"launch failed: {B.status_string(rc)}")
 
@@ -177,7 +239,7 @@ def main() -> int:
     if args.copy_calibration:  # a plain copy of known size, for scaling the HBM counters
         src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
-        for _ in range(3):
+        for _ in range(CALIBRATION_COPIES):
             dst.copy_(src)
         torch.cuda.synchronize()
 
@@ -188,8 +250,9 @@ def main() -> int:
     achieved = alg_bytes / (attn_mean * 1e-3) / 1e9
     tflops = alg_flops / (ms_per_step * 1e-3) / 1e12
     peak_tf = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+    kernel = "attention_kernel" if args.staged else "attention_fused_kernel"
     config = {"workload": f"{w.name} (configuration {args.config})", **DESCRIPTIONS[args.config],
-              "part": args.part,
+              "part": args.part, "path": "staged (3 launches)" if args.staged else "single launch",
               "page_size": 16, "seed": 1000 + args.config, "kv_pool_copies": n_copies,
               "algorithmic_bytes": alg_bytes, "algorithmic_flops": alg_flops}
     line = {
@@ -200,8 +263,8 @@ def main() -> int:
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "tflops": round(tflops, 3), "frac_of_mfma_peak": round(tflops / peak_tf, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
-                     "kernel": "pa::attention_kernel", "kernel_ms_mean": round(attn_mean, 5),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name, kernel),
+                     "kernel": f"pa::{kernel}", "kernel_ms_mean": round(attn_mean, 5),
                      "kernel_ms_p10_p90": [round(float(np.percentile(attn_ms, 10)), 5),
                                            round(float(np.percentile(attn_ms, 90)), 5)],
                      "per_launch": "algorithmic bytes of the whole batch (one launch covers the batch)"},

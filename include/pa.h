@@ -103,22 +103,38 @@ pa_status pa_check_desc(const pa_desc* desc);
 
 /*
  * Bytes of device workspace pa_attention needs for `desc` on the current HIP
- * device (the per-sequence cost prefix and, per workgroup of the persistent
- * launch, room for two partial results of up to 128 rows).  The size depends
- * only on the descriptor and on the device's compute-unit count.
+ * device (per workgroup of the persistent launch: an arrival counter and room
+ * for two partial results of up to 128 rows; the staged plan).  The size
+ * depends only on the descriptor and on the device's compute-unit count.
  * Writes *bytes; returns PA_ERR_NULL_POINTER, a descriptor error or PA_ERR_HIP.
+ *
+ * Workspace state: the arrival counters must be zero when pa_attention starts.
+ * Zero them once after allocating the workspace (pa_workspace_init, or a zero
+ * fill of the whole buffer); every pa_attention call leaves them zero, and so
+ * does pa_plan.  A workspace sized for a larger descriptor serves smaller ones.
  */
 pa_status pa_workspace_size(const pa_desc* desc, size_t* bytes);
 
 /*
+ * Zero the workspace's arrival counters (enqueues one small fill kernel on
+ * `stream`; no hipMemset, so it may be captured in a HIP graph).  Same checks
+ * as pa_attention on desc / workspace / workspace_bytes.
+ */
+pa_status pa_workspace_init(const pa_desc* desc, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Causal GQA attention over the paged cache for a mixed prefill / decode /
- * verify batch (the formula and layouts above).  Enqueues, in order on
- * `stream`: the planner (work list from seq_lens and query_start_loc), the
- * attention kernel (one persistent launch over all rows: decode and verify
- * rows split keys across waves, prefill rows share K/V tiles through LDS;
- * every (row, head) whose keys were split is written as partial results), and
- * the log-sum-exp merge of split rows.  `workspace` must hold at least
- * pa_workspace_size bytes and be 256-byte aligned.  T_q == 0 enqueues nothing.
+ * verify batch (the formula and layouts above), as ONE kernel launch on
+ * `stream`: every workgroup of the persistent launch derives the work list
+ * from seq_lens and query_start_loc (units of (sequence, kv head, row block)
+ * laid on one cost axis cut into equal grains), runs its grain -- decode and
+ * verify rows split keys across waves, prefill rows share K/V chunks through
+ * LDS -- and the workgroup that finishes the last piece of a unit whose keys
+ * were split across grains merges the pieces by log-sum-exp.  `workspace` must
+ * hold at least pa_workspace_size bytes, be 256-byte aligned and have zero
+ * arrival counters (see pa_workspace_size).  T_q == 0 enqueues nothing.
+ * Results are bitwise reproducible for a given batch shape and device, and
+ * bitwise equal to those of the staged path below.
  */
 pa_status pa_attention(const pa_desc* desc, const void* q, const void* k_pool, const void* v_pool,
                        const int32_t* block_table, const int32_t* seq_lens,
@@ -126,13 +142,14 @@ pa_status pa_attention(const pa_desc* desc, const void* q, const void* k_pool, c
                        size_t workspace_bytes, void* stream);
 
 /*
- * The three stages of pa_attention, for callers that time or reuse them.
- * pa_plan writes the plan into the workspace (it reads only seq_lens and
- * query_start_loc; a plan stays valid while those and desc are unchanged).
- * pa_attention_planned runs the attention kernel on a planned workspace:
- * unsplit rows get their final out/lse, split rows leave partial results in
- * the workspace.  pa_merge_planned combines those partials into out/lse.
- * pa_attention == pa_plan + pa_attention_planned + pa_merge_planned.
+ * The same computation in three stages, for callers that inspect, time or
+ * reuse them.  pa_plan writes the plan into the workspace (it reads only
+ * seq_lens and query_start_loc; a plan stays valid while those and desc are
+ * unchanged) and zeroes the arrival counters.  pa_attention_planned runs the
+ * attention kernel on a planned workspace: unsplit rows get their final
+ * out/lse, split rows leave partial results in the workspace.
+ * pa_merge_planned combines those partials into out/lse.  The three together
+ * give bitwise the result of pa_attention.
  */
 pa_status pa_plan(const pa_desc* desc, const int32_t* seq_lens, const int32_t* query_start_loc,
                   void* workspace, size_t workspace_bytes, void* stream);
@@ -166,9 +183,7 @@ typedef struct pa_plan_unit {
 
 typedef struct pa_plan_header {
   int32_t n_units, n_slots, grid, num_seqs;
-  int64_t total_cost;
-  int32_t grains_per_workgroup; /* n_slots = max(1, min(grid * this, total_cost / 5)) */
-  int32_t reserved;
+  int64_t total_cost, reserved;
 } pa_plan_header;
 
 /*

@@ -45,8 +45,7 @@ class PlanUnit(ctypes.Structure):
 
 class PlanHeader(ctypes.Structure):
     _fields_ = [("n_units", ctypes.c_int32), ("n_slots", ctypes.c_int32), ("grid", ctypes.c_int32),
-                ("num_seqs", ctypes.c_int32), ("total_cost", ctypes.c_int64), ("grains_per_workgroup", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("num_seqs", ctypes.c_int32), ("total_cost", ctypes.c_int64), ("reserved", ctypes.c_int64)]
 
 
 _lib = None
@@ -70,6 +69,7 @@ def lib():
         L.pa_status_string.argtypes = [ctypes.c_int]
         L.pa_check_desc.argtypes = [dp]
         L.pa_workspace_size.argtypes = [dp, ctypes.POINTER(sz)]
+        L.pa_workspace_init.argtypes = [dp, vp, sz, vp]
         L.pa_attention.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.pa_plan.argtypes = [dp, vp, vp, vp, sz, vp]
         L.pa_attention_planned.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -79,7 +79,7 @@ def lib():
         L.pa_gather_kv.argtypes = [dp, i32, vp, vp, vp, i32, i32, vp, vp]
         L.pa_merge.argtypes = [i32, i64, i32, vp, vp, i32, vp, vp, vp]
         L.pa_validate.argtypes = [dp, vp, vp, vp, vp, sz, vp]
-        for name in ("pa_check_desc", "pa_workspace_size", "pa_attention", "pa_plan", "pa_attention_planned",
+        for name in ("pa_check_desc", "pa_workspace_size", "pa_workspace_init", "pa_attention", "pa_plan", "pa_attention_planned",
                      "pa_merge_planned", "pa_plan_read", "pa_gather_kv", "pa_merge", "pa_validate"):
             getattr(L, name).restype = ctypes.c_int
         if L.pa_abi_version() != 1:
@@ -134,9 +134,18 @@ def workspace_size(desc: PaDesc) -> int:
     return int(n.value)
 
 
+def workspace_init(desc: PaDesc, workspace, stream=None) -> None:
+    """Zero the workspace's arrival counters (pa_workspace_init)."""
+    _check("pa_workspace_init", lib().pa_workspace_init(ctypes.byref(desc), _ptr(workspace), workspace.numel(),
+                                                        _stream(stream)))
+
+
 def alloc_workspace(desc: PaDesc, device=None) -> torch.Tensor:
-    """A 256-byte-aligned uint8 device buffer of workspace_size(desc) bytes (torch's allocator aligns)."""
-    return torch.empty(max(workspace_size(desc), 256), dtype=torch.uint8, device=device or "cuda")
+    """A 256-byte-aligned uint8 device buffer of workspace_size(desc) bytes (torch's allocator aligns),
+    initialised with pa_workspace_init."""
+    ws = torch.empty(max(workspace_size(desc), 256), dtype=torch.uint8, device=device or "cuda")
+    workspace_init(desc, ws)
+    return ws
 
 
 def _check_inputs(q, k_pool, v_pool, block_table, seq_lens, query_start_loc):

@@ -17,6 +17,7 @@ struct DeviceInfo {
   std::atomic<bool> ready{false};
   int cus = 0;
   int blocks_per_cu[2][2] = {{0, 0}, {0, 0}};  // [dtype][D == 128]
+  int max_grid = 0;                             // largest grid over dtypes and head dims
 };
 
 constexpr int kMaxDevices = 64;
@@ -24,12 +25,13 @@ std::mutex g_mu;
 DeviceInfo g_dev[kMaxDevices];
 
 // Compute units of the current device and how many attention workgroups each holds.
-pa_status device_grid(const pa_desc& d, int* grid) {
+pa_status device_grid(const pa_desc& d, int* grid, int* max_grid = nullptr) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_ERR_HIP;
   DeviceInfo& info = g_dev[dev];
   if (info.ready.load(std::memory_order_acquire)) {
     *grid = info.cus * info.blocks_per_cu[d.dtype == PA_BF16 ? 1 : 0][d.head_dim == 128 ? 1 : 0];
+    if (max_grid) *max_grid = info.max_grid;
     return PA_OK;
   }
   std::lock_guard<std::mutex> lock(g_mu);
@@ -42,18 +44,20 @@ pa_status device_grid(const pa_desc& d, int* grid) {
         const int n = pa::attention_blocks_per_cu(dt, big ? 128 : 64);
         if (n <= 0) return PA_ERR_HIP;
         info.blocks_per_cu[dt][big] = n;
+        if (cus * n > info.max_grid) info.max_grid = cus * n;
       }
     info.cus = cus;
     info.ready.store(true, std::memory_order_release);
   }
   *grid = info.cus * info.blocks_per_cu[d.dtype == PA_BF16 ? 1 : 0][d.head_dim == 128 ? 1 : 0];
+  if (max_grid) *max_grid = info.max_grid;
   return PA_OK;
 }
 
 struct Ws {
   WsLayout L;
   pa_plan_header* hdr;
-  int32_t* grab;
+  int32_t* arrive;
   int64_t* seq_cost;
   pa::SlotStart* slots;
   float* part_lse;
@@ -66,7 +70,7 @@ Ws carve(void* base, const WsLayout& L) {
   Ws w;
   w.L = L;
   w.hdr = reinterpret_cast<pa_plan_header*>(b + L.header);
-  w.grab = reinterpret_cast<int32_t*>(b + L.grab);
+  w.arrive = reinterpret_cast<int32_t*>(b + L.arrive);
   w.seq_cost = reinterpret_cast<int64_t*>(b + L.seq_cost);
   w.slots = reinterpret_cast<pa::SlotStart*>(b + L.slots);
   w.part_lse = reinterpret_cast<float*>(b + L.part_lse);
@@ -82,9 +86,10 @@ pa_status prepare(const pa_desc* desc, void* workspace, size_t workspace_bytes, 
   if (st != PA_OK) return st;
   if (!workspace) return PA_ERR_NULL_POINTER;
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return PA_ERR_BAD_SHAPE;
-  const pa_status gs = device_grid(*desc, grid);
+  int max_grid = 0;
+  const pa_status gs = device_grid(*desc, grid, &max_grid);
   if (gs != PA_OK) return gs;
-  const WsLayout L = pa::ws_layout(*desc, *grid);
+  const WsLayout L = pa::ws_layout(*desc, *grid, max_grid);
   if (workspace_bytes < L.total) return PA_ERR_WORKSPACE_TOO_SMALL;
   *ws = carve(workspace, L);
   return PA_OK;
@@ -115,7 +120,7 @@ pa::AttnArgs attn_args(const pa_desc& d, const void* q, const void* k, const voi
   a.lse = lse;
   a.part_o = ws.part_o;
   a.part_lse = ws.part_lse;
-  a.grab = ws.grab;
+  a.arrive = ws.arrive;
   a.num_q_heads = d.num_q_heads;
   a.max_pages = d.max_pages_per_seq;
   a.scale_log2 = std::fabs(d.scale) * 1.44269504088896340736f;
@@ -161,10 +166,10 @@ pa_status pa_workspace_size(const pa_desc* desc, size_t* bytes) {
   if (!desc || !bytes) return PA_ERR_NULL_POINTER;
   const pa_status st = pa_check_desc(desc);
   if (st != PA_OK) return st;
-  int grid = 0;
-  const pa_status gs = device_grid(*desc, &grid);
+  int grid = 0, max_grid = 0;
+  const pa_status gs = device_grid(*desc, &grid, &max_grid);
   if (gs != PA_OK) return gs;
-  *bytes = pa::ws_layout(*desc, grid).total;
+  *bytes = pa::ws_layout(*desc, grid, max_grid).total;
   return PA_OK;
 }
 
@@ -181,7 +186,7 @@ pa_status pa_plan(const pa_desc* desc, const int32_t* seq_lens, const int32_t* q
   a.hdr = ws.hdr;
   a.seq_cost = ws.seq_cost;
   a.slots = ws.slots;
-  a.grab = ws.grab;
+  a.arrive = ws.arrive;
   a.num_seqs = desc->num_seqs;
   a.num_kv_heads = desc->num_kv_heads;
   a.group = desc->num_q_heads / desc->num_kv_heads;
@@ -212,16 +217,13 @@ pa_status pa_merge_planned(const pa_desc* desc, const int32_t* seq_lens, const i
   if (!seq_lens || !qsl || !out || !lse) return PA_ERR_NULL_POINTER;
   pa::MergeArgs m;
   m.plan = plan_view(*desc, seq_lens, qsl, ws);
-  m.grab = ws.grab;
   m.part_o = ws.part_o;
   m.part_lse = ws.part_lse;
   m.out = out;
   m.lse = lse;
   m.num_q_heads = desc->num_q_heads;
   // one workgroup per grain boundary
-  return pa::launch_merge_planned(m, desc->dtype, desc->head_dim, grid * pa::kGrainsPerWorkgroup, stream) == 0
-             ? PA_OK
-             : PA_ERR_HIP;
+  return pa::launch_merge_planned(m, desc->dtype, desc->head_dim, grid, stream) == 0 ? PA_OK : PA_ERR_HIP;
 }
 
 pa_status pa_attention(const pa_desc* desc, const void* q, const void* k_pool, const void* v_pool,
@@ -233,12 +235,20 @@ pa_status pa_attention(const pa_desc* desc, const void* q, const void* k_pool, c
   if (desc->num_q_tokens == 0) return PA_OK;
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !qsl || !out || !lse || !workspace)
     return PA_ERR_NULL_POINTER;
-  pa_status r = pa_plan(desc, seq_lens, qsl, workspace, workspace_bytes, stream);
-  if (r != PA_OK) return r;
-  r = pa_attention_planned(desc, q, k_pool, v_pool, block_table, seq_lens, qsl, out, lse, workspace,
-                           workspace_bytes, stream);
-  if (r != PA_OK) return r;
-  return pa_merge_planned(desc, seq_lens, qsl, out, lse, workspace, workspace_bytes, stream);
+  int grid = 0;
+  Ws ws;
+  const pa_status ps = prepare(desc, workspace, workspace_bytes, &grid, &ws);
+  if (ps != PA_OK) return ps;
+  const pa::AttnArgs a = attn_args(*desc, q, k_pool, v_pool, block_table, seq_lens, qsl, out, lse, ws);
+  return pa::launch_attention_fused(a, desc->dtype, desc->head_dim, grid, stream) == 0 ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_workspace_init(const pa_desc* desc, void* workspace, size_t workspace_bytes, void* stream) {
+  int grid = 0;
+  Ws ws;
+  const pa_status st = prepare(desc, workspace, workspace_bytes, &grid, &ws);
+  if (st != PA_OK) return st;
+  return pa::launch_fill_zero(ws.arrive, ws.L.seq_cost - ws.L.arrive, stream) == 0 ? PA_OK : PA_ERR_HIP;
 }
 
 pa_status pa_plan_read(const pa_desc* desc, const int32_t* seq_lens, const int32_t* qsl, void* workspace,

@@ -17,29 +17,38 @@ constexpr int kSplitRows = 32;       // a unit with <= 32 rows splits its chunks
 constexpr int kBlockRows = 128;      // a larger unit is cut into blocks of 4 waves x 32 rows
 constexpr int kPlanThreads = 1024;
 
-// Cost weights per 32-key chunk on the planner's balancing axis.  A chunk of a
-// key-split unit (decode / verify: one wave streams 8 KiB of K and 8 KiB of V
-// from HBM) costs more wall time than a chunk of a row-split unit (prefill: the
-// workgroup reads the chunk once and four waves spend MFMA time on it).
+// Cost weights per 32-key chunk on the planner's balancing axis, fitted to
+// measured wall time on MI355X: a chunk of a row-split unit (prefill: up to 128
+// rows of MFMA work on one chunk staged in LDS) takes a little longer than a
+// chunk of a key-split unit (decode / verify: one wave streams 8 KiB of K and
+// 8 KiB of V from HBM for a few rows).
 constexpr int kCostKeySplit = 4;
 constexpr int kCostRowSplit = 5;
-constexpr int kCostMax = kCostKeySplit > kCostRowSplit ? kCostKeySplit : kCostRowSplit;
 // Fixed cost charged at the start of every unit (row and page-table loads, the
-// pipeline fill), so that slices that start many units get fewer chunks.
+// pipeline fill), so that grains that start many units get fewer chunks.
 constexpr int kCostUnitStart = 12;
 
-// The cost axis is cut into up to kGrainsPerWorkgroup * grid equal grains.  Grain
-// boundaries (and so every split of a unit's keys and its partial-result slots)
-// are fixed by the plan; which workgroup runs which grain is decided at run time
-// through an atomic counter, so faster workgroups take more grains.
 // bf16 decode: K of a chunk by global->LDS DMA (1) or straight to registers (0)
 #ifndef PA_K_VIA_LDS
 #define PA_K_VIA_LDS 1
 #endif
-#ifndef PA_GRAINS_PER_WORKGROUP
-#define PA_GRAINS_PER_WORKGROUP 1
-#endif
-constexpr int kGrainsPerWorkgroup = PA_GRAINS_PER_WORKGROUP;
+
+// The cost axis is cut into S equal grains, one per workgroup (measured on
+// MI355X: more, smaller grains per workgroup only added merge work), with
+//   S = min(grid, Ck / kCostKeySplit + Cr / (kRowGrainChunks * kCostRowSplit))
+// for Ck, Cr the total cost of key-split and of row-split units: decode work
+// may be cut down to one chunk per grain (its partial results are a few rows),
+// prefill work no finer than kRowGrainChunks chunks per grain (a piece of a
+// 128-row unit leaves 64 KiB of partial state to merge).  Grain boundaries --
+// and so every split of a unit's keys and its partial-result slots -- depend
+// only on the batch shape and the grid.
+constexpr int kRowGrainChunks = 8;
+inline __host__ __device__ int64_t grain_count(int64_t ck, int64_t cr, int grid) {
+  int64_t s = ck / kCostKeySplit + cr / (int64_t(kRowGrainChunks) * kCostRowSplit);
+  if (s > grid) s = grid;
+  if (s < 1 && ck + cr > 0) s = 1;
+  return s;
+}
 
 // Where grain k starts: its cost range and the unit holding cost c0, as written by the planner.
 struct SlotStart {
@@ -73,7 +82,8 @@ struct AttnArgs {
   float* lse;
   float* part_o;    // [grains][2][128][D]: per grain, the piece of its first and of its last unit
   float* part_lse;  // [grains][2][128]
-  int32_t* grab;    // grain counter (zeroed by the planner and by the merge)
+  int32_t* arrive;  // [grains]: pieces of the split unit whose first piece is in grain k that have
+                    // finished (single-launch path; zero between calls)
   int32_t num_q_heads;
   int32_t max_pages;
   float scale_log2;  // |scale| * log2(e): scores live in the base-2 domain
@@ -90,12 +100,11 @@ struct PlanArgs {
   int32_t num_kv_heads;
   int32_t group;
   int32_t grid;  // workgroups of the persistent attention launch
-  int32_t* grab;
+  int32_t* arrive;  // zeroed for a following single-launch call
 };
 
 struct MergeArgs {
   PlanView plan;
-  int32_t* grab;
   const float* part_o;
   const float* part_lse;
   void* out;
@@ -103,10 +112,11 @@ struct MergeArgs {
   int32_t num_q_heads;
 };
 
-// Workspace: [header | grain counter | per-sequence cost prefix | grain starts | partial lse |
-// partial o | unit list (plan inspection only)], every region 256-byte aligned.
+// Workspace: [header | arrival counters | per-sequence cost prefix | grain starts | partial lse |
+// partial o | unit list (plan inspection only)], every region 256-byte aligned.  The arrival
+// counters must be zero before a single-launch call; every call leaves them zero.
 struct WsLayout {
-  size_t header, grab, seq_cost, slots, part_lse, part_o, units, total;
+  size_t header, arrive, seq_cost, slots, part_lse, part_o, units, total;
   int64_t partial_rows, max_units;
 };
 
@@ -115,18 +125,21 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // Rows of one partial position: the largest unit.
 constexpr int kPartRows = kBlockRows;
 
-inline WsLayout ws_layout(const pa_desc& d, int grid) {
+// grid: workgroups of the attention launch for d; max_grid: the largest such grid of any dtype /
+// head dim on the device (the arrival counters sit at a fixed offset with a fixed size, so one
+// workspace serves every descriptor it is large enough for).
+inline WsLayout ws_layout(const pa_desc& d, int grid, int max_grid) {
   WsLayout L{};
   const int64_t B = d.num_seqs > 0 ? d.num_seqs : 0;
   const int64_t T = d.num_q_tokens > 0 ? d.num_q_tokens : 0;
   const int64_t G = d.num_kv_heads > 0 ? d.num_q_heads / d.num_kv_heads : 1;
   // units per sequence = Hkv * (1 if q_len*G <= 32 else ceil(q_len*G/128))
   L.max_units = int64_t(d.num_kv_heads) * (B + (T * G + kBlockRows - 1) / kBlockRows);
-  const int64_t grains = int64_t(grid) * kGrainsPerWorkgroup;
+  const int64_t grains = grid;
   L.partial_rows = grains * 2 * kPartRows;
   size_t off = 0;
   L.header = off;   off += align256(sizeof(pa_plan_header));
-  L.grab = off;     off += 256;
+  L.arrive = off;   off += align256(sizeof(int32_t) * size_t(max_grid > 0 ? max_grid : 1));
   L.seq_cost = off; off += align256(sizeof(int64_t) * size_t(B + 1));
   L.slots = off;    off += align256(sizeof(SlotStart) * size_t(grains > 0 ? grains : 1));
   L.part_lse = off; off += align256(sizeof(float) * size_t(L.partial_rows));
@@ -142,6 +155,9 @@ inline WsLayout ws_layout(const pa_desc& d, int grid) {
 namespace pa {
 int launch_plan(const PlanArgs& a, void* stream);
 int launch_attention(const AttnArgs& a, int dtype, int head_dim, int grid, void* stream);
+// single launch: in-kernel planning of each grain and merge of split units by their last piece
+int launch_attention_fused(const AttnArgs& a, int dtype, int head_dim, int grid, void* stream);
+int launch_fill_zero(void* p, size_t bytes, void* stream);
 int launch_merge_planned(const MergeArgs& a, int dtype, int head_dim, int grid, void* stream);
 int launch_plan_units(const PlanView& v, pa_plan_unit* units, int64_t max_units, void* stream);
 int launch_gather(int which, int dtype, int Hkv, int D, int max_pages, const void* pool,

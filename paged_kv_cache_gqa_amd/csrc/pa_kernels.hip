@@ -363,20 +363,37 @@ struct ChunkPages {
   const char* v1;
 };
 
+// Physical pages of chunk c (scalar loads of the block table; page b = page a past the end).
+struct PageIds {
+  int a, b;
+};
+__device__ __forceinline__ PageIds page_ids(cptr<int32_t> bt_row, int c, int n_seq) {
+  // both loads unconditional (no wait at a branch join); the second index is clamped to the
+  // sequence's last page, so it never reads past the pages the sequence owns
+  const bool two = c * kChunkKeys + kPage < n_seq;
+  const int ib = two ? 2 * c + 1 : 2 * c;
+  PageIds p;
+  p.a = __builtin_amdgcn_readfirstlane(bt_row[2 * c]);
+  p.b = __builtin_amdgcn_readfirstlane(bt_row[ib]);
+  return p;
+}
+
 template <class TR>
-__device__ __forceinline__ ChunkPages chunk_pages(const AttnArgs& A, cptr<int32_t> bt_row, int kvh, int c,
-                                                  int n_seq) {
-  const int key0 = c * kChunkKeys;
-  const int pa = __builtin_amdgcn_readfirstlane(bt_row[2 * c]);
-  const int pb = key0 + kPage < n_seq ? __builtin_amdgcn_readfirstlane(bt_row[2 * c + 1]) : pa;
+__device__ __forceinline__ ChunkPages pages_of(const AttnArgs& A, int kvh, PageIds p) {
   const int64_t blk = int64_t(kPage) * TR::D * TR::kEb;  // bytes of one (page, head) block
   const int64_t hkv = A.plan.num_kv_heads;
   ChunkPages cp;
-  cp.k0 = static_cast<const char*>(A.k_pool) + (int64_t(pa) * hkv + kvh) * blk;
-  cp.k1 = static_cast<const char*>(A.k_pool) + (int64_t(pb) * hkv + kvh) * blk;
-  cp.v0 = static_cast<const char*>(A.v_pool) + (int64_t(pa) * hkv + kvh) * blk;
-  cp.v1 = static_cast<const char*>(A.v_pool) + (int64_t(pb) * hkv + kvh) * blk;
+  cp.k0 = static_cast<const char*>(A.k_pool) + (int64_t(p.a) * hkv + kvh) * blk;
+  cp.k1 = static_cast<const char*>(A.k_pool) + (int64_t(p.b) * hkv + kvh) * blk;
+  cp.v0 = static_cast<const char*>(A.v_pool) + (int64_t(p.a) * hkv + kvh) * blk;
+  cp.v1 = static_cast<const char*>(A.v_pool) + (int64_t(p.b) * hkv + kvh) * blk;
   return cp;
+}
+
+template <class TR>
+__device__ __forceinline__ ChunkPages chunk_pages(const AttnArgs& A, cptr<int32_t> bt_row, int kvh, int c,
+                                                  int n_seq) {
+  return pages_of<TR>(A, kvh, page_ids(bt_row, c, n_seq));
 }
 
 template <class TR>
@@ -485,6 +502,26 @@ __device__ __forceinline__ u32x4_t load_q_frag(const AttnArgs& A, const RowInfo&
 
 // Final (normalised) output of one row tile's 4 d values at tile t (part < 0), or
 // the same values as partial row r of partial position `part` (slot * 2 + 0/1).
+// Partial results travel between workgroups of one launch that may sit on different XCDs (each
+// with its own L2).  They are written and read with agent-coherent (sc1) buffer accesses, so no
+// L2-wide write-back or invalidate is needed to hand them over.
+constexpr int kCoherent = 16;  // cache-policy bits: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t flat_rsrc(const float* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ void store_coherent(const float* base, uint32_t off, f32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), flat_rsrc(base), off, 0, kCoherent);
+}
+__device__ __forceinline__ void store_coherent(const float* base, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), flat_rsrc(base), off, 0, kCoherent);
+}
+__device__ __forceinline__ f32x4_t load_coherent4(const float* base, uint32_t off) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(flat_rsrc(base), off, 0, kCoherent));
+}
+__device__ __forceinline__ float load_coherent(const float* base, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(flat_rsrc(base), off, 0, kCoherent));
+}
+
 template <class TR>
 __device__ __forceinline__ void emit(const AttnArgs& A, const RowInfo& ri, int r, int part, int t, int quad,
                                      f32x4_t o, float lse_nat, bool write_lse) {
@@ -495,9 +532,9 @@ __device__ __forceinline__ void emit(const AttnArgs& A, const RowInfo& ri, int r
     TR::store_out(dst, o);
     if (write_lse) A.lse[int64_t(ri.tok) * A.num_q_heads + ri.head] = lse_nat;
   } else {
-    const int64_t prow = int64_t(part) * kPartRows + r;
-    *reinterpret_cast<f32x4_t*>(A.part_o + prow * TR::D + d) = o;
-    if (write_lse) A.part_lse[prow] = lse_nat;
+    const uint32_t prow = uint32_t(part) * kPartRows + r;
+    store_coherent(A.part_o, (prow * TR::D + d) * 4, o);
+    if (write_lse) store_coherent(A.part_lse, prow * 4, lse_nat);
   }
 }
 
@@ -547,18 +584,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, ch
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, off, 0, 0, 0);
 }
 
-__device__ __forceinline__ void wait_vmcnt_lgkm0(int n) {
-  // s_waitcnt vmcnt(n) lgkmcnt(0); expcnt left at its maximum
-  switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0070); break;
-    case 2: __builtin_amdgcn_s_waitcnt(0x0072); break;
-    case 4: __builtin_amdgcn_s_waitcnt(0x0074); break;
-    case 6: __builtin_amdgcn_s_waitcnt(0x0076); break;
-    case 8: __builtin_amdgcn_s_waitcnt(0x0078); break;
-    case 12: __builtin_amdgcn_s_waitcnt(0x007C); break;
-    case 16: __builtin_amdgcn_s_waitcnt(0x4070); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0070); break;  // any other count: wait for everything
-  }
+// s_waitcnt vmcnt(0) lgkmcnt(0): every load of this wave has landed.
+__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x0070); }
+
+// s_waitcnt vmcnt(N), leaving LDS / scalar loads (lgkmcnt) and expcnt unwaited.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 // Workgroup barrier that orders LDS accesses for the compiler without waiting on global memory.
@@ -651,14 +684,17 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
   // The loop body has a single path.  A step past the wave's last chunk is a dummy: all its keys
   // are masked and its V is zeroed, so it adds nothing.
   const int mine = i1 > c ? (i1 - c + kWaves - 1) / kWaves : 0;  // chunks of this wave
+  // Page ids are loaded one iteration before their DMA is issued, after the iteration's last LDS
+  // read (those reads wait for every LDS and scalar load in flight).
+  PageIds nx = page_ids(bt_row, min(c + kWaves, i1 - 1), n_seq);
   for (int j = 0; j < mine; ++j) {
     const int cc = c + j * kWaves;
     const int key0 = cc * kChunkKeys;
     const int cn = cc + kWaves;
-    if (cn < i1) cp = chunk_pages<TR>(A, bt_row, U.kv_head, cn, n_seq);
+    if (cn < i1) cp = pages_of<TR>(A, U.kv_head, nx);
     typename TR::PFrag pf[RT];
     if constexpr (kKviaLds) {
-      wait_vmcnt_lgkm0(TR::kVLoads);  // the K DMA of this chunk has landed (only V was issued after it)
+      wait_vmcnt<TR::kVLoads>();  // the K DMA of this chunk has landed (only V was issued after it)
       asm volatile("" ::: "memory");
       TR::template lds_read_k<RG>(kslot, lane, kf);  // completes before the slot is refilled
       asm volatile("" ::: "memory");
@@ -671,16 +707,18 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
       };
       softmax_chunk<TR, RT>(st, getq_asm, kf, key0, p_row, key0 + kChunkKeys - 1 > min_p, A.scale_log2, lane,
                             pf);
+      asm volatile("" ::: "memory");
     } else {
       asm volatile("" ::: "memory");  // keep the Q reads inside the loop
       softmax_chunk<TR, RT>(st, getq, kf, key0, p_row, key0 + kChunkKeys - 1 > min_p, A.scale_log2, lane, pf);
       load_k<TR>(cp, kl, vl, kf);
     }
+    nx = page_ids(bt_row, min(cn + kWaves, i1 - 1), n_seq);
     TR::sanitize_v(vf, quad, n_seq - key0);
     pv_chunk<TR, RT>(st, vf, pf);
     load_v<TR>(cp, kl, vl, vf);
   }
-  if constexpr (kKviaLds) wait_vmcnt_lgkm0(0);  // the last (unused) K DMA has landed before LDS is reused
+  if constexpr (kKviaLds) wait_all_loads();  // the last (unused) K DMA has landed before LDS is reused
   __syncthreads();  // every wave is done with its Q slice before the merge buffer overwrites it
 
   // merge the 4 waves' states through LDS
@@ -725,12 +763,13 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
 
 // One chunk of a row-split unit: start the DMA of chunk `next` (if >= 0) into slot `fill`, then
 // compute on the chunk held in slot `cur` (a different slot, landed before the last barrier).
-template <class TR, int RT, class Issue, class GetQ>
-__device__ __forceinline__ void ring_step(char* fill, const char* cur, Issue issue, int next,
+// `after_reads` runs once this chunk's LDS reads are done (it starts the next page-id loads).
+template <class TR, int RT, class Issue, class After, class GetQ>
+__device__ __forceinline__ void ring_step(char* fill, const char* cur, Issue issue, bool do_issue, After after_reads,
                                           bool active, State<TR, RT>& st, GetQ getq, int key0,
                                           const int (&p_row)[RT], int min_p, int n_seq, float sl2, int lane) {
   using RG = Ring<TR>;
-  if (next >= 0) issue(next, fill);
+  if (do_issue) issue(fill);
   if (active) {
     const int quad = lane >> 4;
     u32x4_t kf[TR::kKF];
@@ -739,8 +778,12 @@ __device__ __forceinline__ void ring_step(char* fill, const char* cur, Issue iss
     softmax_chunk<TR, RT>(st, getq, kf, key0, p_row, key0 + kChunkKeys - 1 > min_p, sl2, lane, pf);
     u32x4_t vf[TR::kVF];
     TR::template lds_read_v<RG>(cur, lane, vf);
+    asm volatile("" ::: "memory");
+    after_reads();
     if (key0 + kChunkKeys > n_seq) TR::sanitize_v(vf, quad, n_seq - key0);
     pv_chunk<TR, RT>(st, vf, pf);
+  } else {
+    after_reads();
   }
 }
 
@@ -788,8 +831,8 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
   // Wave w copies block w of each chunk; lane `lane` of DMA instruction i fills LDS bytes
   // [i*1024 + 16*lane, +16) of the block image, i.e. row r, swizzled column cc.
   char* ring = reinterpret_cast<char*>(sm.buf);
-  auto issue = [&](int c, char* slot) {
-    const ChunkPages cp = chunk_pages<TR>(A, bt_row, U.kv_head, c, n_seq);
+  auto issue = [&](PageIds ids, char* slot) {
+    const ChunkPages cp = pages_of<TR>(A, U.kv_head, ids);
     const __amdgpu_buffer_rsrc_t rs = block_rsrc(w == 0 ? cp.k0 : w == 1 ? cp.k1 : w == 2 ? cp.v0 : cp.v1, RG::kBlk);
     char* dst = slot + w * RG::kBlk;
 #pragma unroll
@@ -809,17 +852,25 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
 
 #pragma unroll
   for (int j = 0; j < RG::kNB - 1; ++j)
-    if (i0 + j < i1) issue(i0 + j, ring + j * RG::kChunk);
+    if (i0 + j < i1) issue(page_ids(bt_row, i0 + j, n_seq), ring + j * RG::kChunk);
+  // page ids of the chunk issued in the next iteration, loaded one iteration ahead
+  PageIds nx = page_ids(bt_row, min(i0 + RG::kNB - 1, i1 - 1), n_seq);
   for (int c = i0; c < i1; ++c) {
     const int j = c - i0;
     const int ahead = min(RG::kNB - 2, i1 - 1 - c);  // chunks this wave issued after chunk c
-    wait_vmcnt_lgkm0(ahead * RG::kInstr);
+    static_assert(RG::kNB <= 4, "waits below cover up to 2 chunks ahead");
+    if (ahead >= 2) wait_vmcnt<2 * RG::kInstr>();
+    else if (ahead == 1) wait_vmcnt<RG::kInstr>();
+    else wait_vmcnt<0>();
     lds_barrier();  // chunk c is in LDS for every wave; chunk c-1's slot is free
-    ring_step<TR, RT>(ring + ((j + RG::kNB - 1) % RG::kNB) * RG::kChunk, ring + (j % RG::kNB) * RG::kChunk,
-                      issue, c + RG::kNB - 1 < i1 ? c + RG::kNB - 1 : -1, active, st, getq, c * kChunkKeys, p_row,
-                      min_p, n_seq, A.scale_log2, lane);
+    const int next = c + RG::kNB - 1;
+    ring_step<TR, RT>(
+        ring + ((j + RG::kNB - 1) % RG::kNB) * RG::kChunk, ring + (j % RG::kNB) * RG::kChunk,
+        [&](char* slot) { issue(nx, slot); }, next < i1,
+        [&] { nx = page_ids(bt_row, min(next + 1, i1 - 1), n_seq); }, active, st, getq, c * kChunkKeys, p_row,
+        min_p, n_seq, A.scale_log2, lane);
   }
-  __builtin_amdgcn_s_waitcnt(0x0070);  // nothing of this unit left in flight
+  wait_all_loads();  // nothing of this unit left in flight
   lds_barrier();                        // every wave is done with the ring before it is reused
 
   if (active) {
@@ -920,17 +971,12 @@ __device__ void cursor_load_seq(UnitCursor& cu, const PlanView& v, P seq_lens, P
   cu.q = seq_units(seq_lens[cu.s], qsl[cu.s + 1] - qsl[cu.s], v.group);
 }
 
-// Position the cursor on the unit whose cost range holds c (0 <= c < total).
-template <class P, class Q>
-__device__ void cursor_find(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl, Q seq_cost, int64_t c) {
-  int lo = 0, hi = v.num_seqs - 1;  // last s with seq_cost[s] <= c
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (seq_cost[mid] <= c) lo = mid; else hi = mid - 1;
-  }
-  cu.s = lo;
-  cu.seq_base = seq_cost[lo];
-  cursor_load_seq(cu, v, seq_lens, qsl);
+// Position the cursor on the unit of sequence s (n keys, qn queries, starting at cost seq_base)
+// whose cost range holds c.
+__device__ void cursor_place(UnitCursor& cu, const PlanView& v, int s, int64_t seq_base, int n, int qn, int64_t c) {
+  cu.s = s;
+  cu.seq_base = seq_base;
+  cu.q = seq_units(n, qn, v.group);
   const int64_t off = c - cu.seq_base;
   cu.g = int(off / cu.q.per_head);
   int64_t acc = cu.seq_base + int64_t(cu.g) * cu.q.per_head;
@@ -944,6 +990,32 @@ __device__ void cursor_find(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl
     }
   }
   cu.U = make_unit(cu.s, cu.q, v.group, cu.g, cu.rb, acc);
+}
+
+// Position the cursor on the unit whose cost range holds c (0 <= c < total).
+template <class P, class Q>
+__device__ void cursor_find(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl, Q seq_cost, int64_t c) {
+  int lo = 0, hi = v.num_seqs - 1;  // last s with seq_cost[s] <= c
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (seq_cost[mid] <= c) lo = mid; else hi = mid - 1;
+  }
+  cursor_place(cu, v, lo, seq_cost[lo], seq_lens[lo], qsl[lo + 1] - qsl[lo], c);
+}
+
+__device__ __forceinline__ SlotStart slot_from_cursor(const UnitCursor& cu, int64_t c0, int64_t c1) {
+  SlotStart r;
+  r.c0 = c0;
+  r.c1 = c1;
+  r.seq_base = cu.seq_base;
+  r.unit_cost0 = cu.U.cost0;
+  r.s = cu.s;
+  r.g = cu.g;
+  r.rb = cu.rb;
+  r.n = cu.q.n;
+  r.qn = cu.q.qn;
+  r.pad[0] = r.pad[1] = r.pad[2] = 0;
+  return r;
 }
 
 // Position the cursor as the planner recorded for one slot.
@@ -989,11 +1061,109 @@ __device__ bool cursor_next(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl
   return true;
 }
 
-// One grain: the chunks whose start cost lies in [c0, c1), unit by unit.
+// Log-sum-exp merge of the n_pieces partial results of a split unit (piece j sits in grain
+// first + j: position 1 -- the grain's last unit -- for j = 0, position 0 after) into out / lse.
+// All kThreads threads of the workgroup take part.  A thread takes kInFlight of its rows at a time
+// and loads kPieces pieces of them together before folding them in, in piece order.
+template <class TR, int kInFlight, int kPieces>
+__device__ void merge_unit(const float* part_o, const float* part_lse, void* out, float* lse, cptr<int32_t> qsl,
+                           int num_q_heads, int group, const pa_plan_unit& U, int64_t first, int n_pieces) {
+  constexpr int kLanesPerRow = TR::D / 4;
+  constexpr int kRowsPerPass = kThreads / kLanesPerRow;
+  const int q0 = qsl[U.seq];
+  const int d4 = threadIdx.x % kLanesPerRow;
+  for (int r0 = threadIdx.x / kLanesPerRow; r0 < U.n_rows; r0 += kInFlight * kRowsPerPass) {
+    float M[kInFlight], L[kInFlight];
+    f32x4_t O[kInFlight];
+#pragma unroll
+    for (int i = 0; i < kInFlight; ++i) {
+      M[i] = -INFINITY;
+      L[i] = 0.f;
+      O[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int j0 = 0; j0 < n_pieces; j0 += kPieces) {
+      float lj[kPieces][kInFlight];
+      f32x4_t oj[kPieces][kInFlight];
+#pragma unroll
+      for (int p = 0; p < kPieces; ++p) {
+        const int j = j0 + p;
+        const uint32_t pbase = uint32_t((2 * (first + j) + (j == 0 ? 1 : 0)) * kPartRows);
+#pragma unroll
+        for (int i = 0; i < kInFlight; ++i) {
+          const int r = r0 + i * kRowsPerPass;
+          lj[p][i] = -INFINITY;
+          if (j < n_pieces && r < U.n_rows) {
+            lj[p][i] = load_coherent(part_lse, (pbase + r) * 4);
+            oj[p][i] = load_coherent4(part_o, ((pbase + r) * TR::D + 4 * d4) * 4);
+          }
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < kPieces; ++p)
+#pragma unroll
+        for (int i = 0; i < kInFlight; ++i) {
+          if (lj[p][i] != -INFINITY) {  // a piece that saw no key of this row adds nothing
+            const float m_new = fmaxf(M[i], lj[p][i]);
+            const float a_old = fast_exp2((M[i] - m_new) * kLog2e);
+            const float a_new = fast_exp2((lj[p][i] - m_new) * kLog2e);
+            L[i] = L[i] * a_old + a_new;
+            O[i] = O[i] * a_old + oj[p][i] * a_new;
+            M[i] = m_new;
+          }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kInFlight; ++i) {
+      const int r = r0 + i * kRowsPerPass;
+      if (r >= U.n_rows) continue;
+      const int rr = U.row0 + r;
+      const int tk = rr / group;
+      const int head = U.kv_head * group + (rr - tk * group);
+      const int64_t orow = int64_t(q0 + tk) * num_q_heads + head;
+      TR::store_out(static_cast<char*>(out) + (orow * TR::D + 4 * d4) * TR::kEb, O[i] * (1.f / L[i]));
+      if (d4 == 0) lse[orow] = M[i] + fast_log2(L[i]) * kLn2;
+    }
+  }
+}
+
+// Grains holding the first and the last chunk of a unit.
+__device__ __forceinline__ int64_t first_grain(const pa_plan_unit& U, int64_t S, int64_t C) {
+  return slot_of(chunk_start(U, 0), S, C);
+}
+__device__ __forceinline__ int64_t last_grain(const pa_plan_unit& U, int64_t S, int64_t C) {
+  return slot_of(chunk_start(U, U.n_chunks - 1), S, C);
+}
+
+// Single launch: after writing its piece of a split unit, the workgroup counts itself in; the
+// one that completes the count merges every piece and re-zeroes the counter for the next call.
+// The pieces are agent-coherent stores that have completed (vmcnt(0)) before the count, and the
+// merging workgroup reads them with agent-coherent loads issued after it saw the count.
 template <class TR>
-__device__ void run_grain(const AttnArgs& A, int grain, Smem<TR>& sm) {
+__device__ void arrive_and_merge(const AttnArgs& A, const pa_plan_unit& U, int64_t S, int64_t C, int* flag) {
+  const int64_t first = first_grain(U, S, C);
+  const int n_pieces = int(last_grain(U, S, C) - first + 1);
+  wait_all_loads();  // this wave's partial stores are done
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int done = __hip_atomic_fetch_add(A.arrive + first, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = done == n_pieces - 1;
+  }
+  __syncthreads();
+  const bool last = *flag;
+  __syncthreads();  // flag read by every thread before it is reused
+  if (!last) return;
+  merge_unit<TR, 4, 4>(A.part_o, A.part_lse, A.out, A.lse, ro(A.plan.qsl), A.num_q_heads, A.plan.group, U, first,
+                    n_pieces);
+  if (threadIdx.x == 0) __hip_atomic_store(A.arrive + first, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One grain: the chunks whose start cost lies in [st.c0, st.c1), unit by unit.  kFused: the
+// single-launch kernel (S grains over total cost C; split units are merged here), else the staged
+// kernel (split units are left as partial results for the merge kernel).
+template <class TR, bool kFused>
+__device__ void run_grain(const AttnArgs& A, int grain, const SlotStart& st, int64_t S, int64_t C, Smem<TR>& sm,
+                          int* flag) {
   const PlanView& v = A.plan;
-  const SlotStart st = load_slot(ro(v.slots) + grain);
   const int64_t c0 = st.c0, c1 = st.c1;
   if (c0 >= c1) return;
   const cptr<int32_t> seq_lens = ro(v.seq_lens);
@@ -1018,28 +1188,140 @@ __device__ void run_grain(const AttnArgs& A, int grain, Smem<TR>& sm) {
       } else {
         run_rowsplit<TR>(A, U, i0, i1, part, sm);
       }
+      if constexpr (kFused) {
+        if (part >= 0) arrive_and_merge<TR>(A, U, S, C, flag);
+      }
     }
   } while (cursor_next(cu, v, seq_lens, qsl));
 }
 
-// Persistent launch: workgroup b runs grain b, then takes grains grid, grid+1, ... from the
-// counter until none is left; the grab for its next grain is issued when a grain starts.
+// Staged path: workgroup b runs grain b, b + grid, ... of the plan in the workspace.
 template <class TR>
 __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs A) {
   __shared__ Smem<TR> sm;
-  __shared__ int next_grain;
-  const int n_grains = ro(A.plan.hdr)->n_slots;
-  int g = blockIdx.x;
-  while (g < n_grains) {
-    int ahead = 0;
-    if (threadIdx.x == 0)
-      ahead = int(gridDim.x) + __hip_atomic_fetch_add(A.grab, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    run_grain<TR>(A, g, sm);
-    __syncthreads();
-    if (threadIdx.x == 0) next_grain = ahead;
-    __syncthreads();
-    g = next_grain;
+  const int64_t S = ro(A.plan.hdr)->n_slots;
+  for (int64_t g = blockIdx.x; g < S; g += gridDim.x)
+    run_grain<TR, false>(A, int(g), load_slot(ro(A.plan.slots) + g), 0, 0, sm, nullptr);
+}
+
+// Sums and scans of one int64 per thread over the kThreads threads of a workgroup.
+__device__ int64_t wg_sum(int64_t x, int64_t* red) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  if (lane == 0) red[wid] = x;
+  __syncthreads();
+  int64_t t = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) t += red[i];
+  __syncthreads();
+  return t;
+}
+__device__ int64_t wg_exclusive_scan(int64_t x, int64_t* red, int64_t* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int64_t incl = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
   }
+  if (lane == 63) red[wid] = incl;
+  __syncthreads();
+  int64_t before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    if (i < wid) before += red[i];
+    all += red[i];
+  }
+  __syncthreads();
+  *total = all;
+  return incl - x + before;
+}
+
+// Sequences per thread in one pass of the in-kernel planner.
+constexpr int kPreSeqs = 4;
+
+struct PreLds {
+  int64_t red[kWaves];
+  SlotStart st;
+  int flag;
+};
+
+// Cost of the kPreSeqs sequences of this thread in the block of kThreads * kPreSeqs at `base`
+// (c), and the part of their sum that is row-split work (returned).
+__device__ __forceinline__ int64_t block_seq_costs(const PlanView& v, cptr<int32_t> sl, cptr<int32_t> qsl, int base,
+                                                   int64_t (&c)[kPreSeqs], int (&n)[kPreSeqs], int (&qn)[kPreSeqs]) {
+  int64_t row = 0;
+#pragma unroll
+  for (int e = 0; e < kPreSeqs; ++e) {
+    const int s = base + threadIdx.x * kPreSeqs + e;
+    n[e] = qn[e] = 0;
+    c[e] = 0;
+    if (s < v.num_seqs) {
+      n[e] = sl[s];
+      qn[e] = qsl[s + 1] - qsl[s];
+      const SeqUnits q = seq_units(n[e], qn[e], v.group);
+      c[e] = int64_t(v.num_kv_heads) * q.per_head;
+      if (!q.split) row += c[e];
+    }
+  }
+  return row;
+}
+
+// Single launch.  Every workgroup derives the plan's total cost C and grain count S from
+// seq_lens and query_start_loc (the same numbers the staged planner writes), finds where its grain
+// starts with a workgroup-wide scan of the per-sequence costs, then runs the grain and merges the
+// split units it completes.
+template <class TR>
+__global__ __launch_bounds__(kThreads, 2) void attention_fused_kernel(AttnArgs A) {
+  __shared__ Smem<TR> sm;
+  __shared__ PreLds pl;
+  const PlanView& v = A.plan;
+  const cptr<int32_t> sl = ro(v.seq_lens), qsl = ro(v.qsl);
+  constexpr int kBlock = kThreads * kPreSeqs;
+  int64_t c[kPreSeqs];
+  int n[kPreSeqs], qn[kPreSeqs];
+  const int64_t row0 = block_seq_costs(v, sl, qsl, 0, c, n, qn);  // kept for the search when B <= kBlock
+  int64_t C = 0, Cr = 0;
+  for (int base = 0; base < v.num_seqs; base += kBlock) {
+    int64_t c2[kPreSeqs];
+    int n2[kPreSeqs], qn2[kPreSeqs];
+    const int64_t row = base > 0 ? block_seq_costs(v, sl, qsl, base, c2, n2, qn2) : row0;
+    int64_t x = 0;
+#pragma unroll
+    for (int e = 0; e < kPreSeqs; ++e) x += base > 0 ? c2[e] : c[e];
+    C += wg_sum(x, pl.red);
+    Cr += wg_sum(row, pl.red);
+  }
+  const int64_t S = grain_count(C - Cr, Cr, int(gridDim.x));
+  const int64_t k = blockIdx.x;
+  if (k >= S) return;
+  const int64_t c0 = slice_begin(k, S, C), c1 = slice_begin(k + 1, S, C);
+  int64_t carry = 0;
+  for (int base = 0; base < v.num_seqs; base += kBlock) {
+    if (base > 0) block_seq_costs(v, sl, qsl, base, c, n, qn);
+    int64_t x = 0;
+#pragma unroll
+    for (int e = 0; e < kPreSeqs; ++e) x += c[e];
+    int64_t tot;
+    int64_t pre = carry + wg_exclusive_scan(x, pl.red, &tot);
+    if (c0 >= pre && c0 < pre + x) {  // exactly one thread holds the sequence of cost c0
+#pragma unroll
+      for (int e = 0; e < kPreSeqs; ++e) {
+        if (c0 >= pre && c0 < pre + c[e]) {
+          UnitCursor cu;
+          cursor_place(cu, v, base + int(threadIdx.x) * kPreSeqs + e, pre, n[e], qn[e], c0);
+          pl.st = slot_from_cursor(cu, c0, c1);
+        }
+        pre += c[e];
+      }
+    }
+    carry += tot;
+    if (c0 < carry) break;  // uniform: every thread holds the same carry
+  }
+  __syncthreads();
+  const SlotStart st = pl.st;
+  run_grain<TR, true>(A, int(k), st, S, C, sm, &pl.flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -1080,18 +1362,22 @@ constexpr int kPlanLdsSeqs = 4096;  // sequences whose cost prefix the planner k
 __global__ __launch_bounds__(kScanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int64_t wave_tot[kScanThreads / 64];
   __shared__ int64_t lds_cost[kPlanLdsSeqs + 1];
-  int64_t carry = 0, units = 0;
+  int64_t carry = 0, units = 0, row_cost = 0;
   for (int base = 0; base < a.num_seqs; base += kScanThreads) {
     const int s = base + threadIdx.x;
     int64_t cost = 0, nu = 0;
+    bool split = true;
     if (s < a.num_seqs) {
       const SeqUnits q = seq_units(a.seq_lens[s], a.qsl[s + 1] - a.qsl[s], a.group);
       cost = int64_t(a.num_kv_heads) * q.per_head;
       nu = int64_t(a.num_kv_heads) * q.nb;
+      split = q.split;
     }
-    int64_t tot, tot_u;
+    int64_t tot, tot_u, tot_r;
     const int64_t ex = block_exclusive_scan(cost, wave_tot, &tot);
     block_exclusive_scan(nu, wave_tot, &tot_u);
+    block_exclusive_scan(split ? 0 : cost, wave_tot, &tot_r);
+    row_cost += tot_r;
     if (s < a.num_seqs) {
       a.seq_cost[s] = carry + ex;
       if (s < kPlanLdsSeqs) lds_cost[s] = carry + ex;
@@ -1100,20 +1386,17 @@ __global__ __launch_bounds__(kScanThreads) void plan_kernel(PlanArgs a) {
     units += tot_u;
   }
   const int64_t C = carry;
-  int64_t S = C / kCostMax;  // every grain at least one chunk of the heaviest kind wide
-  if (S > int64_t(a.grid) * kGrainsPerWorkgroup) S = int64_t(a.grid) * kGrainsPerWorkgroup;
-  if (S < 1 && C > 0) S = 1;
+  const int64_t S = grain_count(C - row_cost, row_cost, a.grid);
   if (threadIdx.x == 0) {
-    *a.grab = 0;
     a.seq_cost[a.num_seqs] = C;
     a.hdr->n_units = int32_t(units);
     a.hdr->n_slots = int32_t(S);
     a.hdr->grid = a.grid;
     a.hdr->num_seqs = a.num_seqs;
     a.hdr->total_cost = C;
-    a.hdr->grains_per_workgroup = kGrainsPerWorkgroup;
     a.hdr->reserved = 0;
   }
+  for (int k = threadIdx.x; k < a.grid; k += kScanThreads) a.arrive[k] = 0;  // for a single launch
   __syncthreads();  // seq_cost (global and LDS) complete
   // where every slot starts: one binary search per slot
   PlanView v;
@@ -1132,15 +1415,7 @@ __global__ __launch_bounds__(kScanThreads) void plan_kernel(PlanArgs a) {
     UnitCursor cu;
     if (a.num_seqs <= kPlanLdsSeqs) cursor_find(cu, v, a.seq_lens, a.qsl, lds_cost, r.c0);
     else cursor_find(cu, v, a.seq_lens, a.qsl, a.seq_cost, r.c0);
-    r.seq_base = cu.seq_base;
-    r.unit_cost0 = cu.U.cost0;
-    r.s = cu.s;
-    r.g = cu.g;
-    r.rb = cu.rb;
-    r.n = cu.q.n;
-    r.qn = cu.q.qn;
-    r.pad[0] = r.pad[1] = r.pad[2] = 0;
-    a.slots[k] = r;
+    a.slots[k] = slot_from_cursor(cu, r.c0, r.c1);
   }
 }
 
@@ -1189,71 +1464,18 @@ __device__ __forceinline__ void merge_row(const float* o_parts, const float* lse
 
 template <class TR>
 __global__ __launch_bounds__(kThreads) void merge_planned_kernel(MergeArgs a) {
-  constexpr int kLanesPerRow = TR::D / 4;
-  constexpr int kRowsPerPass = kThreads / kLanesPerRow;
-  constexpr int kMaxPass = kPartRows / kRowsPerPass;
   const PlanView& v = a.plan;
-  const pa_plan_header* hdr = v.hdr;
-  const int64_t S = hdr->n_slots, C = hdr->total_cost;
+  const int64_t S = ro(v.hdr)->n_slots, C = ro(v.hdr)->total_cost;
   const int k = blockIdx.x;
-  if (k == 0 && threadIdx.x == 0) *a.grab = 0;  // the attention launch has finished: ready for the next one
   if (k == 0 || k >= S) return;
   UnitCursor cu;
   cursor_from_slot(cu, v, load_slot(ro(v.slots) + k));  // the unit holding the first cost of grain k
   const pa_plan_unit& U = cu.U;
-  const int64_t first = slot_of(chunk_start(U, 0), S, C);
-  const int64_t last = slot_of(chunk_start(U, U.n_chunks - 1), S, C);
+  const int64_t first = first_grain(U, S, C);
+  const int64_t last = last_grain(U, S, C);
   if (first != k - 1 || last < k) return;  // boundary k does not open this unit's split
-  const int n_pieces = int(last - first + 1);
-  // piece j sits in slot first + j: position 1 (the slot's last unit) for j = 0, position 0 after
-  const int q0 = ro(v.qsl)[U.seq];
-  const int d4 = threadIdx.x % kLanesPerRow;
-  const int r0 = threadIdx.x / kLanesPerRow;
-  // online merge over the pieces, all rows of this thread in flight together
-  float M[kMaxPass], L[kMaxPass];
-  f32x4_t O[kMaxPass];
-#pragma unroll
-  for (int i = 0; i < kMaxPass; ++i) {
-    M[i] = -INFINITY;
-    L[i] = 0.f;
-    O[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-  for (int j = 0; j < n_pieces; ++j) {
-    const int64_t pbase = (2 * (first + j) + (j == 0 ? 1 : 0)) * int64_t(kPartRows);
-    float lj[kMaxPass];
-    f32x4_t oj[kMaxPass];
-#pragma unroll
-    for (int i = 0; i < kMaxPass; ++i) {
-      const int r = r0 + i * kRowsPerPass;
-      if (r < U.n_rows) {
-        lj[i] = a.part_lse[pbase + r];
-        oj[i] = *reinterpret_cast<const f32x4_t*>(a.part_o + (pbase + r) * TR::D + 4 * d4);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kMaxPass; ++i) {
-      const int r = r0 + i * kRowsPerPass;
-      if (r < U.n_rows && lj[i] != -INFINITY) {  // a piece that saw no key of this row adds nothing
-        const float m_new = fmaxf(M[i], lj[i]);
-        const float a_old = fast_exp2((M[i] - m_new) * kLog2e);
-        const float a_new = fast_exp2((lj[i] - m_new) * kLog2e);
-        L[i] = L[i] * a_old + a_new;
-        O[i] = O[i] * a_old + oj[i] * a_new;
-        M[i] = m_new;
-      }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kMaxPass; ++i) {
-    const int r = r0 + i * kRowsPerPass;
-    if (r >= U.n_rows) continue;
-    const int rr = U.row0 + r;
-    const int tk = rr / v.group;
-    const int head = U.kv_head * v.group + (rr - tk * v.group);
-    const int64_t orow = int64_t(q0 + tk) * a.num_q_heads + head;
-    TR::store_out(static_cast<char*>(a.out) + (orow * TR::D + 4 * d4) * TR::kEb, O[i] * (1.f / L[i]));
-    if (d4 == 0) a.lse[orow] = M[i] + fast_log2(L[i]) * kLn2;
-  }
+  merge_unit<TR, 4, 4>(a.part_o, a.part_lse, a.out, a.lse, ro(v.qsl), a.num_q_heads, v.group, U, first,
+                    int(last - first + 1));
 }
 
 // Stand-alone merge: rows of n_parts partial results (o_parts [P][rows][D], lse_parts [P][rows]).
@@ -1351,12 +1573,44 @@ int launch_attention(const AttnArgs& a, int dtype, int D, int grid, void* stream
 }
 
 template <class TR>
+static int launch_fused_t(const AttnArgs& a, int grid, void* stream) {
+  hipLaunchKernelGGL(attention_fused_kernel<TR>, dim3(grid), dim3(kThreads), 0, as_stream(stream), a);
+  return int(hipGetLastError());
+}
+
+int launch_attention_fused(const AttnArgs& a, int dtype, int D, int grid, void* stream) {
+  if (dtype == PA_BF16) return D == 128 ? launch_fused_t<Bf16<128>>(a, grid, stream) : launch_fused_t<Bf16<64>>(a, grid, stream);
+  return D == 128 ? launch_fused_t<F32<128>>(a, grid, stream) : launch_fused_t<F32<64>>(a, grid, stream);
+}
+
+// The staged and the single-launch kernel run on the same grid (the smaller occupancy of the
+// two), so both cut the batch into the same grains and give bitwise identical results.
+template <class TR>
 static int blocks_per_cu_t() {
-  int n = 0;
-  void (*fn)(AttnArgs) = attention_kernel<TR>;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(fn), kThreads, 0) != hipSuccess)
+  int n = 0, m = 0;
+  void (*staged)(AttnArgs) = attention_kernel<TR>;
+  void (*fused)(AttnArgs) = attention_fused_kernel<TR>;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(staged), kThreads, 0) !=
+          hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, reinterpret_cast<const void*>(fused), kThreads, 0) !=
+          hipSuccess)
     return -1;
-  return n;
+  return n < m ? n : m;
+}
+
+__global__ void fill_zero_kernel(uint32_t* p, int64_t words) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < words; i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = 0u;
+}
+
+int launch_fill_zero(void* p, size_t bytes, void* stream) {
+  const int64_t words = int64_t(bytes / 4);
+  if (words == 0) return 0;
+  int64_t grid = (words + 255) / 256;
+  if (grid > 1024) grid = 1024;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(unsigned(grid)), dim3(256), 0, as_stream(stream),
+                     static_cast<uint32_t*>(p), words);
+  return int(hipGetLastError());
 }
 
 int attention_blocks_per_cu(int dtype, int D) {
