@@ -52,6 +52,8 @@ def open_library(path: str):
     lib.oracle_gather.restype = ip
     lib.oracle_merge.argtypes = [ip, ctypes.c_int64, ip, vp, vp, vp, vp]
     lib.oracle_merge.restype = ip
+    lib.oracle_append.argtypes = [ip, ip, ip, ip, ip, ip, vp, vp, vp, vp, vp, vp, vp]
+    lib.oracle_append.restype = ip
     lib.oracle_max_threads.restype = ip
     return lib
 
@@ -151,3 +153,25 @@ def merge(o_parts, lse_parts, lib=None):
     lse = np.zeros(rows, dtype=np.float64)
     _check(lib.oracle_merge(P, rows, D, _ptr(o_parts), _ptr(lse_parts), _ptr(o), _ptr(lse)))
     return o, lse
+
+
+def append(k_new, v_new, k_pool, v_pool, block_table, seq_lens, query_start_loc, lib=None):
+    """Paged KV append: copies of k_pool / v_pool with the new tokens' rows written in.
+
+    k_new, v_new: [T_q][Hkv][D]; token i of sequence s goes to position seq_lens[s] - q_s + i."""
+    lib = _load(lib)
+    k_new = np.ascontiguousarray(k_new)
+    v_new = np.ascontiguousarray(v_new)
+    k_out = np.array(k_pool, copy=True, order="C")
+    v_out = np.array(v_pool, copy=True, order="C")
+    dt = _dtype_code(k_out)
+    assert _dtype_code(v_out) == dt and _dtype_code(k_new) == dt and _dtype_code(v_new) == dt
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    qsl = np.ascontiguousarray(query_start_loc, dtype=np.int32)
+    NP, Hkv, _, D = k_out.shape
+    B = sl.shape[0]
+    assert k_new.shape == (int(qsl[-1]), Hkv, D) and v_new.shape == k_new.shape
+    _check(lib.oracle_append(B, Hkv, D, dt, NP, bt.shape[1], _ptr(bt), _ptr(sl), _ptr(qsl), _ptr(k_new),
+                             _ptr(v_new), _ptr(k_out), _ptr(v_out)))
+    return k_out, v_out

@@ -199,6 +199,49 @@ int oracle_gather(int which, int dtype, int Hkv, int D, int num_pages, int max_p
 }
 
 /*
+ * Paged KV append: the K/V rows of a batch's new tokens go into their pages.
+ * New token i of sequence s (query token r = qsl[s] + i) sits at position
+ * p = n_s - q_s + i -- the same reading as the attention above, where seq_lens
+ * count the new tokens -- so, with pg = block_table[s][p / 16], t = p % 16:
+ *     k_pool[pg][g][t][d] = k_new[r][g][d],   v_pool[pg][g][d][t] = v_new[r][g][d]
+ * for every K/V head g and d (element bits copied).  k_new and v_new are
+ * [T_q][Hkv][D].  Nothing else in the pools changes.  (XY-Serve verdict page,
+ * "core_discovery": K/V live in a PagedAttention-style block cache that every
+ * step appends to.)
+ */
+int oracle_append(int B, int Hkv, int D, int dtype, int num_pages, int max_pages, const int32_t* block_table,
+                  const int32_t* seq_lens, const int32_t* qsl, const void* k_new, const void* v_new, void* k_pool,
+                  void* v_pool) {
+  if (B < 0 || Hkv <= 0 || D <= 0 || (dtype != ORACLE_F32 && dtype != ORACLE_BF16)) return ORACLE_BAD_ARG;
+  const size_t eb = dtype == ORACLE_BF16 ? 2 : 4;
+  if (B > 0 && qsl[0] != 0) return ORACLE_BAD_CONTENT;
+  for (int s = 0; s < B; ++s) {
+    const int n = seq_lens[s], q = qsl[s + 1] - qsl[s];
+    if (q < 0 || q > n || (n + ORACLE_PAGE - 1) / ORACLE_PAGE > max_pages) return ORACLE_BAD_CONTENT;
+    for (int p = n - q; p < n; ++p) {
+      const int64_t pg = block_table[(int64_t)s * max_pages + p / ORACLE_PAGE];
+      if (pg < 0 || pg >= num_pages) return ORACLE_BAD_CONTENT;
+    }
+  }
+  for (int s = 0; s < B; ++s) {
+    const int n = seq_lens[s], q = qsl[s + 1] - qsl[s];
+    for (int i = 0; i < q; ++i) {
+      const int64_t r = qsl[s] + i;
+      const int p = n - q + i;
+      const int64_t pg = block_table[(int64_t)s * max_pages + p / ORACLE_PAGE];
+      const int t = p % ORACLE_PAGE;
+      for (int g = 0; g < Hkv; ++g)
+        for (int d = 0; d < D; ++d) {
+          const int64_t src = (r * Hkv + g) * D + d;
+          memcpy((char*)k_pool + k_offset(pg, g, t, d, Hkv, D) * eb, (const char*)k_new + src * eb, eb);
+          memcpy((char*)v_pool + v_offset(pg, g, t, d, Hkv, D) * eb, (const char*)v_new + src * eb, eb);
+        }
+    }
+  }
+  return ORACLE_OK;
+}
+
+/*
  * Combine attention results computed over disjoint key sets.
  * o_parts: [P][rows][D], lse_parts: [P][rows]  ->  o: [rows][D], lse: [rows].
  * A part with lse = -inf (it saw no key) contributes nothing.

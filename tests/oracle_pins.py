@@ -359,5 +359,52 @@ def pin_gather(lib=None):
             assert gv.tobytes() == np.ascontiguousarray(ev).tobytes()
 
 
+def pin_append(lib=None):
+    """Paged KV append, pinned without its own formula: (1) the pinned page-walk gather of every
+    sequence returns its old context followed by exactly its new rows; (2) nothing else changes (the
+    new values lie in [1000, 1001), which no pool value does, and exactly T_q * Hkv * D elements of
+    each pool differ); (3) attention over the appended pools equals fp64 torch SDPA over the dense
+    concatenation of the old context and the new rows."""
+    import torch
+    for seed, (B, maxlen, Hq, Hkv, D, dt, maxq) in enumerate([
+            (4, 200, 8, 2, 64, "f32", 40), (5, 300, 4, 1, 128, "bf16", 70), (6, 60, 8, 8, 64, "bf16", 1)]):
+        w = W.make_random(300 + seed, B, maxlen, Hq, Hkv, D, dt, max_q=maxq)
+        T = w.num_q_tokens
+        rng = np.random.default_rng(400 + seed)
+        k_new = narrow(1000.0 + rng.random((T, Hkv, D)), dt)
+        v_new = narrow(1000.0 + rng.random((T, Hkv, D)), dt)
+        k2, v2 = oracle.append(k_new, v_new, w.k_pool, w.v_pool, w.block_table, w.seq_lens, w.query_start_loc,
+                               lib=lib)
+        for old, new in ((w.k_pool, k2), (w.v_pool, v2)):
+            changed = widen(old) != widen(new)
+            assert int(changed.sum()) == T * Hkv * D, (seed, int(changed.sum()))
+        q = torch.from_numpy(widen(w.q))
+        G = Hq // Hkv
+        after = _replace(w, k_pool=k2, v_pool=v2)
+        o, l = run(after, lib)
+        for s in range(w.num_seqs):
+            n = int(w.seq_lens[s])
+            q0, q1 = int(w.query_start_loc[s]), int(w.query_start_loc[s + 1])
+            win = q1 - q0
+            gk_old = oracle.gather(w.k_pool, w.block_table, w.seq_lens, s, "k", lib=lib)
+            gv_old = oracle.gather(w.v_pool, w.block_table, w.seq_lens, s, "v", lib=lib)
+            gk = oracle.gather(k2, w.block_table, w.seq_lens, s, "k", lib=lib)
+            gv = oracle.gather(v2, w.block_table, w.seq_lens, s, "v", lib=lib)
+            for g_old, g_new, rows in ((gk_old, gk, k_new), (gv_old, gv, v_new)):
+                assert g_new[:, :n - win].tobytes() == g_old[:, :n - win].tobytes(), seed
+                assert g_new[:, n - win:].tobytes() == np.ascontiguousarray(rows[q0:q1].transpose(1, 0, 2)).tobytes()
+            if win == 0:
+                continue
+            K = np.concatenate([widen(gk_old[:, :n - win]), widen(k_new[q0:q1]).transpose(1, 0, 2)], axis=1)
+            V = np.concatenate([widen(gv_old[:, :n - win]), widen(v_new[q0:q1]).transpose(1, 0, 2)], axis=1)
+            Kt = torch.from_numpy(K).repeat_interleave(G, dim=0)
+            Vt = torch.from_numpy(V).repeat_interleave(G, dim=0)
+            Q = q[q0:q1].transpose(0, 1).contiguous()
+            mask = torch.arange(n)[None, :] <= (n - win + torch.arange(win))[:, None]
+            ref = torch.nn.functional.scaled_dot_product_attention(Q[None], Kt[None], Vt[None],
+                                                                   attn_mask=mask[None, None], scale=w.scale)[0]
+            assert np.max(np.abs(o[q0:q1] - ref.transpose(0, 1).numpy())) <= 1e-9, (seed, s)
+
+
 ALL_PINS = [pin_brute_force, pin_golden, pin_closed_forms, pin_invariants, pin_merge_of_splits,
-            pin_sdpa, pin_gather]
+            pin_sdpa, pin_gather, pin_append]

@@ -37,6 +37,10 @@ def test_oracle_matches_torch_sdpa_fp64():
     P.pin_sdpa()
 
 
+def test_oracle_append():
+    P.pin_append()
+
+
 def test_oracle_gather_page_walk():
     P.pin_gather()
 
@@ -102,6 +106,11 @@ MUTATIONS = [
     ("softmax sign flipped", "const double w = exp(x[j] - m);", "const double w = exp(m - x[j]);"),
     ("query head taken as KV head", "widen(q, dtype, qoff + d)", "widen(q, dtype, (r * Hq + g) * (int64_t)D + d)"),
     ("merge weight w.r.t. the max", "v += exp(li - total) * o_parts", "v += exp(li - m) * o_parts"),
+    ("append one position late", "const int p = n - q + i;", "const int p = n - q + i + (i + 1 < q);"),
+    ("append V with K's layout", "memcpy((char*)v_pool + v_offset(pg, g, t, d, Hkv, D) * eb",
+     "memcpy((char*)v_pool + k_offset(pg, g, t, d, Hkv, D) * eb"),
+    ("append reads the wrong head", "const int64_t src = (r * Hkv + g) * D + d;",
+     "const int64_t src = (r * Hkv + (Hkv - 1 - g)) * D + d;"),
     ("page lookup off by one page", "const int64_t pg = bt[j / ORACLE_PAGE];\n        const int t = j % ORACLE_PAGE;\n        double",
      "const int64_t pg = bt[(j / ORACLE_PAGE + 1) % ((n + 15) / 16)];\n        const int t = j % ORACLE_PAGE;\n        double"),
 ]
