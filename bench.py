@@ -130,6 +130,70 @@ def cpu_baseline(w, alg_bytes: int, min_seconds: float = 10.0, min_runs: int = 3
                       f"({sum(times):.1f} s in all), median {t:.3f} s per batch; fp64 two-pass softmax"}
 
 
+def bench_append(args, w) -> int:
+    """Time pa_append_kv: the K/V rows of every new token of the batch written into their pages.
+    Algorithmic bytes: the new rows read and written once (K and V), plus one block-table entry
+    per touched page."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_gqa_amd as pa
+    from paged_kv_cache_gqa_amd import binding as B
+    import ctypes
+
+    t = pa.to_device(w)
+    T, Hkv, D = w.num_q_tokens, w.num_kv_heads, w.head_dim
+    g = torch.Generator(device="cuda").manual_seed(1000 + args.config)
+    dt = t["k_pool"].dtype
+    k_new = torch.randn((T, Hkv, D), generator=g, device="cuda").to(dt)
+    v_new = torch.randn((T, Hkv, D), generator=g, device="cuda").to(dt)
+    ql = w.q_lens()
+    first = (w.seq_lens - ql) // 16
+    last = (w.seq_lens - 1) // 16
+    pages = int(np.sum(np.where(ql > 0, last - first + 1, 0)))
+    alg_bytes = 2 * 2 * T * Hkv * D * k_new.element_size() + 4 * pages
+    stream = torch.cuda.current_stream()
+    desc = B.PaDesc(num_seqs=w.num_seqs, num_q_tokens=T, num_q_heads=Hkv, num_kv_heads=Hkv, head_dim=D,
+                    page_size=16, num_pages=w.num_pages, max_pages_per_seq=w.max_pages_per_seq,
+                    dtype=B._DTYPES[dt], scale=1.0)
+    vp = ctypes.c_void_p
+    cargs = (ctypes.byref(desc), vp(k_new.data_ptr()), vp(v_new.data_ptr()), vp(t["block_table"].data_ptr()),
+             vp(t["seq_lens"].data_ptr()), vp(t["query_start_loc"].data_ptr()), vp(t["k_pool"].data_ptr()),
+             vp(t["v_pool"].data_ptr()), vp(stream.cuda_stream))
+    L = B.lib()
+    for _ in range(args.warmup):
+        L.pa_append_kv(*cargs)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in events:
+        a.record(stream)
+        rc = L.pa_append_kv(*cargs)
+        b.record(stream)
+        if rc:
+            raise RuntimeError(f"launch failed: {B.status_string(rc)}")
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ks = [a.elapsed_time(b) for a, b in events]
+    kmean = statistics.fmean(ks)
+    name = w.name
+    line = {
+        "metric": "paged KV append GB/s (new K/V rows read + written, block-table entries), 1 MI355X",
+        "value": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded; shapes of the named configuration)",
+        "config": {"workload": f"{name} (configuration {args.config}) new tokens", "new_tokens": T, "kv_heads": Hkv,
+                   "head_dim": D, "pages_touched": pages, "algorithmic_bytes": alg_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(alg_bytes / (kmean * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(alg_bytes / (kmean * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
+                     "traffic": None, "kernel": "pa::append_kv_kernel", "kernel_ms_mean": round(kmean, 5),
+                     "kernel_ms_p10_p90": [round(float(np.percentile(ks, 10)), 5),
+                                           round(float(np.percentile(ks, 90)), 5)]},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +202,9 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--part", default="all", choices=["all", "prefill", "decode"],
                     help="configuration 3 only: time its prefill chunks or its decode rows alone")
+    ap.add_argument("--op", default="attention", choices=["attention", "append"],
+                    help="attention (default): the attention call; append: the paged KV append of the batch's new "
+                         "tokens (pa_append_kv)")
     ap.add_argument("--staged", action="store_true",
                     help="time pa_plan + pa_attention_planned + pa_merge_planned instead of the single launch")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
@@ -176,6 +243,8 @@ def main() -> int:
         keep = np.nonzero(ql > 1 if args.part == "prefill" else ql == 1)[0]
         w = W.subset(w, keep)
         w.name = f"{W.CONFIG_NAMES[args.config]}-{args.part}-part"
+    if args.op == "append":
+        return bench_append(args, w)
     alg_bytes = w.algorithmic_bytes()
     alg_flops = w.algorithmic_flops()
     t = pa.to_device(w)

@@ -218,6 +218,27 @@ pa_status pa_merge(int32_t n_parts, int64_t rows, int32_t head_dim, const float*
                    const float* lse_parts, int32_t out_dtype, void* out, float* lse, void* stream);
 
 /*
+ * Paged KV append -- the step before attention in a decode or chunked-prefill
+ * loop: write the K and V rows of the batch's new tokens into their pages.
+ * New token i of sequence s (row query_start_loc[s] + i of k_new / v_new)
+ * goes to position p = seq_lens[s] - q_s + i, i.e. page
+ * block_table[s][p / 16], slot p % 16 -- the positions pa_attention reads as
+ * the window's own keys (seq_lens count the new tokens).  Sources: XY-Serve
+ * verdict page, core_discovery (K/V kept in a PagedAttention-style block
+ * cache that each step extends).
+ *   k_new, v_new   [T_q][Hkv][D]  desc->dtype, device memory, read only
+ *   k_pool, v_pool as above; only the (page, head, slot) rows of new tokens
+ *                  are written, element bits copied unchanged
+ * desc->num_q_heads and desc->scale are not used.  Two new tokens that map
+ * to the same slot is undefined behaviour (sequences that share pages must
+ * not append into a shared page); pa_validate checks the block-table range.
+ * Enqueued on `stream`; no workspace.
+ */
+pa_status pa_append_kv(const pa_desc* desc, const void* k_new, const void* v_new, const int32_t* block_table,
+                       const int32_t* seq_lens, const int32_t* query_start_loc, void* k_pool, void* v_pool,
+                       void* stream);
+
+/*
  * Check the batch contents on the device: query_start_loc starts at 0, is
  * non-decreasing and ends at T_q; 0 <= q_len <= seq_len; ceil(seq_len/16) <=
  * max_pages_per_seq; every block-table entry a sequence reads lies in

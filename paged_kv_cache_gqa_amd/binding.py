@@ -79,8 +79,9 @@ def lib():
         L.pa_gather_kv.argtypes = [dp, i32, vp, vp, vp, i32, i32, vp, vp]
         L.pa_merge.argtypes = [i32, i64, i32, vp, vp, i32, vp, vp, vp]
         L.pa_validate.argtypes = [dp, vp, vp, vp, vp, sz, vp]
+        L.pa_append_kv.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp]
         for name in ("pa_check_desc", "pa_workspace_size", "pa_workspace_init", "pa_attention", "pa_plan", "pa_attention_planned",
-                     "pa_merge_planned", "pa_plan_read", "pa_gather_kv", "pa_merge", "pa_validate"):
+                     "pa_merge_planned", "pa_plan_read", "pa_gather_kv", "pa_merge", "pa_validate", "pa_append_kv"):
             getattr(L, name).restype = ctypes.c_int
         if L.pa_abi_version() != 1:
             raise PagedAttentionError("load", -1, "ABI version mismatch")
@@ -222,6 +223,24 @@ def gather_kv(desc: PaDesc, which: int, pool, block_table, seq_lens, seq: int, n
     _check("pa_gather_kv", lib().pa_gather_kv(ctypes.byref(desc), int(which), _ptr(pool), _ptr(block_table),
                                               _ptr(seq_lens), int(seq), int(n_keys), _ptr(dense), _stream(stream)))
     return dense
+
+
+def append_kv(k_new, v_new, k_pool, v_pool, block_table, seq_lens, query_start_loc, stream=None) -> None:
+    """Paged KV append (pa_append_kv): write k_new / v_new [T_q][Hkv][D] into the pools at each
+    sequence's last q_len positions."""
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("k_pool", k_pool), ("v_pool", v_pool),
+                    ("block_table", block_table), ("seq_lens", seq_lens), ("query_start_loc", query_start_loc)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    T, Hkv, D = k_new.shape
+    if v_new.shape != k_new.shape or k_new.dtype != k_pool.dtype or v_new.dtype != k_pool.dtype:
+        raise ValueError("k_new / v_new must be [T_q][Hkv][D] in the pools' dtype")
+    desc = PaDesc(num_seqs=seq_lens.shape[0], num_q_tokens=T, num_q_heads=Hkv, num_kv_heads=Hkv, head_dim=D,
+                  page_size=PAGE_SIZE, num_pages=k_pool.shape[0], max_pages_per_seq=block_table.shape[1],
+                  dtype=_DTYPES[k_pool.dtype], scale=1.0)
+    _check("pa_append_kv", lib().pa_append_kv(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(block_table),
+                                              _ptr(seq_lens), _ptr(query_start_loc), _ptr(k_pool), _ptr(v_pool),
+                                              _stream(stream)))
 
 
 def merge(o_parts, lse_parts, out_dtype=torch.float32, stream=None):

@@ -303,6 +303,28 @@ pa_status pa_merge(int32_t n_parts, int64_t rows, int32_t head_dim, const float*
                                                                                                         : PA_ERR_HIP;
 }
 
+pa_status pa_append_kv(const pa_desc* desc, const void* k_new, const void* v_new, const int32_t* block_table,
+                       const int32_t* seq_lens, const int32_t* qsl, void* k_pool, void* v_pool, void* stream) {
+  if (!desc) return PA_ERR_NULL_POINTER;
+  const pa_status st = pa_check_desc(desc);
+  if (st != PA_OK) return st;
+  if (desc->num_seqs == 0 || desc->num_q_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !block_table || !seq_lens || !qsl || !k_pool || !v_pool) return PA_ERR_NULL_POINTER;
+  if (desc->num_kv_heads > 65535) return PA_ERR_BAD_SHAPE;  // grid y
+  pa::AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.qsl = qsl;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.head_dim = desc->head_dim;
+  a.max_pages = desc->max_pages_per_seq;
+  return pa::launch_append_kv(a, desc->dtype, desc->num_seqs, desc->num_q_tokens, stream) == 0 ? PA_OK : PA_ERR_HIP;
+}
+
 pa_status pa_validate(const pa_desc* desc, const int32_t* block_table, const int32_t* seq_lens, const int32_t* qsl,
                       void* workspace, size_t workspace_bytes, void* stream) {
   if (!desc) return PA_ERR_NULL_POINTER;

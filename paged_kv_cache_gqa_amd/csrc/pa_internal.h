@@ -112,6 +112,19 @@ struct MergeArgs {
   int32_t num_q_heads;
 };
 
+struct AppendArgs {
+  const void* k_new;  // [T_q][Hkv][D]
+  const void* v_new;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* qsl;
+  void* k_pool;
+  void* v_pool;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t max_pages;
+};
+
 // Workspace: [header | arrival counters | per-sequence cost prefix | grain starts | partial lse |
 // partial o | unit list (plan inspection only)], every region 256-byte aligned.  The arrival
 // counters must be zero before a single-launch call; every call leaves them zero.
@@ -165,6 +178,9 @@ int launch_gather(int which, int dtype, int Hkv, int D, int max_pages, const voi
                   void* stream);
 int launch_merge(int n_parts, int64_t rows, int D, const float* o_parts, const float* lse_parts,
                  int out_dtype, void* out, float* lse, void* stream);
+// pages of one sequence per workgroup of the append kernel
+constexpr int kAppendPages = 2;
+int launch_append_kv(const AppendArgs& a, int dtype, int num_seqs, int num_q_tokens, void* stream);
 int launch_validate(const pa_desc& d, const int32_t* block_table, const int32_t* seq_lens,
                     const int32_t* qsl, int32_t* flag, void* stream);
 // Workgroups per CU the attention kernel can hold (occupancy query), or < 0 on error.

@@ -1495,6 +1495,64 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(int n_parts, int64_t ro
 }
 
 // ---------------------------------------------------------------------------
+// Paged KV append: the K/V rows of the new tokens go to positions n - q .. n - 1 of their
+// sequence (the window's own keys for the attention call).  Workgroup (s, g, z) writes pages
+// first + kAppendPages*z ... of sequence s, K/V head g.  K rows are copied as 16-byte vectors.
+// V rows of a page are staged in LDS ([slot][D], padded rows) and written back transposed: a full
+// page's [D][16] block as whole 16-byte vectors, a partial page slot by slot.
+// ---------------------------------------------------------------------------
+template <typename E>
+__global__ __launch_bounds__(256) void append_kv_kernel(AppendArgs a) {
+  constexpr int kPerVec = 16 / sizeof(E);            // elements per 16-byte vector
+  constexpr int kPitch = 128 + 16 / sizeof(E);        // LDS row pitch in elements (D <= 128, 16-byte pad)
+  __shared__ __align__(16) E tile[kPage * kPitch];
+  const int s = blockIdx.x, g = blockIdx.y;
+  const int n = a.seq_lens[s];
+  const int q0 = a.qsl[s];
+  const int qn = a.qsl[s + 1] - q0;
+  if (qn <= 0) return;
+  const int p0 = n - qn;  // position of the first new token
+  const int jl = (n - 1) / kPage;
+  const int D = a.head_dim, Hkv = a.num_kv_heads;
+  const int vpr = D / kPerVec;  // 16-byte vectors per row
+  const int32_t* bt = a.block_table + int64_t(s) * a.max_pages;
+  const E* kn = static_cast<const E*>(a.k_new);
+  const E* vn = static_cast<const E*>(a.v_new);
+  E* kp = static_cast<E*>(a.k_pool);
+  E* vp = static_cast<E*>(a.v_pool);
+  for (int j0 = p0 / kPage + int(blockIdx.z) * kAppendPages; j0 <= jl; j0 += int(gridDim.z) * kAppendPages)
+  for (int j = j0; j <= min(jl, j0 + kAppendPages - 1); ++j) {
+    const int lo = max(p0, j * kPage) - j * kPage, hi = min(n, (j + 1) * kPage) - j * kPage;  // slots [lo, hi)
+    const int w = hi - lo;
+    const int64_t blk = (int64_t(bt[j]) * Hkv + g) * D * kPage;  // (page, head) block, in elements
+    for (int idx = threadIdx.x; idx < w * vpr; idx += blockDim.x) {
+      const int it = idx / vpr, c = idx - it * vpr;
+      const int t = lo + it;
+      const int64_t row = (int64_t(q0 + j * kPage + t - p0) * Hkv + g) * D + c * kPerVec;  // new-token row
+      *reinterpret_cast<u32x4_t*>(kp + blk + int64_t(t) * D + c * kPerVec) =
+          *reinterpret_cast<const u32x4_t*>(kn + row);
+      *reinterpret_cast<u32x4_t*>(tile + t * kPitch + c * kPerVec) = *reinterpret_cast<const u32x4_t*>(vn + row);
+    }
+    __syncthreads();
+    if (w == kPage) {
+      for (int idx = threadIdx.x; idx < D * (kPage / kPerVec); idx += blockDim.x) {
+        const int d = idx / (kPage / kPerVec), t0 = (idx - d * (kPage / kPerVec)) * kPerVec;
+        E e[kPerVec];
+#pragma unroll
+        for (int k = 0; k < kPerVec; ++k) e[k] = tile[(t0 + k) * kPitch + d];
+        *reinterpret_cast<u32x4_t*>(vp + blk + int64_t(d) * kPage + t0) = __builtin_bit_cast(u32x4_t, e);
+      }
+    } else {
+      for (int e = threadIdx.x; e < D * w; e += blockDim.x) {
+        const int d = e / w, t = lo + (e - d * w);
+        vp[blk + int64_t(d) * kPage + t] = tile[t * kPitch + d];
+      }
+    }
+    __syncthreads();  // the tile is reused for the next page
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Page-walk gather: dense[g][j][d] = pool element of key j of sequence seq.
 // ---------------------------------------------------------------------------
 template <typename E>
@@ -1664,6 +1722,25 @@ int launch_gather(int which, int dtype, int Hkv, int D, int max_pages, const voi
     hipLaunchKernelGGL(gather_kernel<uint32_t>, dim3(unsigned(grid)), dim3(256), 0, as_stream(stream), which, Hkv, D,
                        max_pages, static_cast<const uint32_t*>(pool), block_table, seq_lens, seq, n_keys,
                        static_cast<uint32_t*>(dense));
+  return int(hipGetLastError());
+}
+
+int launch_append_kv(const AppendArgs& a, int dtype, int num_seqs, int num_q_tokens, void* stream) {
+  if (num_seqs == 0) return 0;
+  // a sequence's new tokens touch at most ceil(T_q / 16) + 1 pages
+  const int max_pages = (num_q_tokens + kPage - 1) / kPage + 1;
+  // page groups per (sequence, head): enough for the longest possible window, but no more than keeps
+  // the grid near 4096 workgroups (most windows are short; the kernel strides over the rest)
+  int groups = (max_pages + kAppendPages - 1) / kAppendPages;
+  const int64_t base = int64_t(num_seqs) * a.num_kv_heads;
+  const int cap = int(base >= 4096 ? 1 : 4096 / base);
+  if (groups > cap) groups = cap;
+  if (groups > 65535) groups = 65535;
+  const dim3 grid(unsigned(num_seqs), unsigned(a.num_kv_heads), unsigned(groups));
+  if (dtype == PA_BF16)
+    hipLaunchKernelGGL(append_kv_kernel<uint16_t>, grid, dim3(256), 0, as_stream(stream), a);
+  else
+    hipLaunchKernelGGL(append_kv_kernel<uint32_t>, grid, dim3(256), 0, as_stream(stream), a);
   return int(hipGetLastError());
 }
 
