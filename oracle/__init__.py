@@ -54,6 +54,9 @@ def open_library(path: str):
     lib.oracle_merge.restype = ip
     lib.oracle_append.argtypes = [ip, ip, ip, ip, ip, ip, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_append.restype = ip
+    lib.oracle_attention_tree.argtypes = [ip, ip, ip, ip, ip, ip, ip, vp, vp, vp, vp, vp, vp, vp,
+                                          ctypes.c_double, vp, vp]
+    lib.oracle_attention_tree.restype = ip
     lib.oracle_max_threads.restype = ip
     return lib
 
@@ -175,3 +178,27 @@ def append(k_new, v_new, k_pool, v_pool, block_table, seq_lens, query_start_loc,
     _check(lib.oracle_append(B, Hkv, D, dt, NP, bt.shape[1], _ptr(bt), _ptr(sl), _ptr(qsl), _ptr(k_new),
                              _ptr(v_new), _ptr(k_out), _ptr(v_out)))
     return k_out, v_out
+
+
+def attention_tree(q, k_pool, v_pool, block_table, seq_lens, query_start_loc, tree_mask, scale: float, lib=None):
+    """fp64 attention with tree-structured verify windows: tree_mask [T_q] uint64, bit k of row r's
+    mask lets it see window token k (windows of at most 64 tokens; longer windows are causal)."""
+    lib = _load(lib)
+    q = np.ascontiguousarray(q)
+    k_pool = np.ascontiguousarray(k_pool)
+    v_pool = np.ascontiguousarray(v_pool)
+    dt = _dtype_code(q)
+    assert _dtype_code(k_pool) == dt and _dtype_code(v_pool) == dt
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    qsl = np.ascontiguousarray(query_start_loc, dtype=np.int32)
+    tm = np.ascontiguousarray(tree_mask, dtype=np.uint64)
+    T, Hq, D = q.shape
+    NP, Hkv = k_pool.shape[0], k_pool.shape[1]
+    B = sl.shape[0]
+    assert tm.shape == (T,) and qsl.shape == (B + 1,) and int(qsl[-1]) == T
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    lse = np.zeros((T, Hq), dtype=np.float64)
+    _check(lib.oracle_attention_tree(B, Hq, Hkv, D, dt, NP, bt.shape[1], _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                     _ptr(bt), _ptr(sl), _ptr(qsl), _ptr(tm), float(scale), _ptr(out), _ptr(lse)))
+    return out, lse

@@ -171,6 +171,81 @@ int oracle_attention(int B, int Hq, int Hkv, int D, int dtype, int num_pages, in
 }
 
 /*
+ * Tree-structured verify windows (XY-Serve verdict page, referee_report
+ * "significance" and desk_editor letter: verification of speculative token
+ * trees).  Row i of a window of q <= 64 tokens over n keys sees every context
+ * key j < n - q, and window key j = n - q + k only where bit k of
+ * tree_mask[r] is set, and never a key past its own position n - q + i.  Rows
+ * of windows longer than 64 follow the causal rule (their mask is ignored).
+ * A row that sees no key gets out = 0 and lse = -inf.  Otherwise the same
+ * two-pass fp64 computation as oracle_attention.
+ */
+static int tree_visible(int j, int p, int win0, int qn, uint64_t mask) {
+  if (j > p) return 0;
+  if (j < win0 || qn > 64) return 1;
+  return (int)((mask >> (j - win0)) & 1u);
+}
+
+int oracle_attention_tree(int B, int Hq, int Hkv, int D, int dtype, int num_pages, int max_pages,
+                          const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_table, const int32_t* seq_lens, const int32_t* qsl,
+                          const uint64_t* tree_mask, double scale, double* out, double* lse) {
+  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return ORACLE_BAD_ARG;
+  int rc = check_batch(B, Hq, Hkv, D, num_pages, max_pages, block_table, seq_lens, qsl);
+  if (rc != ORACLE_OK) return rc;
+  const int G = Hq / Hkv;
+  int max_n = 0;
+  for (int s = 0; s < B; ++s) max_n = seq_lens[s] > max_n ? seq_lens[s] : max_n;
+  double* x = (double*)malloc(sizeof(double) * (size_t)(max_n > 0 ? max_n : 1));
+  double* acc = (double*)malloc(sizeof(double) * (size_t)D);
+  if (!x || !acc) {
+    free(x);
+    free(acc);
+    return ORACLE_NO_MEMORY;
+  }
+  for (int s = 0; s < B; ++s) {
+    const int n = seq_lens[s];
+    const int qn = qsl[s + 1] - qsl[s];
+    const int win0 = n - qn;
+    const int32_t* bt = block_table + (int64_t)s * max_pages;
+    for (int i = 0; i < qn; ++i) {
+      const int64_t r = qsl[s] + i;
+      const int p = win0 + i;
+      for (int h = 0; h < Hq; ++h) {
+        const int kvh = h / G; /* K/V head read by query head h */
+        const int64_t qrow = (r * Hq + h) * (int64_t)D;
+        double m = -INFINITY;
+        for (int j = 0; j <= p; ++j) {
+          if (!tree_visible(j, p, win0, qn, tree_mask[r])) continue;
+          const int64_t page = bt[j / ORACLE_PAGE];
+          const int slot = j % ORACLE_PAGE;
+          double qk = 0.0;
+          for (int d = 0; d < D; ++d)
+            qk += widen(q, dtype, qrow + d) * widen(k_pool, dtype, k_offset(page, kvh, slot, d, Hkv, D));
+          x[j] = qk * scale;
+          m = x[j] > m ? x[j] : m;
+        }
+        double l = 0.0;
+        for (int d = 0; d < D; ++d) acc[d] = 0.0;
+        for (int j = 0; j <= p; ++j) {
+          if (!tree_visible(j, p, win0, qn, tree_mask[r])) continue;
+          const int64_t page = bt[j / ORACLE_PAGE];
+          const int slot = j % ORACLE_PAGE;
+          const double wj = exp(x[j] - m);
+          l += wj;
+          for (int d = 0; d < D; ++d) acc[d] += wj * widen(v_pool, dtype, v_offset(page, kvh, slot, d, Hkv, D));
+        }
+        for (int d = 0; d < D; ++d) out[qrow + d] = l > 0.0 ? acc[d] / l : 0.0;
+        lse[r * Hq + h] = l > 0.0 ? m + log(l) : -INFINITY;
+      }
+    }
+  }
+  free(x);
+  free(acc);
+  return ORACLE_OK;
+}
+
+/*
  * Gather sequence `seq`'s rows of one pool into dense [Hkv][n][D] order by
  * walking its block table (element bytes copied unchanged).
  * which = 0: K pool layout [NP][Hkv][16][D]; which = 1: V pool layout [NP][Hkv][D][16].

@@ -278,3 +278,34 @@ def subset(w: Workload, seqs) -> Workload:
                     seq_lens=w.seq_lens[seqs].copy(), query_start_loc=qsl,
                     block_table=np.ascontiguousarray(w.block_table[seqs]), q=np.ascontiguousarray(w.q[rows]),
                     k_pool=w.k_pool, v_pool=w.v_pool, meta=dict(w.meta, subset=seqs.tolist()))
+
+
+def causal_masks(q_lens) -> np.ndarray:
+    """Tree masks that encode the plain causal rule: row i of a window sees window tokens 0..i."""
+    rows = []
+    for q in np.asarray(q_lens):
+        for i in range(int(q)):
+            rows.append((1 << (i + 1)) - 1 if i < 63 else (1 << 64) - 1)
+    return np.array(rows, dtype=np.uint64)
+
+
+def random_trees(q_lens, seed: int):
+    """A random draft tree per window (token 0 is the root, token k > 0 has a parent in [0, k)) and
+    the per-row masks: bit k of row i's mask is set iff window token k is i or an ancestor of i.
+    Windows longer than 64 tokens get causal masks.  Returns (masks uint64 [T_q], parents list)."""
+    rng = np.random.default_rng([seed, 7])
+    masks, parents = [], []
+    for q in np.asarray(q_lens):
+        q = int(q)
+        par = [-1] + [int(rng.integers(0, k)) for k in range(1, q)]
+        parents.append(par)
+        for i in range(q):
+            if q > 64:
+                masks.append((1 << (i + 1)) - 1 if i < 63 else (1 << 64) - 1)
+                continue
+            m, k = 0, i
+            while k >= 0:
+                m |= 1 << k
+                k = par[k]
+            masks.append(m)
+    return np.array(masks, dtype=np.uint64), parents

@@ -406,5 +406,66 @@ def pin_append(lib=None):
             assert np.max(np.abs(o[q0:q1] - ref.transpose(0, 1).numpy())) <= 1e-9, (seed, s)
 
 
+def pin_tree(lib=None):
+    """Tree-structured verify windows.  (1) causal masks give exactly the plain attention; (2) with
+    random draft trees, every row equals fp64 torch SDPA of that one query over the sequence's
+    context followed by the K/V of its ancestor path (built from the parent pointers, not from the
+    masks); (3) windows longer than 64 tokens ignore their masks; (4) a row that sees no key gives
+    out = 0 and lse = -inf."""
+    import torch
+    for seed, (B, maxlen, Hq, Hkv, D, dt, maxq) in enumerate([
+            (4, 120, 8, 2, 64, "f32", 12), (3, 90, 4, 1, 64, "bf16", 20), (5, 60, 8, 8, 64, "bf16", 6)]):
+        w = W.make_random(500 + seed, B, maxlen, Hq, Hkv, D, dt, max_q=maxq)
+        args = (w.q, w.k_pool, w.v_pool, w.block_table, w.seq_lens, w.query_start_loc)
+        o_ref, l_ref = run(w, lib)
+        o, l = oracle.attention_tree(*args, W.causal_masks(w.q_lens()), w.scale, lib=lib)
+        assert np.max(np.abs(o - o_ref)) <= 1e-13 and np.max(np.abs(l - l_ref)) <= 1e-13, seed
+        masks, parents = W.random_trees(w.q_lens(), 600 + seed)
+        o, l = oracle.attention_tree(*args, masks, w.scale, lib=lib)
+        q = widen(w.q)
+        G = Hq // Hkv
+        for s in range(w.num_seqs):
+            n = int(w.seq_lens[s])
+            q0, q1 = int(w.query_start_loc[s]), int(w.query_start_loc[s + 1])
+            win = q1 - q0
+            K, V = dense_kv(w, s)
+            for i in range(win):
+                path, k = [], i
+                while k >= 0:
+                    path.append(n - win + k)
+                    k = parents[s][k]
+                keys = list(range(n - win)) + sorted(path)
+                Kp = torch.from_numpy(K[:, keys]).repeat_interleave(G, dim=0)
+                Vp = torch.from_numpy(V[:, keys]).repeat_interleave(G, dim=0)
+                Q = torch.from_numpy(q[q0 + i])[:, None, :]  # [Hq][1][D]
+                ref = torch.nn.functional.scaled_dot_product_attention(Q[None], Kp[None], Vp[None], scale=w.scale)[0]
+                ref_l = torch.logsumexp((Q @ Kp.transpose(1, 2).contiguous())[:, 0] * w.scale, dim=-1)
+                assert np.max(np.abs(o[q0 + i] - ref[:, 0].numpy())) <= 1e-12, (seed, s, i)
+                assert np.max(np.abs(l[q0 + i] - ref_l.numpy())) <= 1e-12, (seed, s, i)
+    # (3) a 70-token window over 150 keys and a 20-token window: the long window ignores its masks
+    rng = np.random.default_rng(510)
+    lw = from_logical("f32", 4, 2, 16, 0.25, 20, [
+        dict(page_ids=[3, 7, 1, 12, 0, 9, 15, 4, 11, 18], keys=rng.standard_normal((150, 2, 16)),
+             values=rng.standard_normal((150, 2, 16)), queries=rng.standard_normal((70, 4, 16))),
+        dict(page_ids=[5, 2], keys=rng.standard_normal((30, 2, 16)), values=rng.standard_normal((30, 2, 16)),
+             queries=rng.standard_normal((20, 4, 16)))])
+    masks, _ = W.random_trees(lw.q_lens(), 7)
+    masks[:70] = rng.integers(0, 2**63, size=70, dtype=np.int64).astype(np.uint64)  # garbage: ignored
+    causal = W.causal_masks(lw.q_lens())
+    o_ref, l_ref = oracle.attention_tree(lw.q, lw.k_pool, lw.v_pool, lw.block_table, lw.seq_lens,
+                                         lw.query_start_loc, causal, lw.scale, lib=lib)
+    o, l = oracle.attention_tree(lw.q, lw.k_pool, lw.v_pool, lw.block_table, lw.seq_lens, lw.query_start_loc,
+                                 masks, lw.scale, lib=lib)
+    assert np.max(np.abs(o[:70] - o_ref[:70])) <= 1e-13 and np.max(np.abs(l[:70] - l_ref[:70])) <= 1e-13
+    assert np.max(np.abs(o[70:] - o_ref[70:])) > 1e-6  # the short window's tree does change its rows
+    # (4) no context and a row whose mask hides even itself
+    ew = from_logical("f32", 4, 2, 8, 0.3, 4, [
+        dict(page_ids=[2], keys=rng.standard_normal((3, 2, 8)), values=rng.standard_normal((3, 2, 8)),
+             queries=rng.standard_normal((3, 4, 8)))])
+    o, l = oracle.attention_tree(ew.q, ew.k_pool, ew.v_pool, ew.block_table, ew.seq_lens, ew.query_start_loc,
+                                 np.array([1, 0, 7], dtype=np.uint64), ew.scale, lib=lib)
+    assert np.all(o[1] == 0.0) and np.all(np.isneginf(l[1])) and np.all(np.isfinite(l[[0, 2]]))
+
+
 ALL_PINS = [pin_brute_force, pin_golden, pin_closed_forms, pin_invariants, pin_merge_of_splits,
-            pin_sdpa, pin_gather, pin_append]
+            pin_sdpa, pin_gather, pin_append, pin_tree]

@@ -41,6 +41,10 @@ def test_oracle_append():
     P.pin_append()
 
 
+def test_oracle_tree_masks():
+    P.pin_tree()
+
+
 def test_oracle_gather_page_walk():
     P.pin_gather()
 
@@ -111,6 +115,11 @@ MUTATIONS = [
      "memcpy((char*)v_pool + k_offset(pg, g, t, d, Hkv, D) * eb"),
     ("append reads the wrong head", "const int64_t src = (r * Hkv + g) * D + d;",
      "const int64_t src = (r * Hkv + (Hkv - 1 - g)) * D + d;"),
+    ("tree bit index off by one", "return (int)((mask >> (j - win0)) & 1u);", "return (int)((mask >> (j - win0 + 1)) & 1u);"),
+    ("tree window starts one late", "const int win0 = n - qn;\n    const int32_t* bt", "const int win0 = n - qn + 1;\n    const int32_t* bt"),
+    ("tree always shows the row itself", "return (int)((mask >> (j - win0)) & 1u);",
+     "return j == p ? 1 : (int)((mask >> (j - win0)) & 1u);"),
+    ("tree masks applied to long windows", "if (j < win0 || qn > 64) return 1;", "if (j < win0) return 1;"),
     ("page lookup off by one page", "const int64_t pg = bt[j / ORACLE_PAGE];\n        const int t = j % ORACLE_PAGE;\n        double",
      "const int64_t pg = bt[(j / ORACLE_PAGE + 1) % ((n + 15) / 16)];\n        const int t = j % ORACLE_PAGE;\n        double"),
 ]
