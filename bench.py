@@ -202,9 +202,10 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--part", default="all", choices=["all", "prefill", "decode"],
                     help="configuration 3 only: time its prefill chunks or its decode rows alone")
-    ap.add_argument("--op", default="attention", choices=["attention", "append"],
+    ap.add_argument("--op", default="attention", choices=["attention", "append", "tree"],
                     help="attention (default): the attention call; append: the paged KV append of the batch's new "
-                         "tokens (pa_append_kv)")
+                         "tokens (pa_append_kv); tree: attention with each window a random draft-token tree "
+                         "(pa_attention_tree)")
     ap.add_argument("--staged", action="store_true",
                     help="time pa_plan + pa_attention_planned + pa_merge_planned instead of the single launch")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
@@ -224,7 +225,8 @@ def main() -> int:
 
     if args.record_traffic:
         from paged_kv_cache_gqa_amd import workloads as W
-        name = W.CONFIG_NAMES[args.config] + ("" if args.part == "all" else f"-{args.part}-part")
+        name = W.CONFIG_NAMES[args.config] + ("" if args.part == "all" else f"-{args.part}-part") + \
+            ("-tree" if args.op == "tree" else "")
         kernel = "attention_kernel" if args.staged else "attention_fused_kernel"
         print(json.dumps(record_traffic(name, *args.record_traffic, kernel=kernel)))
         return 0
@@ -265,9 +267,15 @@ def main() -> int:
     sp = vp(stream.cuda_stream)
     wsn = ws.numel()
     plan_args = (dref, vp(t["seq_lens"].data_ptr()), vp(t["query_start_loc"].data_ptr()), vp(ws.data_ptr()), wsn, sp)
+    tree = args.op == "tree"
+    if tree:
+        masks, _ = W.random_trees(w.q_lens(), 1000 + args.config)
+        tm = torch.from_numpy(masks.view(np.int64)).cuda()
+    mask_arg = (vp(tm.data_ptr()),) if tree else ()
     attn_args = [(dref, vp(t["q"].data_ptr()), vp(k.data_ptr()), vp(v.data_ptr()), vp(t["block_table"].data_ptr()),
-                  vp(t["seq_lens"].data_ptr()), vp(t["query_start_loc"].data_ptr()), vp(out.data_ptr()),
+                  vp(t["seq_lens"].data_ptr()), vp(t["query_start_loc"].data_ptr()), *mask_arg, vp(out.data_ptr()),
                   vp(lse.data_ptr()), vp(ws.data_ptr()), wsn, sp) for k, v in pools]
+    attention_call = L.pa_attention_tree if tree else L.pa_attention
     merge_args = (dref, vp(t["seq_lens"].data_ptr()), vp(t["query_start_loc"].data_ptr()), vp(out.data_ptr()),
                   vp(lse.data_ptr()), vp(ws.data_ptr()), wsn, sp)
 
@@ -283,7 +291,7 @@ def main() -> int:
         else:
             if ev is not None:
                 ev[0].record(stream)
-            rc = L.pa_attention(*attn_args[i % n_copies])
+            rc = attention_call(*attn_args[i % n_copies])
             if ev is not None:
                 ev[1].record(stream)
         if rc:
@@ -321,8 +329,11 @@ def main() -> int:
     tflops = alg_flops / (ms_per_step * 1e-3) / 1e12
     peak_tf = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
     kernel = "attention_kernel" if args.staged else "attention_fused_kernel"
+    if tree and args.staged:
+        raise SystemExit("--op tree runs the single launch only")
     config = {"workload": f"{w.name} (configuration {args.config})", **DESCRIPTIONS[args.config],
               "part": args.part, "path": "staged (3 launches)" if args.staged else "single launch",
+              "windows": "random draft-token trees (per-row ancestor masks)" if tree else "causal",
               "page_size": 16, "seed": 1000 + args.config, "kv_pool_copies": n_copies,
               "algorithmic_bytes": alg_bytes, "algorithmic_flops": alg_flops}
     line = {
@@ -333,7 +344,7 @@ def main() -> int:
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "tflops": round(tflops, 3), "frac_of_mfma_peak": round(tflops / peak_tf, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name, kernel),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name + ("-tree" if tree else ""), kernel),
                      "kernel": f"pa::{kernel}", "kernel_ms_mean": round(attn_mean, 5),
                      "kernel_ms_p10_p90": [round(float(np.percentile(attn_ms, 10)), 5),
                                            round(float(np.percentile(attn_ms, 90)), 5)],

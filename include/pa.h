@@ -142,6 +142,25 @@ pa_status pa_attention(const pa_desc* desc, const void* q, const void* k_pool, c
                        size_t workspace_bytes, void* stream);
 
 /*
+ * pa_attention for batches whose verify windows are draft-token trees
+ * (speculative decoding with a token tree: XY-Serve verdict page,
+ * referee_report "significance" and the desk-editor letter on verifying token
+ * trees).  tree_mask [T_q] uint64 (device memory, read only): for a sequence
+ * whose window has q <= 64 tokens, window row i sees every context key
+ * (positions < n - q), and window token k (position n - q + k) only where bit
+ * k of tree_mask[query_start_loc[s] + i] is set; keys past the row's own
+ * position n - q + i stay hidden whatever its bits say.  Rows of windows
+ * longer than 64 tokens follow the causal rule and their entries are
+ * ignored.  The causal rule is the mask with bits 0..i set.  A row that sees
+ * no key gets out = 0 and lse = -inf.  Same launch, workspace and errors as
+ * pa_attention; tree_mask may not be NULL when T_q > 0.
+ */
+pa_status pa_attention_tree(const pa_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_table, const int32_t* seq_lens, const int32_t* query_start_loc,
+                            const uint64_t* tree_mask, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * The same computation in three stages, for callers that inspect, time or
  * reuse them.  pa_plan writes the plan into the workspace (it reads only
  * seq_lens and query_start_loc; a plan stays valid while those and desc are

@@ -10,7 +10,7 @@ seeded input generator) can be used without torch or a GPU.
 _BINDING_NAMES = {
     "attention", "plan", "attention_planned", "merge_planned", "plan_read", "gather_kv", "merge", "validate",
     "check_desc", "workspace_size", "alloc_workspace", "make_desc", "status_string", "abi_version", "lib",
-    "PagedAttentionError", "PaDesc", "to_device", "append_kv", "workspace_init",
+    "PagedAttentionError", "PaDesc", "to_device", "append_kv", "workspace_init", "attention_tree",
 }
 
 

@@ -80,8 +80,9 @@ def lib():
         L.pa_merge.argtypes = [i32, i64, i32, vp, vp, i32, vp, vp, vp]
         L.pa_validate.argtypes = [dp, vp, vp, vp, vp, sz, vp]
         L.pa_append_kv.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.pa_attention_tree.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for name in ("pa_check_desc", "pa_workspace_size", "pa_workspace_init", "pa_attention", "pa_plan", "pa_attention_planned",
-                     "pa_merge_planned", "pa_plan_read", "pa_gather_kv", "pa_merge", "pa_validate", "pa_append_kv"):
+                     "pa_merge_planned", "pa_plan_read", "pa_gather_kv", "pa_merge", "pa_validate", "pa_append_kv", "pa_attention_tree"):
             getattr(L, name).restype = ctypes.c_int
         if L.pa_abi_version() != 1:
             raise PagedAttentionError("load", -1, "ABI version mismatch")
@@ -182,6 +183,27 @@ def attention(q, k_pool, v_pool, block_table, seq_lens, query_start_loc, scale: 
     _check("pa_attention", lib().pa_attention(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                               _ptr(block_table), _ptr(seq_lens), _ptr(query_start_loc), _ptr(out),
                                               _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def attention_tree(q, k_pool, v_pool, block_table, seq_lens, query_start_loc, tree_mask, scale: float, out=None,
+                   lse=None, workspace=None, stream=None):
+    """pa_attention_tree: verify windows as draft-token trees.  tree_mask: [T_q] int64 device tensor holding
+    each row's uint64 mask bits.  Returns (out, lse)."""
+    _check_inputs(q, k_pool, v_pool, block_table, seq_lens, query_start_loc)
+    if not tree_mask.is_cuda or tree_mask.dtype not in (torch.int64, torch.uint64) or tree_mask.shape != q.shape[:1]:
+        raise ValueError("tree_mask must be a [T_q] int64 / uint64 device tensor")
+    desc = make_desc(q, k_pool, block_table, seq_lens, scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(desc, q.device)
+    _check("pa_attention_tree",
+           lib().pa_attention_tree(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                   _ptr(seq_lens), _ptr(query_start_loc), _ptr(tree_mask.contiguous()), _ptr(out),
+                                   _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out, lse
 
 

@@ -120,6 +120,7 @@ pa::AttnArgs attn_args(const pa_desc& d, const void* q, const void* k, const voi
   a.lse = lse;
   a.part_o = ws.part_o;
   a.part_lse = ws.part_lse;
+  a.tree_mask = nullptr;
   a.arrive = ws.arrive;
   a.num_q_heads = d.num_q_heads;
   a.max_pages = d.max_pages_per_seq;
@@ -226,9 +227,11 @@ pa_status pa_merge_planned(const pa_desc* desc, const int32_t* seq_lens, const i
   return pa::launch_merge_planned(m, desc->dtype, desc->head_dim, grid, stream) == 0 ? PA_OK : PA_ERR_HIP;
 }
 
-pa_status pa_attention(const pa_desc* desc, const void* q, const void* k_pool, const void* v_pool,
-                       const int32_t* block_table, const int32_t* seq_lens, const int32_t* qsl, void* out, float* lse,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+pa_status single_launch(const pa_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* block_table, const int32_t* seq_lens, const int32_t* qsl,
+                        const uint64_t* tree_mask, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   if (!desc) return PA_ERR_NULL_POINTER;
   const pa_status st = pa_check_desc(desc);
   if (st != PA_OK) return st;
@@ -239,8 +242,26 @@ pa_status pa_attention(const pa_desc* desc, const void* q, const void* k_pool, c
   Ws ws;
   const pa_status ps = prepare(desc, workspace, workspace_bytes, &grid, &ws);
   if (ps != PA_OK) return ps;
-  const pa::AttnArgs a = attn_args(*desc, q, k_pool, v_pool, block_table, seq_lens, qsl, out, lse, ws);
+  pa::AttnArgs a = attn_args(*desc, q, k_pool, v_pool, block_table, seq_lens, qsl, out, lse, ws);
+  a.tree_mask = tree_mask;
   return pa::launch_attention_fused(a, desc->dtype, desc->head_dim, grid, stream) == 0 ? PA_OK : PA_ERR_HIP;
+}
+}  // namespace
+
+pa_status pa_attention(const pa_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_table, const int32_t* seq_lens, const int32_t* qsl, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return single_launch(desc, q, k_pool, v_pool, block_table, seq_lens, qsl, nullptr, out, lse, workspace,
+                       workspace_bytes, stream);
+}
+
+pa_status pa_attention_tree(const pa_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_table, const int32_t* seq_lens, const int32_t* qsl,
+                            const uint64_t* tree_mask, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (desc && desc->num_q_tokens > 0 && !tree_mask) return PA_ERR_NULL_POINTER;
+  return single_launch(desc, q, k_pool, v_pool, block_table, seq_lens, qsl, tree_mask, out, lse, workspace,
+                       workspace_bytes, stream);
 }
 
 pa_status pa_workspace_init(const pa_desc* desc, void* workspace, size_t workspace_bytes, void* stream) {

@@ -82,6 +82,7 @@ struct AttnArgs {
   float* lse;
   float* part_o;    // [grains][2][128][D]: per grain, the piece of its first and of its last unit
   float* part_lse;  // [grains][2][128]
+  const uint64_t* tree_mask;  // [T_q] per-row window masks, or null for the causal rule
   int32_t* arrive;  // [grains]: pieces of the split unit whose first piece is in grain k that have
                     // finished (single-launch path; zero between calls)
   int32_t num_q_heads;

@@ -412,13 +412,22 @@ __device__ __forceinline__ void load_v(const ChunkPages& cp, uint32_t kl, uint32
   for (int f = 0; f < TR::kVF; ++f) vf[f] = frag<TR>(cp, kl, vl, TR::kKF + f);
 }
 
+// Tree-structured verify windows: per row tile, the lane's row mask (bit k: window token k
+// visible; all ones for rows of windows longer than 64 tokens) and the first window key.
+template <int RT>
+struct TreeMask {
+  uint64_t m[RT];
+  int win0;
+};
+
 // Scores of one chunk for every row tile, masked, folded into the online softmax.
 // Returns the P operands; rescales O by exp2(m_old - m_new).
-// `getq(rt, qf)` fills the Q fragments of row tile rt (from registers or LDS).
-template <class TR, int RT, class GetQ>
+// `getq(rt, qf)` fills the Q fragments of row tile rt (from registers or LDS).  kTree: keys of
+// the window are also masked by the rows' tree masks.
+template <class TR, int RT, bool kTree, class GetQ>
 __device__ __forceinline__ void softmax_chunk(State<TR, RT>& st, GetQ getq, const u32x4_t (&kf)[TR::kKF], int key0,
-                                              const int (&p_row)[RT], bool mask, float sl2, int lane,
-                                              typename TR::PFrag (&pf)[RT]) {
+                                              const int (&p_row)[RT], const TreeMask<RT>& tm, bool mask, float sl2,
+                                              int lane, typename TR::PFrag (&pf)[RT]) {
   const int quad = lane >> 4;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -434,8 +443,21 @@ __device__ __forceinline__ void softmax_chunk(State<TR, RT>& st, GetQ getq, cons
     }
     if (mask) {
       const int lim = p_row[rt] - key0;  // element j visible iff its key <= lim
+      // tree rows: a window key k (>= 0) is visible only where bit k of the row's mask is set.
+      // Written branch-free (bitwise & | on the conditions, the bit index clamped to 0..63): a
+      // short-circuit form compiled to divergent branches that lost the score of visible keys.
+      const uint32_t m_lo = uint32_t(tm.m[rt]), m_hi = uint32_t(tm.m[rt] >> 32);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = p_key(j, quad) <= lim ? x[j] : -INFINITY;
+      for (int j = 0; j < 8; ++j) {
+        bool vis = p_key(j, quad) <= lim;
+        if constexpr (kTree) {
+          const int k = key0 + p_key(j, quad) - tm.win0;  // window token index of the key
+          const uint32_t kc = uint32_t(min(max(k, 0), 63));
+          const uint32_t bit = ((kc < 32 ? m_lo : m_hi) >> (kc & 31)) & 1u;
+          vis = vis & ((k < 0) | (bit != 0u));
+        }
+        x[j] = vis ? x[j] : -INFINITY;
+      }
     }
     float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     mx = quad_max(mx);
@@ -490,6 +512,23 @@ __device__ __forceinline__ RowInfo row_info(const AttnArgs& A, const pa_plan_uni
   ri.head = U.kv_head * A.plan.group + hh;
   ri.p = ri.valid ? n_seq - qn + t : -1;
   return ri;
+}
+
+// The tree masks of a unit's row tiles (rows of windows longer than 64 tokens: all ones) and the
+// first key from which chunks need masking: the window start for a tree window, else the first
+// row's diagonal.
+template <int RT, bool kTree>
+__device__ __forceinline__ int tree_setup(const AttnArgs& A, const RowInfo (&ri)[RT], int n_seq, int qn, int min_p,
+                                          TreeMask<RT>& tm) {
+  tm.win0 = n_seq - qn;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    tm.m[rt] = (kTree && qn <= 64 && ri[rt].valid) ? A.tree_mask[ri[rt].tok] : ~uint64_t(0);
+    // The loads complete here, before the unit's first DMA: the waits for the DMAs count the loads
+    // issued after them, and a mask load moved past a DMA would throw that count off.
+    if constexpr (kTree) asm volatile("" ::"v"(tm.m[rt]));
+  }
+  return (kTree && qn <= 64) ? tm.win0 : min_p + 1;
 }
 
 // Q fragment of one row; for a negative scale the signs are flipped (exact), so that the
@@ -604,7 +643,7 @@ __device__ __forceinline__ void lds_barrier() {
 // ---------------------------------------------------------------------------
 // Key-split unit (decode / verify, <= 32 rows): wave w takes chunks i0+w, i0+w+4, ...
 // ---------------------------------------------------------------------------
-template <class TR, int RT>
+template <class TR, int RT, bool kTree>
 __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, int i0, int i1, int part, Smem<TR>& sm) {
   int lane = threadIdx.x & 63;
   asm volatile("" : "+v"(lane));  // lane-derived values are recomputed per unit, not held across the unit loop
@@ -624,6 +663,8 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
     p_row[rt] = ri[rt].p;
   }
   const int min_p = n_seq - qn + U.row0 / A.plan.group;  // first row's last visible key
+  TreeMask<RT> tm;
+  const int mask_from = tree_setup<RT, kTree>(A, ri, n_seq, qn, min_p, tm);
 
   // Q fragments live in this wave's slice of LDS (re-read every chunk; keeps VGPRs for K/V in flight).
   // Order of issue at a unit start: Q loads, then the first chunk's K/V loads, then the LDS copy of Q,
@@ -705,12 +746,13 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
         for (int f = 0; f < TR::kQF; ++f) a[f] = lds_addr(qlds + (rt * TR::kQF + f) * 64 + lane);
         lds_read_b128<TR::kQF>(a, qf);
       };
-      softmax_chunk<TR, RT>(st, getq_asm, kf, key0, p_row, key0 + kChunkKeys - 1 > min_p, A.scale_log2, lane,
-                            pf);
+      softmax_chunk<TR, RT, kTree>(st, getq_asm, kf, key0, p_row, tm, key0 + kChunkKeys - 1 >= mask_from,
+                                   A.scale_log2, lane, pf);
       asm volatile("" ::: "memory");
     } else {
       asm volatile("" ::: "memory");  // keep the Q reads inside the loop
-      softmax_chunk<TR, RT>(st, getq, kf, key0, p_row, key0 + kChunkKeys - 1 > min_p, A.scale_log2, lane, pf);
+      softmax_chunk<TR, RT, kTree>(st, getq, kf, key0, p_row, tm, key0 + kChunkKeys - 1 >= mask_from,
+                                   A.scale_log2, lane, pf);
       load_k<TR>(cp, kl, vl, kf);
     }
     nx = page_ids(bt_row, min(cn + kWaves, i1 - 1), n_seq);
@@ -764,10 +806,11 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
 // One chunk of a row-split unit: start the DMA of chunk `next` (if >= 0) into slot `fill`, then
 // compute on the chunk held in slot `cur` (a different slot, landed before the last barrier).
 // `after_reads` runs once this chunk's LDS reads are done (it starts the next page-id loads).
-template <class TR, int RT, class Issue, class After, class GetQ>
+template <class TR, int RT, bool kTree, class Issue, class After, class GetQ>
 __device__ __forceinline__ void ring_step(char* fill, const char* cur, Issue issue, bool do_issue, After after_reads,
                                           bool active, State<TR, RT>& st, GetQ getq, int key0,
-                                          const int (&p_row)[RT], int min_p, int n_seq, float sl2, int lane) {
+                                          const int (&p_row)[RT], const TreeMask<RT>& tm, int mask_from, int n_seq,
+                                          float sl2, int lane) {
   using RG = Ring<TR>;
   if (do_issue) issue(fill);
   if (active) {
@@ -775,7 +818,7 @@ __device__ __forceinline__ void ring_step(char* fill, const char* cur, Issue iss
     u32x4_t kf[TR::kKF];
     TR::template lds_read_k<RG>(cur, lane, kf);
     typename TR::PFrag pf[RT];
-    softmax_chunk<TR, RT>(st, getq, kf, key0, p_row, key0 + kChunkKeys - 1 > min_p, sl2, lane, pf);
+    softmax_chunk<TR, RT, kTree>(st, getq, kf, key0, p_row, tm, key0 + kChunkKeys - 1 >= mask_from, sl2, lane, pf);
     u32x4_t vf[TR::kVF];
     TR::template lds_read_v<RG>(cur, lane, vf);
     asm volatile("" ::: "memory");
@@ -792,7 +835,7 @@ __device__ __forceinline__ void ring_step(char* fill, const char* cur, Issue iss
 // workgroup streams chunks through an LDS ring with global->LDS DMA, kNB - 1
 // chunks ahead of the one being computed; every wave issues 1/4 of each chunk.
 // ---------------------------------------------------------------------------
-template <class TR>
+template <class TR, bool kTree>
 __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, int i0, int i1, int part, Smem<TR>& sm) {
   using RG = Ring<TR>;
   constexpr int RT = 2;
@@ -815,6 +858,8 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
     p_row[rt] = ri[rt].p;
   }
   const int min_p = n_seq - qn + (U.row0 + 32 * w) / A.plan.group;
+  TreeMask<RT> tm;
+  const int mask_from = tree_setup<RT, kTree>(A, ri, n_seq, qn, min_p, tm);
 
   u32x4_t qreg[RT][TR::kQF];
 #pragma unroll
@@ -864,11 +909,11 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
     else wait_vmcnt<0>();
     lds_barrier();  // chunk c is in LDS for every wave; chunk c-1's slot is free
     const int next = c + RG::kNB - 1;
-    ring_step<TR, RT>(
+    ring_step<TR, RT, kTree>(
         ring + ((j + RG::kNB - 1) % RG::kNB) * RG::kChunk, ring + (j % RG::kNB) * RG::kChunk,
         [&](char* slot) { issue(nx, slot); }, next < i1,
         [&] { nx = page_ids(bt_row, min(next + 1, i1 - 1), n_seq); }, active, st, getq, c * kChunkKeys, p_row,
-        min_p, n_seq, A.scale_log2, lane);
+        tm, mask_from, n_seq, A.scale_log2, lane);
   }
   wait_all_loads();  // nothing of this unit left in flight
   lds_barrier();                        // every wave is done with the ring before it is reused
@@ -1120,8 +1165,9 @@ __device__ void merge_unit(const float* part_o, const float* part_lse, void* out
       const int tk = rr / group;
       const int head = U.kv_head * group + (rr - tk * group);
       const int64_t orow = int64_t(q0 + tk) * num_q_heads + head;
-      TR::store_out(static_cast<char*>(out) + (orow * TR::D + 4 * d4) * TR::kEb, O[i] * (1.f / L[i]));
-      if (d4 == 0) lse[orow] = M[i] + fast_log2(L[i]) * kLn2;
+      // a row that saw no key at all (possible under a tree mask) gets out = 0, lse = -inf
+      TR::store_out(static_cast<char*>(out) + (orow * TR::D + 4 * d4) * TR::kEb, O[i] * (L[i] > 0.f ? 1.f / L[i] : 0.f));
+      if (d4 == 0) lse[orow] = L[i] > 0.f ? M[i] + fast_log2(L[i]) * kLn2 : -INFINITY;
     }
   }
 }
@@ -1160,7 +1206,7 @@ __device__ void arrive_and_merge(const AttnArgs& A, const pa_plan_unit& U, int64
 // One grain: the chunks whose start cost lies in [st.c0, st.c1), unit by unit.  kFused: the
 // single-launch kernel (S grains over total cost C; split units are merged here), else the staged
 // kernel (split units are left as partial results for the merge kernel).
-template <class TR, bool kFused>
+template <class TR, bool kFused, bool kTree>
 __device__ void run_grain(const AttnArgs& A, int grain, const SlotStart& st, int64_t S, int64_t C, Smem<TR>& sm,
                           int* flag) {
   const PlanView& v = A.plan;
@@ -1183,10 +1229,10 @@ __device__ void run_grain(const AttnArgs& A, int grain, const SlotStart& st, int
       // and the one it ends inside (position 1)
       const int part = (i0 > 0 || i1 < U.n_chunks) ? 2 * grain + (cs < c0 ? 0 : 1) : -1;
       if (U.kind == 0) {
-        if (U.n_rows <= 16) run_keysplit<TR, 1>(A, U, i0, i1, part, sm);
-        else run_keysplit<TR, 2>(A, U, i0, i1, part, sm);
+        if (U.n_rows <= 16) run_keysplit<TR, 1, kTree>(A, U, i0, i1, part, sm);
+        else run_keysplit<TR, 2, kTree>(A, U, i0, i1, part, sm);
       } else {
-        run_rowsplit<TR>(A, U, i0, i1, part, sm);
+        run_rowsplit<TR, kTree>(A, U, i0, i1, part, sm);
       }
       if constexpr (kFused) {
         if (part >= 0) arrive_and_merge<TR>(A, U, S, C, flag);
@@ -1201,7 +1247,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs A) {
   __shared__ Smem<TR> sm;
   const int64_t S = ro(A.plan.hdr)->n_slots;
   for (int64_t g = blockIdx.x; g < S; g += gridDim.x)
-    run_grain<TR, false>(A, int(g), load_slot(ro(A.plan.slots) + g), 0, 0, sm, nullptr);
+    run_grain<TR, false, false>(A, int(g), load_slot(ro(A.plan.slots) + g), 0, 0, sm, nullptr);
 }
 
 // Sums and scans of one int64 per thread over the kThreads threads of a workgroup.
@@ -1272,7 +1318,7 @@ __device__ __forceinline__ int64_t block_seq_costs(const PlanView& v, cptr<int32
 // seq_lens and query_start_loc (the same numbers the staged planner writes), finds where its grain
 // starts with a workgroup-wide scan of the per-sequence costs, then runs the grain and merges the
 // split units it completes.
-template <class TR>
+template <class TR, bool kTree>
 __global__ __launch_bounds__(kThreads, 2) void attention_fused_kernel(AttnArgs A) {
   __shared__ Smem<TR> sm;
   __shared__ PreLds pl;
@@ -1321,7 +1367,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fused_kernel(AttnArgs A
   }
   __syncthreads();
   const SlotStart st = pl.st;
-  run_grain<TR, true>(A, int(k), st, S, C, sm, &pl.flag);
+  run_grain<TR, true, kTree>(A, int(k), st, S, C, sm, &pl.flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -1632,7 +1678,10 @@ int launch_attention(const AttnArgs& a, int dtype, int D, int grid, void* stream
 
 template <class TR>
 static int launch_fused_t(const AttnArgs& a, int grid, void* stream) {
-  hipLaunchKernelGGL(attention_fused_kernel<TR>, dim3(grid), dim3(kThreads), 0, as_stream(stream), a);
+  if (a.tree_mask)
+    hipLaunchKernelGGL((attention_fused_kernel<TR, true>), dim3(grid), dim3(kThreads), 0, as_stream(stream), a);
+  else
+    hipLaunchKernelGGL((attention_fused_kernel<TR, false>), dim3(grid), dim3(kThreads), 0, as_stream(stream), a);
   return int(hipGetLastError());
 }
 
@@ -1641,19 +1690,24 @@ int launch_attention_fused(const AttnArgs& a, int dtype, int D, int grid, void* 
   return D == 128 ? launch_fused_t<F32<128>>(a, grid, stream) : launch_fused_t<F32<64>>(a, grid, stream);
 }
 
-// The staged and the single-launch kernel run on the same grid (the smaller occupancy of the
-// two), so both cut the batch into the same grains and give bitwise identical results.
+// The staged and the single-launch kernels (with and without tree masks) run on the same grid (the
+// smallest occupancy), so all cut the batch into the same grains and the staged and single-launch
+// paths give bitwise identical results.
 template <class TR>
 static int blocks_per_cu_t() {
-  int n = 0, m = 0;
+  int n = 0, m = 0, t = 0;
   void (*staged)(AttnArgs) = attention_kernel<TR>;
-  void (*fused)(AttnArgs) = attention_fused_kernel<TR>;
+  void (*fused)(AttnArgs) = attention_fused_kernel<TR, false>;
+  void (*tree)(AttnArgs) = attention_fused_kernel<TR, true>;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(staged), kThreads, 0) !=
           hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, reinterpret_cast<const void*>(fused), kThreads, 0) !=
+          hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&t, reinterpret_cast<const void*>(tree), kThreads, 0) !=
           hipSuccess)
     return -1;
-  return n < m ? n : m;
+  n = n < m ? n : m;
+  return n < t ? n : t;
 }
 
 __global__ void fill_zero_kernel(uint32_t* p, int64_t words) {

@@ -116,7 +116,8 @@ MUTATIONS = [
     ("append reads the wrong head", "const int64_t src = (r * Hkv + g) * D + d;",
      "const int64_t src = (r * Hkv + (Hkv - 1 - g)) * D + d;"),
     ("tree bit index off by one", "return (int)((mask >> (j - win0)) & 1u);", "return (int)((mask >> (j - win0 + 1)) & 1u);"),
-    ("tree window starts one late", "const int win0 = n - qn;\n    const int32_t* bt", "const int win0 = n - qn + 1;\n    const int32_t* bt"),
+    ("tree shows the first window token as context", "if (j < win0 || qn > 64) return 1;",
+     "if (j <= win0 || qn > 64) return 1;"),
     ("tree always shows the row itself", "return (int)((mask >> (j - win0)) & 1u);",
      "return j == p ? 1 : (int)((mask >> (j - win0)) & 1u);"),
     ("tree masks applied to long windows", "if (j < win0 || qn > 64) return 1;", "if (j < win0) return 1;"),
