@@ -57,6 +57,11 @@ def open_library(path: str):
     lib.oracle_attention_tree.argtypes = [ip, ip, ip, ip, ip, ip, ip, vp, vp, vp, vp, vp, vp, vp,
                                           ctypes.c_double, vp, vp]
     lib.oracle_attention_tree.restype = ip
+    lib.oracle_fp8_decode.argtypes = [ip]
+    lib.oracle_fp8_decode.restype = ctypes.c_double
+    lib.oracle_attention_fp8.argtypes = [ip, ip, ip, ip, ip, ip, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         ctypes.c_double, vp, vp, ip]
+    lib.oracle_attention_fp8.restype = ip
     lib.oracle_max_threads.restype = ip
     return lib
 
@@ -201,4 +206,34 @@ def attention_tree(q, k_pool, v_pool, block_table, seq_lens, query_start_loc, tr
     lse = np.zeros((T, Hq), dtype=np.float64)
     _check(lib.oracle_attention_tree(B, Hq, Hkv, D, dt, NP, bt.shape[1], _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                      _ptr(bt), _ptr(sl), _ptr(qsl), _ptr(tm), float(scale), _ptr(out), _ptr(lse)))
+    return out, lse
+
+
+def fp8_decode(code: int, lib=None) -> float:
+    """Value of one OCP FP8 E4M3 code (0..255)."""
+    return float(_load(lib).oracle_fp8_decode(int(code)))
+
+
+def attention_fp8(q, k_codes, v_codes, k_scale, v_scale, block_table, seq_lens, query_start_loc, scale: float,
+                  threads: int = 0, lib=None):
+    """fp64 attention over FP8 E4M3 pages with per-(page, kv head) scales.
+    q: [T_q][Hq][D] bf16 bits; k_codes [NP][Hkv][16][D], v_codes [NP][Hkv][D][16] uint8;
+    k_scale, v_scale [NP][Hkv] float32."""
+    lib = _load(lib)
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    kc = np.ascontiguousarray(k_codes, dtype=np.uint8)
+    vc = np.ascontiguousarray(v_codes, dtype=np.uint8)
+    ks = np.ascontiguousarray(k_scale, dtype=np.float32)
+    vs = np.ascontiguousarray(v_scale, dtype=np.float32)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    qsl = np.ascontiguousarray(query_start_loc, dtype=np.int32)
+    T, Hq, D = q.shape
+    NP, Hkv = kc.shape[0], kc.shape[1]
+    assert kc.shape == (NP, Hkv, 16, D) and vc.shape == (NP, Hkv, D, 16) and ks.shape == vs.shape == (NP, Hkv)
+    B = sl.shape[0]
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    lse = np.zeros((T, Hq), dtype=np.float64)
+    _check(lib.oracle_attention_fp8(B, Hq, Hkv, D, NP, bt.shape[1], _ptr(q), _ptr(kc), _ptr(vc), _ptr(ks), _ptr(vs),
+                                    _ptr(bt), _ptr(sl), _ptr(qsl), float(scale), _ptr(out), _ptr(lse), int(threads)))
     return out, lse

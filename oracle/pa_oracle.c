@@ -246,6 +246,98 @@ int oracle_attention_tree(int B, int Hq, int Hkv, int D, int dtype, int num_page
 }
 
 /*
+ * FP8 KV pages (the Arctic review lists quantized KV caches among the
+ * serving optimizations; OCP FP8 E4M3 is the MI355X's native 8-bit float).
+ * A code is decoded from the E4M3 definition: 1 sign bit, 4 exponent bits
+ * (bias 7), 3 mantissa bits; exponent 0 is subnormal (m/8 * 2^-6); the code
+ * with all exponent and mantissa bits set is NaN; there is no infinity.
+ */
+double oracle_fp8_decode(int code) {
+  const int sgn = (code >> 7) & 1, ex = (code >> 3) & 15, man = code & 7;
+  if (ex == 15 && man == 7) return NAN;
+  const double mag = ex == 0 ? ldexp(man / 8.0, -6) : ldexp(1.0 + man / 8.0, ex - 7);
+  return sgn ? -mag : mag;
+}
+
+/*
+ * Attention over FP8 pages: q is bf16; k_codes / v_codes hold E4M3 codes in
+ * the pool layouts above; k_scale / v_scale [NP][Hkv] fp32 hold one scale per
+ * (page, kv head).  Key j of sequence s is k = decode(code) * k_scale[pg][g],
+ * and V likewise; then exactly the computation of oracle_attention.
+ */
+int oracle_attention_fp8(int B, int Hq, int Hkv, int D, int num_pages, int max_pages, const uint16_t* q,
+                         const uint8_t* k_codes, const uint8_t* v_codes, const float* k_scale, const float* v_scale,
+                         const int32_t* block_table, const int32_t* seq_lens, const int32_t* qsl, double scale,
+                         double* out, double* lse, int nthreads) {
+  int rc = check_batch(B, Hq, Hkv, D, num_pages, max_pages, block_table, seq_lens, qsl);
+  if (rc != ORACLE_OK) return rc;
+  const int G = Hq / Hkv;
+  const int64_t T = B > 0 ? qsl[B] : 0;
+  int max_n = 0;
+  for (int s = 0; s < B; ++s) max_n = seq_lens[s] > max_n ? seq_lens[s] : max_n;
+  double table[256];
+  for (int c = 0; c < 256; ++c) table[c] = oracle_fp8_decode(c);
+  int32_t* row_seq = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+  if (!row_seq) return ORACLE_NO_MEMORY;
+  for (int s = 0; s < B; ++s)
+    for (int32_t r = qsl[s]; r < qsl[s + 1]; ++r) row_seq[r] = s;
+  int failed = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel
+  {
+    double* sc = (double*)malloc(sizeof(double) * (size_t)(max_n > 0 ? max_n : 1));
+    double* num = (double*)malloc(sizeof(double) * (size_t)D);
+    if (!sc || !num) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t rh = 0; rh < T * Hq; ++rh) {
+      if (!sc || !num) continue;
+      const int64_t r = rh / Hq;
+      const int h = (int)(rh % Hq);
+      const int s = row_seq[r];
+      const int kvh = h / G;
+      const int n = seq_lens[s];
+      const int last = n - (qsl[s + 1] - qsl[s]) + (int)(r - qsl[s]);
+      const int32_t* bt = block_table + (int64_t)s * max_pages;
+      const int64_t qrow = (r * Hq + h) * (int64_t)D;
+      double mx = -INFINITY;
+      for (int j = 0; j <= last; ++j) {
+        const int64_t page = bt[j / ORACLE_PAGE];
+        const int slot = j % ORACLE_PAGE;
+        const double ks = (double)k_scale[page * Hkv + kvh];
+        double qk = 0.0;
+        for (int d = 0; d < D; ++d)
+          qk += widen(q, ORACLE_BF16, qrow + d) * (table[k_codes[k_offset(page, kvh, slot, d, Hkv, D)]] * ks);
+        sc[j] = qk * scale;
+        mx = sc[j] > mx ? sc[j] : mx;
+      }
+      double den = 0.0;
+      for (int d = 0; d < D; ++d) num[d] = 0.0;
+      for (int j = 0; j <= last; ++j) {
+        const int64_t page = bt[j / ORACLE_PAGE];
+        const int slot = j % ORACLE_PAGE;
+        const double vs = (double)v_scale[page * Hkv + kvh];
+        const double wj = exp(sc[j] - mx);
+        den += wj;
+        for (int d = 0; d < D; ++d) num[d] += wj * (table[v_codes[v_offset(page, kvh, slot, d, Hkv, D)]] * vs);
+      }
+      for (int d = 0; d < D; ++d) out[qrow + d] = num[d] / den;
+      lse[r * Hq + h] = mx + log(den);
+    }
+    free(sc);
+    free(num);
+  }
+  free(row_seq);
+  return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/*
  * Gather sequence `seq`'s rows of one pool into dense [Hkv][n][D] order by
  * walking its block table (element bytes copied unchanged).
  * which = 0: K pool layout [NP][Hkv][16][D]; which = 1: V pool layout [NP][Hkv][D][16].

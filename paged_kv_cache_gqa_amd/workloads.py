@@ -83,21 +83,29 @@ class Workload:
 
     @property
     def elem_bytes(self) -> int:
-        return 2 if self.dtype == "bf16" else 4
+        """Bytes of one Q / output element (bf16 for FP8-KV batches)."""
+        return 2 if self.dtype in ("bf16", "fp8") else 4
+
+    @property
+    def kv_elem_bytes(self) -> int:
+        """Bytes of one K / V pool element."""
+        return 1 if self.dtype == "fp8" else self.elem_bytes
 
     def q_lens(self) -> np.ndarray:
         return np.diff(self.query_start_loc).astype(np.int64)
 
     def algorithmic_bytes(self) -> int:
         """Bytes the path must move at least once: every valid K and V row once per
-        KV head, Q in, output out, LSE out, and the block-table entries used."""
+        KV head, Q in, output out, LSE out, and the block-table entries used (FP8 pages: also
+        the K and V scale of every used (page, kv head))."""
         n = self.seq_lens.astype(np.int64)
         eb = self.elem_bytes
         hkv, hq, d = self.num_kv_heads, self.num_q_heads, self.head_dim
         tq = self.num_q_tokens
-        kv = int(n.sum()) * hkv * d * eb * 2
+        kv = int(n.sum()) * hkv * d * self.kv_elem_bytes * 2
         pages = int(((n + PAGE_SIZE - 1) // PAGE_SIZE).sum())
-        return kv + 2 * tq * hq * d * eb + 4 * tq * hq + 4 * pages
+        scales = 2 * 4 * pages * hkv if self.dtype == "fp8" else 0
+        return kv + 2 * tq * hq * d * eb + 4 * tq * hq + 4 * pages + scales
 
     def algorithmic_flops(self) -> int:
         """4*D flops (QK^T and PV) per (query row, query head, visible key)."""
@@ -309,3 +317,38 @@ def random_trees(q_lens, seed: int):
                 k = par[k]
             masks.append(m)
     return np.array(masks, dtype=np.uint64), parents
+
+
+FP8_MAX = 448.0  # largest finite OCP FP8 E4M3 value
+
+
+def _quantize_pool(pool: np.ndarray, chunk_pages: int = 4096):
+    """Per-(page, kv head) FP8 E4M3 codes and scales of a pool [NP][Hkv][...]: scale = amax / 448
+    over the block (1 for an all-zero block), code = E4M3 rounding of x / scale (torch's
+    float8_e4m3fn conversion: round to nearest, ties to even)."""
+    import torch
+    NP, Hkv = pool.shape[:2]
+    codes = np.empty(pool.shape, dtype=np.uint8)
+    scales = np.empty((NP, Hkv), dtype=np.float32)
+    for p0 in range(0, NP, chunk_pages):
+        p1 = min(NP, p0 + chunk_pages)
+        x = pool[p0:p1]
+        x = bf16_bits_to_f32(x) if x.dtype == np.uint16 else x.astype(np.float32)
+        amax = np.abs(x).reshape(p1 - p0, Hkv, -1).max(axis=2)
+        sc = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
+        y = x / sc.reshape(p1 - p0, Hkv, *([1] * (x.ndim - 2)))
+        codes[p0:p1] = torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        scales[p0:p1] = sc
+    return codes, scales
+
+
+def to_fp8(w: Workload) -> Workload:
+    """The same batch with FP8 E4M3 K/V pages (per-(page, kv head) scales in meta["k_scale"] and
+    meta["v_scale"]) and bf16 queries."""
+    kc, ks = _quantize_pool(w.k_pool)
+    vc, vs = _quantize_pool(w.v_pool)
+    q = w.q if w.q.dtype == np.uint16 else f32_to_bf16_bits(w.q)
+    meta = dict(w.meta, k_scale=ks, v_scale=vs)
+    return Workload(name=w.name + "-fp8kv", dtype="fp8", num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                    head_dim=w.head_dim, scale=w.scale, seq_lens=w.seq_lens, query_start_loc=w.query_start_loc,
+                    block_table=w.block_table, q=q, k_pool=kc, v_pool=vc, meta=meta)

@@ -467,5 +467,60 @@ def pin_tree(lib=None):
     assert np.all(o[1] == 0.0) and np.all(np.isneginf(l[1])) and np.all(np.isfinite(l[[0, 2]]))
 
 
+def _fp8_values(codes):
+    """float64 values of E4M3 codes by torch's float8_e4m3fn (a library decode, not the oracle's)."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def pin_fp8(lib=None):
+    """FP8 E4M3 pages.  (1) the oracle's decode of all 256 codes equals torch's float8_e4m3fn
+    (NaN codes included); (2) with power-of-two scales the dequantized pools are exact in float32
+    and attention over the FP8 pages equals the (pinned) float32 attention over them; (3) with
+    arbitrary scales it equals fp64 torch SDPA over K/V dequantized by torch and gathered by a
+    Python page walk."""
+    import torch
+    dec = np.array([oracle.fp8_decode(c, lib=lib) for c in range(256)])
+    ref = _fp8_values(np.arange(256))
+    assert np.array_equal(np.isnan(dec), np.isnan(ref)) and np.array_equal(dec[~np.isnan(dec)], ref[~np.isnan(ref)])
+    for seed, (B, maxlen, Hq, Hkv, D, maxq) in enumerate([(4, 150, 8, 2, 64, 5), (3, 90, 4, 1, 64, 30),
+                                                          (3, 70, 8, 8, 128, 1)]):
+        w8 = W.to_fp8(W.make_random(700 + seed, B, maxlen, Hq, Hkv, D, "bf16", max_q=maxq))
+        ks, vs = w8.meta["k_scale"], w8.meta["v_scale"]
+        p2 = lambda x: np.exp2(np.round(np.log2(x))).astype(np.float32)  # noqa: E731
+        ks2, vs2 = p2(ks), p2(vs)
+        args = (w8.block_table, w8.seq_lens, w8.query_start_loc, w8.scale)
+        o8, l8 = oracle.attention_fp8(w8.q, w8.k_pool, w8.v_pool, ks2, vs2, *args, lib=lib)
+        kf = (_fp8_values(w8.k_pool) * ks2[:, :, None, None]).astype(np.float32)
+        vf = (_fp8_values(w8.v_pool) * vs2[:, :, None, None]).astype(np.float32)
+        assert np.array_equal(kf[np.isfinite(kf)].astype(np.float64),
+                              (_fp8_values(w8.k_pool) * ks2[:, :, None, None])[np.isfinite(kf)])  # exact in f32
+        qf = W.bf16_bits_to_f32(w8.q)
+        o32, l32 = oracle.attention(qf, kf, vf, *args, lib=lib)
+        assert np.max(np.abs(o8 - o32)) <= 1e-13 and np.max(np.abs(l8 - l32)) <= 1e-13, seed
+        o8, l8 = oracle.attention_fp8(w8.q, w8.k_pool, w8.v_pool, ks, vs, *args, lib=lib)
+        K64 = _fp8_values(w8.k_pool) * ks.astype(np.float64)[:, :, None, None]
+        V64 = _fp8_values(w8.v_pool) * vs.astype(np.float64)[:, :, None, None]
+        G = Hq // Hkv
+        q = torch.from_numpy(qf.astype(np.float64))
+        for s in range(w8.num_seqs):
+            n = int(w8.seq_lens[s])
+            q0, q1 = int(w8.query_start_loc[s]), int(w8.query_start_loc[s + 1])
+            if q1 == q0:
+                continue
+            win = q1 - q0
+            pages = w8.block_table[s, np.arange(n) // PS]
+            slots = np.arange(n) % PS
+            K = K64[pages, :, slots, :].transpose(1, 0, 2)  # [Hkv][n][D]
+            V = V64[pages, :, :, slots].transpose(1, 0, 2)
+            Kt = torch.from_numpy(np.ascontiguousarray(K)).repeat_interleave(G, dim=0)
+            Vt = torch.from_numpy(np.ascontiguousarray(V)).repeat_interleave(G, dim=0)
+            Q = q[q0:q1].transpose(0, 1).contiguous()
+            mask = torch.arange(n)[None, :] <= (n - win + torch.arange(win))[:, None]
+            ref = torch.nn.functional.scaled_dot_product_attention(Q[None], Kt[None], Vt[None],
+                                                                   attn_mask=mask[None, None], scale=w8.scale)[0]
+            assert np.max(np.abs(o8[q0:q1] - ref.transpose(0, 1).numpy())) <= 1e-12, (seed, s)
+
+
 ALL_PINS = [pin_brute_force, pin_golden, pin_closed_forms, pin_invariants, pin_merge_of_splits,
-            pin_sdpa, pin_gather, pin_append, pin_tree]
+            pin_sdpa, pin_gather, pin_append, pin_tree, pin_fp8]

@@ -45,6 +45,10 @@ def test_oracle_tree_masks():
     P.pin_tree()
 
 
+def test_oracle_fp8_pages():
+    P.pin_fp8()
+
+
 def test_oracle_gather_page_walk():
     P.pin_gather()
 
@@ -121,6 +125,12 @@ MUTATIONS = [
     ("tree always shows the row itself", "return (int)((mask >> (j - win0)) & 1u);",
      "return j == p ? 1 : (int)((mask >> (j - win0)) & 1u);"),
     ("tree masks applied to long windows", "if (j < win0 || qn > 64) return 1;", "if (j < win0) return 1;"),
+    ("fp8 exponent bias off by one", "ldexp(1.0 + man / 8.0, ex - 7)", "ldexp(1.0 + man / 8.0, ex - 8)"),
+    ("fp8 subnormals one binade low", "ldexp(man / 8.0, -6)", "ldexp(man / 8.0, -7)"),
+    ("fp8 K scale of the wrong head", "const double ks = (double)k_scale[page * Hkv + kvh];",
+     "const double ks = (double)k_scale[page * Hkv + (Hkv - 1 - kvh)];"),
+    ("fp8 V scaled by the K scale", "const double vs = (double)v_scale[page * Hkv + kvh];",
+     "const double vs = (double)k_scale[page * Hkv + kvh];"),
     ("page lookup off by one page", "const int64_t pg = bt[j / ORACLE_PAGE];\n        const int t = j % ORACLE_PAGE;\n        double",
      "const int64_t pg = bt[(j / ORACLE_PAGE + 1) % ((n + 15) / 16)];\n        const int t = j % ORACLE_PAGE;\n        double"),
 ]
