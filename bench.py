@@ -202,10 +202,11 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--part", default="all", choices=["all", "prefill", "decode"],
                     help="configuration 3 only: time its prefill chunks or its decode rows alone")
-    ap.add_argument("--op", default="attention", choices=["attention", "append", "tree"],
+    ap.add_argument("--op", default="attention", choices=["attention", "append", "tree", "fp8"],
                     help="attention (default): the attention call; append: the paged KV append of the batch's new "
                          "tokens (pa_append_kv); tree: attention with each window a random draft-token tree "
-                         "(pa_attention_tree)")
+                         "(pa_attention_tree); fp8: attention over the batch's K/V quantized to FP8 E4M3 pages with "
+                         "per-(page, kv head) scales (pa_attention_fp8kv)")
     ap.add_argument("--staged", action="store_true",
                     help="time pa_plan + pa_attention_planned + pa_merge_planned instead of the single launch")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
@@ -247,6 +248,8 @@ def main() -> int:
         w.name = f"{W.CONFIG_NAMES[args.config]}-{args.part}-part"
     if args.op == "append":
         return bench_append(args, w)
+    if args.op == "fp8":
+        w = W.to_fp8(w)
     alg_bytes = w.algorithmic_bytes()
     alg_flops = w.algorithmic_flops()
     t = pa.to_device(w)
@@ -271,11 +274,13 @@ def main() -> int:
     if tree:
         masks, _ = W.random_trees(w.q_lens(), 1000 + args.config)
         tm = torch.from_numpy(masks.view(np.int64)).cuda()
+    fp8 = args.op == "fp8"
     mask_arg = (vp(tm.data_ptr()),) if tree else ()
-    attn_args = [(dref, vp(t["q"].data_ptr()), vp(k.data_ptr()), vp(v.data_ptr()), vp(t["block_table"].data_ptr()),
-                  vp(t["seq_lens"].data_ptr()), vp(t["query_start_loc"].data_ptr()), *mask_arg, vp(out.data_ptr()),
-                  vp(lse.data_ptr()), vp(ws.data_ptr()), wsn, sp) for k, v in pools]
-    attention_call = L.pa_attention_tree if tree else L.pa_attention
+    scale_args = (vp(t["k_scale"].data_ptr()), vp(t["v_scale"].data_ptr())) if fp8 else ()
+    attn_args = [(dref, vp(t["q"].data_ptr()), vp(k.data_ptr()), vp(v.data_ptr()), *scale_args,
+                  vp(t["block_table"].data_ptr()), vp(t["seq_lens"].data_ptr()), vp(t["query_start_loc"].data_ptr()),
+                  *mask_arg, vp(out.data_ptr()), vp(lse.data_ptr()), vp(ws.data_ptr()), wsn, sp) for k, v in pools]
+    attention_call = L.pa_attention_tree if tree else L.pa_attention_fp8kv if fp8 else L.pa_attention
     merge_args = (dref, vp(t["seq_lens"].data_ptr()), vp(t["query_start_loc"].data_ptr()), vp(out.data_ptr()),
                   vp(lse.data_ptr()), vp(ws.data_ptr()), wsn, sp)
 
@@ -327,19 +332,21 @@ def main() -> int:
     value = alg_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (attn_mean * 1e-3) / 1e9
     tflops = alg_flops / (ms_per_step * 1e-3) / 1e12
-    peak_tf = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+    compute_dtype = "bf16" if w.dtype in ("bf16", "fp8") else w.dtype  # FP8 pages run through bf16 MFMAs
+    peak_tf = BF16_PEAK_TFLOPS if compute_dtype == "bf16" else FP32_PEAK_TFLOPS
     kernel = "attention_kernel" if args.staged else "attention_fused_kernel"
-    if tree and args.staged:
-        raise SystemExit("--op tree runs the single launch only")
+    if (tree or fp8) and args.staged:
+        raise SystemExit("--op tree / fp8 run the single launch only")
     config = {"workload": f"{w.name} (configuration {args.config})", **DESCRIPTIONS[args.config],
               "part": args.part, "path": "staged (3 launches)" if args.staged else "single launch",
               "windows": "random draft-token trees (per-row ancestor masks)" if tree else "causal",
+              "kv_pages": "FP8 E4M3, per-(page, kv head) fp32 scales" if fp8 else w.dtype,
               "page_size": 16, "seed": 1000 + args.config, "kv_pool_copies": n_copies,
               "algorithmic_bytes": alg_bytes, "algorithmic_flops": alg_flops}
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded; shapes of the named configuration)",
+        "vs_baseline": None, "dtype": compute_dtype, "data": "synthetic (seeded; shapes of the named configuration)",
         "config": config,
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "tflops": round(tflops, 3), "frac_of_mfma_peak": round(tflops / peak_tf, 5),

@@ -142,6 +142,25 @@ pa_status pa_attention(const pa_desc* desc, const void* q, const void* k_pool, c
                        size_t workspace_bytes, void* stream);
 
 /*
+ * pa_attention over FP8 KV pages (a quantized KV cache, as listed among the
+ * serving optimizations in the "Arctic Inference with Shift Parallelism"
+ * review; MI355X decodes OCP FP8 natively).  k_pool / v_pool hold OCP FP8 E4M3
+ * codes, one byte per element, in the layouts above; k_scale / v_scale
+ * [NP][Hkv] float32 (device memory) hold one scale per (page, kv head): key j
+ * of sequence s is E4M3(k_pool[pg][g][t][:]) * k_scale[pg][g], and V likewise.
+ * q and out are bf16 (desc->dtype must be PA_BF16, else PA_ERR_UNSUPPORTED);
+ * lse as for pa_attention.  The codes are converted to bf16 exactly and go
+ * through the bf16 MFMAs; the K scale multiplies a page's scores and the V
+ * scale its softmax weights before those are rounded to bf16.  Same single
+ * launch, workspace (sized by pa_workspace_size for the bf16 descriptor) and
+ * errors as pa_attention.
+ */
+pa_status pa_attention_fp8kv(const pa_desc* desc, const void* q, const uint8_t* k_pool, const uint8_t* v_pool,
+                             const float* k_scale, const float* v_scale, const int32_t* block_table,
+                             const int32_t* seq_lens, const int32_t* query_start_loc, void* out, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_attention for batches whose verify windows are draft-token trees
  * (speculative decoding with a token tree: XY-Serve verdict page,
  * referee_report "significance" and the desk-editor letter on verifying token

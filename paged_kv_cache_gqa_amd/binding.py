@@ -81,8 +81,10 @@ def lib():
         L.pa_validate.argtypes = [dp, vp, vp, vp, vp, sz, vp]
         L.pa_append_kv.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.pa_attention_tree.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.pa_attention_fp8kv.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for name in ("pa_check_desc", "pa_workspace_size", "pa_workspace_init", "pa_attention", "pa_plan", "pa_attention_planned",
-                     "pa_merge_planned", "pa_plan_read", "pa_gather_kv", "pa_merge", "pa_validate", "pa_append_kv", "pa_attention_tree"):
+                     "pa_merge_planned", "pa_plan_read", "pa_gather_kv", "pa_merge", "pa_validate", "pa_append_kv", "pa_attention_tree",
+                     "pa_attention_fp8kv"):
             getattr(L, name).restype = ctypes.c_int
         if L.pa_abi_version() != 1:
             raise PagedAttentionError("load", -1, "ABI version mismatch")
@@ -207,6 +209,36 @@ def attention_tree(q, k_pool, v_pool, block_table, seq_lens, query_start_loc, tr
     return out, lse
 
 
+def attention_fp8kv(q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens, query_start_loc, scale: float,
+                    out=None, lse=None, workspace=None, stream=None):
+    """pa_attention_fp8kv: K/V pools of FP8 E4M3 codes (uint8) with [NP][Hkv] float32 scales; q and out bf16.
+    Returns (out, lse)."""
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("k_scale", k_scale), ("v_scale", v_scale),
+                    ("block_table", block_table), ("seq_lens", seq_lens), ("query_start_loc", query_start_loc)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if q.dtype != torch.bfloat16 or k_pool.dtype != torch.uint8 or v_pool.dtype != torch.uint8:
+        raise TypeError("q must be bf16 and the pools uint8 FP8 E4M3 codes")
+    if k_scale.dtype != torch.float32 or k_scale.shape != k_pool.shape[:2] or v_scale.shape != k_scale.shape:
+        raise ValueError("k_scale / v_scale must be float32 [NP][Hkv]")
+    T, Hq, D = q.shape
+    NP, Hkv = k_pool.shape[:2]
+    desc = PaDesc(num_seqs=seq_lens.shape[0], num_q_tokens=T, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                  page_size=PAGE_SIZE, num_pages=NP, max_pages_per_seq=block_table.shape[1], dtype=PA_BF16,
+                  scale=float(scale))
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(desc, q.device)
+    _check("pa_attention_fp8kv",
+           lib().pa_attention_fp8kv(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
+                                    _ptr(v_scale), _ptr(block_table), _ptr(seq_lens), _ptr(query_start_loc),
+                                    _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, lse
+
+
 def plan(desc: PaDesc, seq_lens, query_start_loc, workspace, stream=None) -> None:
     _check("pa_plan", lib().pa_plan(ctypes.byref(desc), _ptr(seq_lens), _ptr(query_start_loc), _ptr(workspace),
                                     workspace.numel(), _stream(stream)))
@@ -293,7 +325,10 @@ def to_device(w, device="cuda"):
             return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
-    return {"q": arr(w.q), "k_pool": arr(w.k_pool), "v_pool": arr(w.v_pool),
+    extra = {}
+    if "k_scale" in w.meta:  # FP8 pages
+        extra = {"k_scale": arr(w.meta["k_scale"]), "v_scale": arr(w.meta["v_scale"])}
+    return {**extra, "q": arr(w.q), "k_pool": arr(w.k_pool), "v_pool": arr(w.v_pool),
             "block_table": torch.from_numpy(np.ascontiguousarray(w.block_table, dtype=np.int32)).to(device),
             "seq_lens": torch.from_numpy(np.ascontiguousarray(w.seq_lens, dtype=np.int32)).to(device),
             "query_start_loc": torch.from_numpy(np.ascontiguousarray(w.query_start_loc, dtype=np.int32)).to(device)}

@@ -121,6 +121,8 @@ pa::AttnArgs attn_args(const pa_desc& d, const void* q, const void* k, const voi
   a.part_o = ws.part_o;
   a.part_lse = ws.part_lse;
   a.tree_mask = nullptr;
+  a.k_scale = nullptr;
+  a.v_scale = nullptr;
   a.arrive = ws.arrive;
   a.num_q_heads = d.num_q_heads;
   a.max_pages = d.max_pages_per_seq;
@@ -253,6 +255,28 @@ pa_status pa_attention(const pa_desc* desc, const void* q, const void* k_pool, c
                        void* workspace, size_t workspace_bytes, void* stream) {
   return single_launch(desc, q, k_pool, v_pool, block_table, seq_lens, qsl, nullptr, out, lse, workspace,
                        workspace_bytes, stream);
+}
+
+pa_status pa_attention_fp8kv(const pa_desc* desc, const void* q, const uint8_t* k_pool, const uint8_t* v_pool,
+                             const float* k_scale, const float* v_scale, const int32_t* block_table,
+                             const int32_t* seq_lens, const int32_t* qsl, void* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!desc) return PA_ERR_NULL_POINTER;
+  const pa_status st = pa_check_desc(desc);
+  if (st != PA_OK) return st;
+  if (desc->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;  // q and out are bf16
+  if (desc->num_q_tokens == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !k_scale || !v_scale || !block_table || !seq_lens || !qsl || !out || !lse ||
+      !workspace)
+    return PA_ERR_NULL_POINTER;
+  int grid = 0;
+  Ws ws;
+  const pa_status ps = prepare(desc, workspace, workspace_bytes, &grid, &ws);
+  if (ps != PA_OK) return ps;
+  pa::AttnArgs a = attn_args(*desc, q, k_pool, v_pool, block_table, seq_lens, qsl, out, lse, ws);
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  return pa::launch_attention_fp8kv(a, desc->head_dim, grid, stream) == 0 ? PA_OK : PA_ERR_HIP;
 }
 
 pa_status pa_attention_tree(const pa_desc* desc, const void* q, const void* k_pool, const void* v_pool,

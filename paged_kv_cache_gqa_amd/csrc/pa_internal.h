@@ -83,6 +83,8 @@ struct AttnArgs {
   float* part_o;    // [grains][2][128][D]: per grain, the piece of its first and of its last unit
   float* part_lse;  // [grains][2][128]
   const uint64_t* tree_mask;  // [T_q] per-row window masks, or null for the causal rule
+  const float* k_scale;       // [NP][Hkv] FP8 pages: scale of each (page, kv head), else null
+  const float* v_scale;
   int32_t* arrive;  // [grains]: pieces of the split unit whose first piece is in grain k that have
                     // finished (single-launch path; zero between calls)
   int32_t num_q_heads;
@@ -171,6 +173,8 @@ int launch_plan(const PlanArgs& a, void* stream);
 int launch_attention(const AttnArgs& a, int dtype, int head_dim, int grid, void* stream);
 // single launch: in-kernel planning of each grain and merge of split units by their last piece
 int launch_attention_fused(const AttnArgs& a, int dtype, int head_dim, int grid, void* stream);
+// single launch over FP8 E4M3 pages (bf16 q / out; a.k_scale, a.v_scale set)
+int launch_attention_fp8kv(const AttnArgs& a, int head_dim, int grid, void* stream);
 int launch_fill_zero(void* p, size_t bytes, void* stream);
 int launch_merge_planned(const MergeArgs& a, int dtype, int head_dim, int grid, void* stream);
 int launch_plan_units(const PlanView& v, pa_plan_unit* units, int64_t max_units, void* stream);

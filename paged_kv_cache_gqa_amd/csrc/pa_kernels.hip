@@ -136,6 +136,17 @@ __device__ __forceinline__ void lds_read4_b64(const uint32_t (&a)[4], u32x2_t& r
       : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
       : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
 }
+__device__ __forceinline__ void lds_read4_b32(const uint32_t (&a)[4], uint32_t& r0, uint32_t& r1, uint32_t& r2,
+                                              uint32_t& r3) {
+  asm volatile(
+      "ds_read_b32 %0, %4\n"
+      "ds_read_b32 %1, %5\n"
+      "ds_read_b32 %2, %6\n"
+      "ds_read_b32 %3, %7\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+}
 // 16-byte LDS write that the compiler does not order behind DMAs in flight (the data it writes
 // does not overlap any DMA target; LDS operations of one wave execute in issue order).
 __device__ __forceinline__ void lds_write_b128(uint32_t a, u32x4_t v) {
@@ -169,6 +180,9 @@ struct Bf16 {
   static constexpr int kTiles = D / 16;
   static constexpr bool kBf16 = true;
   static constexpr int kVLoads = 2 * kVF;  // global load instructions per chunk of V (two pages per tile)
+  static constexpr int kEbKV = kEb;        // bytes per K/V pool element
+  static constexpr bool kScaled = false;   // per-(page, head) K/V scales
+  using VRaw = u32x4_t;                    // a V fragment as loaded
 
   __device__ static int q_off(int f, int quad) { return (32 * f + 8 * quad) * kEb; }
   // lane offsets within a (page, head) block: K row = lane%16, d = 8*quad (+32*kk)
@@ -184,6 +198,10 @@ struct Bf16 {
     const uint2 b = ld8(v1 + vl + t * 16 * kPage * kEb);
     return u32x4_t{a.x, a.y, b.x, b.y};
   }
+  __device__ static VRaw load_v_raw(const char* v0, const char* v1, uint32_t vl, int g) {
+    return load_frag(nullptr, nullptr, v0, v1, 0u, vl, kKF + g);
+  }
+  __device__ static u32x4_t v_convert(const VRaw& r) { return r; }
   __device__ static f32x4_t qk(const u32x4_t* kf, int h, const u32x4_t* qf) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -265,6 +283,9 @@ struct F32 {
   static constexpr int kTiles = D / 16;
   static constexpr bool kBf16 = false;
   static constexpr int kVLoads = kVF;
+  static constexpr int kEbKV = kEb;
+  static constexpr bool kScaled = false;
+  using VRaw = u32x4_t;
 
   __device__ static int q_off(int f, int quad) { return (16 * f + 4 * quad) * kEb; }
   __device__ static uint32_t k_lane(int lane) { return uint32_t(((lane & 15) * D + 4 * (lane >> 4)) * kEb); }
@@ -275,6 +296,10 @@ struct F32 {
     const int g = f - kKF;
     return ld16(((g & 1) ? v1 : v0) + vl + (g >> 1) * 16 * kPage * kEb);
   }
+  __device__ static VRaw load_v_raw(const char* v0, const char* v1, uint32_t vl, int g) {
+    return load_frag(nullptr, nullptr, v0, v1, 0u, vl, kKF + g);
+  }
+  __device__ static u32x4_t v_convert(const VRaw& r) { return r; }
   __device__ static f32x4_t qk(const u32x4_t* kf, int h, const u32x4_t* qf) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -332,6 +357,96 @@ struct F32 {
   __device__ static void store_out(char* dst, f32x4_t o) { *reinterpret_cast<f32x4_t*>(dst) = o; }
 };
 
+// OCP FP8 E4M3 -> bf16, four values (exact: every E4M3 value is a bf16 value).
+__device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t x) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(int(x), false);  // bytes 0, 1
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(int(x), true);   // bytes 2, 3
+  return uint2{pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1])};
+}
+__device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(u32x2_t x) {
+  const uint2 lo = fp8x4_to_bf16x4(x[0]), hi = fp8x4_to_bf16x4(x[1]);
+  return u32x4_t{lo.x, lo.y, hi.x, hi.y};
+}
+__device__ __forceinline__ uint32_t ld4(const char* p) { return *reinterpret_cast<const uint32_t*>(p); }
+
+// FP8 KV pages: K/V pools hold OCP FP8 E4M3 codes with one fp32 scale per (page, kv head) for K
+// and for V; q and out are bf16.  Fragments are converted to bf16 (exactly) and go through the
+// bf16 MFMAs; the K scale multiplies a page's scores, the V scale its P values.
+template <int D_>
+struct Fp8Kv {
+  static constexpr int D = D_;
+  static constexpr int kEb = 2;    // q, out: bf16
+  static constexpr int kEbKV = 1;  // pools: one byte per element
+  static constexpr int kQF = D / 32;
+  static constexpr int kKF = 2 * (D / 32);
+  static constexpr int kVF = D / 16;
+  static constexpr int kNF = kKF + kVF;
+  static constexpr int kTiles = D / 16;
+  static constexpr bool kBf16 = true;
+  static constexpr int kVLoads = 2 * kVF;
+  static constexpr bool kScaled = true;
+  using VRaw = u32x2_t;  // 4 codes of page 0 (keys 4q..4q+3), 4 codes of page 1
+
+  __device__ static int q_off(int f, int quad) { return (32 * f + 8 * quad) * kEb; }
+  __device__ static uint32_t k_lane(int lane) { return uint32_t((lane & 15) * D + 8 * (lane >> 4)); }
+  __device__ static uint32_t v_lane(int lane) { return uint32_t((lane & 15) * kPage + 4 * (lane >> 4)); }
+  __device__ static VRaw load_v_raw(const char* v0, const char* v1, uint32_t vl, int t) {
+    return VRaw{ld4(v0 + vl + t * 16 * kPage), ld4(v1 + vl + t * 16 * kPage)};
+  }
+  __device__ static u32x4_t v_convert(const VRaw& r) {
+    const uint2 a = fp8x4_to_bf16x4(r[0]), b = fp8x4_to_bf16x4(r[1]);
+    return u32x4_t{a.x, a.y, b.x, b.y};
+  }
+  // K comes through LDS only (the register path is not instantiated for this trait)
+  __device__ static u32x4_t load_frag(const char*, const char*, const char*, const char*, uint32_t, uint32_t, int) {
+    return u32x4_t{0u, 0u, 0u, 0u};
+  }
+  __device__ static f32x4_t qk(const u32x4_t* kf, int h, const u32x4_t* qf) { return Bf16<D>::qk(kf, h, qf); }
+  __device__ static void sanitize_v(u32x4_t* vf, int quad, int n_valid) { Bf16<D>::sanitize_v(vf, quad, n_valid); }
+  using PFrag = typename Bf16<D>::PFrag;
+  __device__ static PFrag make_p(const float (&p)[8]) { return Bf16<D>::make_p(p); }
+  __device__ static f32x4_t pv(const u32x4_t* vf, int t, const PFrag& p, f32x4_t acc) { return Bf16<D>::pv(vf, t, p, acc); }
+  // fragments from the LDS block images of Ring<Fp8Kv<D>> (K rows of D bytes, XOR-swizzled by 16-byte
+  // column; V^T rows of 16 bytes = one column per d)
+  template <class RG>
+  __device__ static void lds_read_k(const char* slot, int lane, u32x4_t (&kf)[kKF]) {
+    const int m = lane & 15, quad = lane >> 4;
+#pragma unroll
+    for (int f0 = 0; f0 < kKF; f0 += 4) {
+      uint32_t a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int f = f0 + i, h = f / (D / 32), kk = f % (D / 32);
+        a[i] = lds_addr(slot + h * RG::kBlk + m * RG::kPitchK + RG::swz_k(m, 2 * kk + (quad >> 1)) * 16 +
+                        8 * (quad & 1));
+      }
+      u32x2_t x[4];
+      lds_read4_b64(a, x[0], x[1], x[2], x[3]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kf[f0 + i] = fp8x8_to_bf16x8(x[i]);
+    }
+  }
+  template <class RG>
+  __device__ static void lds_read_v(const char* slot, int lane, u32x4_t (&vf)[kVF]) {
+    const int m = lane & 15, quad = lane >> 4;
+#pragma unroll
+    for (int t0 = 0; t0 < kVF; t0 += 2) {
+      uint32_t a[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int d = 16 * (t0 + i) + m;
+        a[2 * i] = lds_addr(slot + 2 * RG::kBlk + d * RG::kPitchV + 4 * quad);
+        a[2 * i + 1] = lds_addr(slot + 3 * RG::kBlk + d * RG::kPitchV + 4 * quad);
+      }
+      uint32_t x0, x1, x2, x3;
+      lds_read4_b32(a, x0, x1, x2, x3);
+      vf[t0] = v_convert(VRaw{x0, x1});
+      vf[t0 + 1] = v_convert(VRaw{x2, x3});
+    }
+  }
+  __device__ static void store_out(char* dst, f32x4_t o) { Bf16<D>::store_out(dst, o); }
+};
+
 // ---------------------------------------------------------------------------
 // Per-lane online-softmax state for RT tiles of 16 query rows.
 // Lane (row n = lane%16, quad q) holds O^T[d = 16t + 4q + e][n] for every tile t.
@@ -380,7 +495,7 @@ __device__ __forceinline__ PageIds page_ids(cptr<int32_t> bt_row, int c, int n_s
 
 template <class TR>
 __device__ __forceinline__ ChunkPages pages_of(const AttnArgs& A, int kvh, PageIds p) {
-  const int64_t blk = int64_t(kPage) * TR::D * TR::kEb;  // bytes of one (page, head) block
+  const int64_t blk = int64_t(kPage) * TR::D * TR::kEbKV;  // bytes of one (page, head) block
   const int64_t hkv = A.plan.num_kv_heads;
   ChunkPages cp;
   cp.k0 = static_cast<const char*>(A.k_pool) + (int64_t(p.a) * hkv + kvh) * blk;
@@ -407,9 +522,36 @@ __device__ __forceinline__ void load_k(const ChunkPages& cp, uint32_t kl, uint32
   for (int f = 0; f < TR::kKF; ++f) kf[f] = frag<TR>(cp, kl, vl, f);
 }
 template <class TR>
-__device__ __forceinline__ void load_v(const ChunkPages& cp, uint32_t kl, uint32_t vl, u32x4_t (&vf)[TR::kVF]) {
+__device__ __forceinline__ void load_v(const ChunkPages& cp, uint32_t vl, typename TR::VRaw (&vr)[TR::kVF]) {
 #pragma unroll
-  for (int f = 0; f < TR::kVF; ++f) vf[f] = frag<TR>(cp, kl, vl, TR::kKF + f);
+  for (int f = 0; f < TR::kVF; ++f) vr[f] = TR::load_v_raw(cp.v0, cp.v1, vl, f);
+}
+
+// Per-(page, kv head) scales of one chunk (FP8 pages): lane l loads (k0, k1, v0, v1)[l & 3], the
+// K and V scales of the chunk's two pages; read_scales broadcasts them once the load has landed.
+struct ChunkScale {
+  float k0, k1, v0, v1;
+};
+template <class TR>
+__device__ __forceinline__ float load_scale_lane(const AttnArgs& A, int kvh, PageIds p, int lane) {
+  if constexpr (!TR::kScaled) {
+    return 0.f;
+  } else {
+    const int sel = lane & 3;
+    const float* base = (sel & 2) ? A.v_scale : A.k_scale;
+    return base[int64_t((sel & 1) ? p.b : p.a) * A.plan.num_kv_heads + kvh];
+  }
+}
+template <class TR>
+__device__ __forceinline__ ChunkScale read_scales(float v) {
+  ChunkScale c{1.f, 1.f, 1.f, 1.f};
+  if constexpr (TR::kScaled) {
+    c.k0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    c.k1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 1));
+    c.v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 2));
+    c.v1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 3));
+  }
+  return c;
 }
 
 // Tree-structured verify windows: per row tile, the lane's row mask (bit k: window token k
@@ -426,8 +568,8 @@ struct TreeMask {
 // the window are also masked by the rows' tree masks.
 template <class TR, int RT, bool kTree, class GetQ>
 __device__ __forceinline__ void softmax_chunk(State<TR, RT>& st, GetQ getq, const u32x4_t (&kf)[TR::kKF], int key0,
-                                              const int (&p_row)[RT], const TreeMask<RT>& tm, bool mask, float sl2,
-                                              int lane, typename TR::PFrag (&pf)[RT]) {
+                                              const int (&p_row)[RT], const TreeMask<RT>& tm, const ChunkScale& cs,
+                                              bool mask, float sl2, int lane, typename TR::PFrag (&pf)[RT]) {
   const int quad = lane >> 4;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -440,6 +582,13 @@ __device__ __forceinline__ void softmax_chunk(State<TR, RT>& st, GetQ getq, cons
     for (int e = 0; e < 4; ++e) {
       x[e] = s0[e];
       x[4 + e] = s1[e];
+    }
+    if constexpr (TR::kScaled) {  // the K scale of each page multiplies its keys' scores
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] *= cs.k0;
+        x[4 + e] *= cs.k1;
+      }
     }
     if (mask) {
       const int lim = p_row[rt] - key0;  // element j visible iff its key <= lim
@@ -479,7 +628,17 @@ __device__ __forceinline__ void softmax_chunk(State<TR, RT>& st, GetQ getq, cons
       sum += p[j];
     }
     st.l[rt] += sum;
-    pf[rt] = TR::make_p(p);
+    if constexpr (TR::kScaled) {  // the V scale of each page multiplies its P values (the sum l does not)
+      float pv[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pv[j] = p[j] * cs.v0;
+        pv[4 + j] = p[4 + j] * cs.v1;
+      }
+      pf[rt] = TR::make_p(pv);
+    } else {
+      pf[rt] = TR::make_p(p);
+    }
   }
 }
 
@@ -584,15 +743,15 @@ __device__ __forceinline__ void emit(const AttnArgs& A, const RowInfo& ri, int r
 // by row) so that the fragment reads are free of bank conflicts.
 template <class TR>
 struct Ring {
-  static constexpr int kBlk = kPage * TR::D * TR::kEb;  // bytes of one (page, head) block
+  static constexpr int kBlk = kPage * TR::D * TR::kEbKV;  // bytes of one (page, head) block
   static constexpr int kChunk = 4 * kBlk;
   static constexpr int kNB = 65536 / kChunk > 4 ? 4 : (65536 / kChunk < 2 ? 2 : 65536 / kChunk);  // ring slots
   static constexpr int kInstr = kBlk / 1024;  // DMA instructions per wave per chunk
-  static constexpr int kPitchK = TR::D * TR::kEb;  // K row (slot) pitch
+  static constexpr int kPitchK = TR::D * TR::kEbKV;  // K row (slot) pitch
   static constexpr int kNCk = kPitchK / 16;
-  static constexpr int kPitchV = kPage * TR::kEb;  // V^T row (d) pitch: 32 or 64 bytes
-  static constexpr int kNCv = kPitchV / 16;        // 2 or 4 columns
-  static constexpr int kShV = kNCv == 2 ? 3 : 2;   // rows per 256 bytes = 1 << kShV
+  static constexpr int kPitchV = kPage * TR::kEbKV;  // V^T row (d) pitch: 16, 32 or 64 bytes
+  static constexpr int kNCv = kPitchV / 16;          // 1, 2 or 4 columns
+  static constexpr int kShV = kNCv == 4 ? 2 : 3;     // rows per 256 bytes = 1 << kShV (swizzle period)
   static constexpr int kBytes = kNB * kChunk;
   // swizzled column of global column c in row r
   __device__ static int swz_k(int r, int c) { return c ^ (r & (kNCk - 1)); }
@@ -709,11 +868,14 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
   };
   const int c = i0 + w;
   u32x4_t kf[TR::kKF];
-  u32x4_t vf[TR::kVF];
-  ChunkPages cp = chunk_pages<TR>(A, bt_row, U.kv_head, c < i1 ? c : i0, n_seq);
+  typename TR::VRaw vr[TR::kVF];
+  PageIds cp_ids = page_ids(bt_row, c < i1 ? c : i0, n_seq);
+  ChunkPages cp = pages_of<TR>(A, U.kv_head, cp_ids);
+  // FP8 pages: each chunk's scales are loaded just before its K DMA (so only V follows the DMA)
+  float scl_cur = load_scale_lane<TR>(A, U.kv_head, cp_ids, lane);
   if constexpr (kKviaLds) dma_k(kslot, cp);
   else load_k<TR>(cp, kl, vl, kf);
-  load_v<TR>(cp, kl, vl, vf);
+  load_v<TR>(cp, vl, vr);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -732,13 +894,18 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
     const int cc = c + j * kWaves;
     const int key0 = cc * kChunkKeys;
     const int cn = cc + kWaves;
-    if (cn < i1) cp = pages_of<TR>(A, U.kv_head, nx);
+    if (cn < i1) {
+      cp_ids = nx;
+      cp = pages_of<TR>(A, U.kv_head, nx);
+    }
     typename TR::PFrag pf[RT];
+    float scl_nxt = 0.f;
     if constexpr (kKviaLds) {
       wait_vmcnt<TR::kVLoads>();  // the K DMA of this chunk has landed (only V was issued after it)
       asm volatile("" ::: "memory");
       TR::template lds_read_k<RG>(kslot, lane, kf);  // completes before the slot is refilled
       asm volatile("" ::: "memory");
+      scl_nxt = load_scale_lane<TR>(A, U.kv_head, cp_ids, lane);
       dma_k(kslot, cp);
       auto getq_asm = [&](int rt, u32x4_t (&qf)[TR::kQF]) {  // Q reads behind the DMA just issued
         uint32_t a[TR::kQF];
@@ -746,19 +913,24 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
         for (int f = 0; f < TR::kQF; ++f) a[f] = lds_addr(qlds + (rt * TR::kQF + f) * 64 + lane);
         lds_read_b128<TR::kQF>(a, qf);
       };
-      softmax_chunk<TR, RT, kTree>(st, getq_asm, kf, key0, p_row, tm, key0 + kChunkKeys - 1 >= mask_from,
-                                   A.scale_log2, lane, pf);
+      softmax_chunk<TR, RT, kTree>(st, getq_asm, kf, key0, p_row, tm, read_scales<TR>(scl_cur),
+                                   key0 + kChunkKeys - 1 >= mask_from, A.scale_log2, lane, pf);
       asm volatile("" ::: "memory");
     } else {
       asm volatile("" ::: "memory");  // keep the Q reads inside the loop
-      softmax_chunk<TR, RT, kTree>(st, getq, kf, key0, p_row, tm, key0 + kChunkKeys - 1 >= mask_from,
-                                   A.scale_log2, lane, pf);
+      softmax_chunk<TR, RT, kTree>(st, getq, kf, key0, p_row, tm, read_scales<TR>(scl_cur),
+                                   key0 + kChunkKeys - 1 >= mask_from, A.scale_log2, lane, pf);
+      scl_nxt = load_scale_lane<TR>(A, U.kv_head, cp_ids, lane);
       load_k<TR>(cp, kl, vl, kf);
     }
+    scl_cur = scl_nxt;
     nx = page_ids(bt_row, min(cn + kWaves, i1 - 1), n_seq);
+    u32x4_t vf[TR::kVF];
+#pragma unroll
+    for (int f = 0; f < TR::kVF; ++f) vf[f] = TR::v_convert(vr[f]);
     TR::sanitize_v(vf, quad, n_seq - key0);
     pv_chunk<TR, RT>(st, vf, pf);
-    load_v<TR>(cp, kl, vl, vf);
+    load_v<TR>(cp, vl, vr);
   }
   if constexpr (kKviaLds) wait_all_loads();  // the last (unused) K DMA has landed before LDS is reused
   __syncthreads();  // every wave is done with its Q slice before the merge buffer overwrites it
@@ -809,8 +981,8 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
 template <class TR, int RT, bool kTree, class Issue, class After, class GetQ>
 __device__ __forceinline__ void ring_step(char* fill, const char* cur, Issue issue, bool do_issue, After after_reads,
                                           bool active, State<TR, RT>& st, GetQ getq, int key0,
-                                          const int (&p_row)[RT], const TreeMask<RT>& tm, int mask_from, int n_seq,
-                                          float sl2, int lane) {
+                                          const int (&p_row)[RT], const TreeMask<RT>& tm, const ChunkScale& cs,
+                                          int mask_from, int n_seq, float sl2, int lane) {
   using RG = Ring<TR>;
   if (do_issue) issue(fill);
   if (active) {
@@ -818,7 +990,8 @@ __device__ __forceinline__ void ring_step(char* fill, const char* cur, Issue iss
     u32x4_t kf[TR::kKF];
     TR::template lds_read_k<RG>(cur, lane, kf);
     typename TR::PFrag pf[RT];
-    softmax_chunk<TR, RT, kTree>(st, getq, kf, key0, p_row, tm, key0 + kChunkKeys - 1 >= mask_from, sl2, lane, pf);
+    softmax_chunk<TR, RT, kTree>(st, getq, kf, key0, p_row, tm, cs, key0 + kChunkKeys - 1 >= mask_from, sl2, lane,
+                                 pf);
     u32x4_t vf[TR::kVF];
     TR::template lds_read_v<RG>(cur, lane, vf);
     asm volatile("" ::: "memory");
@@ -876,7 +1049,12 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
   // Wave w copies block w of each chunk; lane `lane` of DMA instruction i fills LDS bytes
   // [i*1024 + 16*lane, +16) of the block image, i.e. row r, swizzled column cc.
   char* ring = reinterpret_cast<char*>(sm.buf);
-  auto issue = [&](PageIds ids, char* slot) {
+  // FP8 pages: every wave loads a chunk's scales just before its DMAs; they travel with the chunk
+  // through a shift register (scl[0] belongs to the chunk being computed).
+  constexpr int kPerChunk = RG::kInstr + (TR::kScaled ? 1 : 0);  // this wave's loads per chunk
+  float scl[RG::kNB];
+  auto issue = [&](PageIds ids, char* slot) -> float {
+    const float sc = load_scale_lane<TR>(A, U.kv_head, ids, lane);
     const ChunkPages cp = pages_of<TR>(A, U.kv_head, ids);
     const __amdgpu_buffer_rsrc_t rs = block_rsrc(w == 0 ? cp.k0 : w == 1 ? cp.k1 : w == 2 ? cp.v0 : cp.v1, RG::kBlk);
     char* dst = slot + w * RG::kBlk;
@@ -893,27 +1071,32 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
       }
       dma16(rs, src, dst + i * 1024);
     }
+    return sc;
   };
 
 #pragma unroll
   for (int j = 0; j < RG::kNB - 1; ++j)
-    if (i0 + j < i1) issue(page_ids(bt_row, i0 + j, n_seq), ring + j * RG::kChunk);
+    scl[j] = i0 + j < i1 ? issue(page_ids(bt_row, i0 + j, n_seq), ring + j * RG::kChunk) : 0.f;
   // page ids of the chunk issued in the next iteration, loaded one iteration ahead
   PageIds nx = page_ids(bt_row, min(i0 + RG::kNB - 1, i1 - 1), n_seq);
   for (int c = i0; c < i1; ++c) {
     const int j = c - i0;
     const int ahead = min(RG::kNB - 2, i1 - 1 - c);  // chunks this wave issued after chunk c
     static_assert(RG::kNB <= 4, "waits below cover up to 2 chunks ahead");
-    if (ahead >= 2) wait_vmcnt<2 * RG::kInstr>();
-    else if (ahead == 1) wait_vmcnt<RG::kInstr>();
+    if (ahead >= 2) wait_vmcnt<2 * kPerChunk>();
+    else if (ahead == 1) wait_vmcnt<kPerChunk>();
     else wait_vmcnt<0>();
     lds_barrier();  // chunk c is in LDS for every wave; chunk c-1's slot is free
     const int next = c + RG::kNB - 1;
+    float scl_new = 0.f;
     ring_step<TR, RT, kTree>(
         ring + ((j + RG::kNB - 1) % RG::kNB) * RG::kChunk, ring + (j % RG::kNB) * RG::kChunk,
-        [&](char* slot) { issue(nx, slot); }, next < i1,
+        [&](char* slot) { scl_new = issue(nx, slot); }, next < i1,
         [&] { nx = page_ids(bt_row, min(next + 1, i1 - 1), n_seq); }, active, st, getq, c * kChunkKeys, p_row,
-        tm, mask_from, n_seq, A.scale_log2, lane);
+        tm, read_scales<TR>(scl[0]), mask_from, n_seq, A.scale_log2, lane);
+#pragma unroll
+    for (int k = 0; k + 1 < RG::kNB - 1; ++k) scl[k] = scl[k + 1];
+    scl[RG::kNB - 2] = scl_new;
   }
   wait_all_loads();  // nothing of this unit left in flight
   lds_barrier();                        // every wave is done with the ring before it is reused
@@ -1690,6 +1873,16 @@ int launch_attention_fused(const AttnArgs& a, int dtype, int D, int grid, void* 
   return D == 128 ? launch_fused_t<F32<128>>(a, grid, stream) : launch_fused_t<F32<64>>(a, grid, stream);
 }
 
+int launch_attention_fp8kv(const AttnArgs& a, int D, int grid, void* stream) {
+  if (D == 128)
+    hipLaunchKernelGGL((attention_fused_kernel<Fp8Kv<128>, false>), dim3(grid), dim3(kThreads), 0,
+                       as_stream(stream), a);
+  else
+    hipLaunchKernelGGL((attention_fused_kernel<Fp8Kv<64>, false>), dim3(grid), dim3(kThreads), 0,
+                       as_stream(stream), a);
+  return int(hipGetLastError());
+}
+
 // The staged and the single-launch kernels (with and without tree masks) run on the same grid (the
 // smallest occupancy), so all cut the batch into the same grains and the staged and single-launch
 // paths give bitwise identical results.
@@ -1725,8 +1918,22 @@ int launch_fill_zero(void* p, size_t bytes, void* stream) {
   return int(hipGetLastError());
 }
 
+template <class TR>
+static int fp8_blocks_per_cu_t() {
+  int n = 0;
+  void (*fn)(AttnArgs) = attention_fused_kernel<TR, false>;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(fn), kThreads, 0) != hipSuccess)
+    return -1;
+  return n;
+}
+
+// bf16 descriptors also cover FP8 pages (bf16 q / out): their grid is the smaller of the two occupancies
 int attention_blocks_per_cu(int dtype, int D) {
-  if (dtype == PA_BF16) return D == 128 ? blocks_per_cu_t<Bf16<128>>() : blocks_per_cu_t<Bf16<64>>();
+  if (dtype == PA_BF16) {
+    const int a = D == 128 ? blocks_per_cu_t<Bf16<128>>() : blocks_per_cu_t<Bf16<64>>();
+    const int b = D == 128 ? fp8_blocks_per_cu_t<Fp8Kv<128>>() : fp8_blocks_per_cu_t<Fp8Kv<64>>();
+    return a < 0 || b < 0 ? -1 : (a < b ? a : b);
+  }
   return D == 128 ? blocks_per_cu_t<F32<128>>() : blocks_per_cu_t<F32<64>>();
 }
 

@@ -1,0 +1,89 @@
+"""GPU parity of attention over FP8 E4M3 KV pages (pa_attention_fp8kv) against the oracle's
+attention_fp8 on the same codes and scales.  The oracle dequantizes exactly in fp64; the kernel
+converts the codes to bf16 exactly and applies the per-(page, head) scales to scores and softmax
+weights, so the bf16 tolerances apply: 2e-2 max-abs and 2e-3 mean-abs for out and lse."""
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_cache_gqa_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU-only container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import paged_kv_cache_gqa_amd as pa  # noqa: E402
+
+
+def run_fp8(w):
+    t = pa.to_device(w)
+    out, lse = pa.attention_fp8kv(t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["v_scale"], t["block_table"],
+                                  t["seq_lens"], t["query_start_loc"], w.scale)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def ref_fp8(w):
+    return oracle.attention_fp8(w.q, w.k_pool, w.v_pool, w.meta["k_scale"], w.meta["v_scale"], w.block_table,
+                                w.seq_lens, w.query_start_loc, w.scale)
+
+
+def check(w, out, lse, ref=None):
+    ref_o, ref_l = ref if ref is not None else ref_fp8(w)
+    o, l = out.float().cpu().numpy(), lse.cpu().numpy()
+    eo, el = np.abs(o - ref_o), np.abs(l - ref_l)
+    msg = (f"{w.name}: max|dout|={eo.max():.3e} mean={eo.mean():.3e} max|dlse|={el.max():.3e} "
+           f"mean={el.mean():.3e}")
+    print(msg, flush=True)
+    assert np.isfinite(o).all() and np.isfinite(l).all(), msg
+    assert eo.max() <= 2e-2 and el.max() <= 2e-2 and eo.mean() <= 2e-3 and el.mean() <= 2e-3, msg
+
+
+CASES = [
+    # seed, B, max_len, Hq, Hkv, D, max_q
+    (111, 7, 900, 32, 8, 128, 1),     # decode: key-split units
+    (112, 6, 700, 32, 8, 128, 5),     # verify windows
+    (113, 4, 800, 8, 1, 128, 300),    # prefill chunks: 128-row units through the LDS ring
+    (114, 9, 300, 8, 2, 64, 20),
+    (115, 5, 500, 64, 8, 128, 1),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"s{c[0]}-D{c[5]}-G{c[3] // c[4]}-q{c[6]}" for c in CASES])
+def test_fp8_random(case):
+    seed, B, L, Hq, Hkv, D, mq = case
+    w = W.to_fp8(W.make_random(seed, B, L, Hq, Hkv, D, "bf16", max_q=mq))
+    out, lse = run_fp8(w)
+    check(w, out, lse)
+
+
+@pytest.mark.parametrize("c", [2, 3, 4])
+def test_fp8_full_config(c):
+    w = W.to_fp8(W.make_config(c))
+    out, lse = run_fp8(w)
+    check(w, out, lse)
+
+
+def test_fp8_nan_codes_in_unused_slots_change_nothing():
+    w = W.to_fp8(W.make_random(116, 6, 400, 32, 8, 128, "bf16", max_q=3))
+    o1, l1 = run_fp8(w)
+    used = np.zeros((w.num_pages, 16), dtype=bool)
+    for s in range(w.num_seqs):
+        for j in range(int(w.seq_lens[s])):
+            used[w.block_table[s, j // 16], j % 16] = True
+    k, v = w.k_pool.copy(), w.v_pool.copy()
+    k[~used[:, None, :, None].repeat(w.num_kv_heads, 1).repeat(w.head_dim, 3)] = 0x7F  # E4M3 NaN
+    v[~used[:, None, None, :].repeat(w.num_kv_heads, 1).repeat(w.head_dim, 2)] = 0xFF
+    w.k_pool, w.v_pool = k, v
+    o2, l2 = run_fp8(w)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_fp8_rejects_non_bf16_queries():
+    w = W.to_fp8(W.make_random(117, 3, 100, 8, 2, 64, "bf16", max_q=1))
+    t = pa.to_device(w)
+    with pytest.raises(TypeError):
+        pa.attention_fp8kv(t["q"].float(), t["k_pool"], t["v_pool"], t["k_scale"], t["v_scale"], t["block_table"],
+                           t["seq_lens"], t["query_start_loc"], w.scale)
