@@ -194,6 +194,67 @@ def bench_append(args, w) -> int:
     return 0
 
 
+def bench_prefix(args) -> int:
+    """Shared-prefix attention on the system-prompt decode batch: the cascade (prefix pass, suffix
+    pass, merge) against plain pa_attention on the same batch.  value = distinct K/V bytes (the
+    shared prefix once per group) plus Q, out, LSE and block-table entries, over the step time."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_gqa_amd as pa
+    from paged_kv_cache_gqa_amd import binding as B
+    from paged_kv_cache_gqa_amd import workloads as W
+
+    w = W.make_shared_prefix_config()
+    t = pa.to_device(w)
+    gs = torch.from_numpy(w.meta["group_start"].astype(np.int32)).cuda()
+    pl = torch.from_numpy(w.meta["prefix_len"].astype(np.int32)).cuda()
+    desc = pa.make_desc(t["q"], t["k_pool"], t["block_table"], t["seq_lens"], w.scale)
+    ws = pa.shared_prefix_workspace(desc, int(pl.shape[0]))
+    out = torch.empty_like(t["q"])
+    lse = torch.empty(t["q"].shape[:2], dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    vp = ctypes.c_void_p
+    L = B.lib()
+    dref = ctypes.byref(desc)
+    base = (dref, vp(t["q"].data_ptr()), vp(t["k_pool"].data_ptr()), vp(t["v_pool"].data_ptr()),
+            vp(t["block_table"].data_ptr()), vp(t["seq_lens"].data_ptr()), vp(t["query_start_loc"].data_ptr()))
+    tail = (vp(out.data_ptr()), vp(lse.data_ptr()), vp(ws.data_ptr()), ws.numel(), vp(stream.cuda_stream))
+    calls = {"shared_prefix": lambda: L.pa_attention_shared_prefix(*base, int(pl.shape[0]), vp(gs.data_ptr()),
+                                                                    vp(pl.data_ptr()), *tail),
+             "plain": lambda: L.pa_attention(*base, *tail)}
+    ms = {}
+    for name, fn in calls.items():
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            if fn():
+                raise RuntimeError(f"{name} launch failed")
+        torch.cuda.synchronize()
+        ms[name] = (time.perf_counter() - t0) * 1e3 / args.steps
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    uniq = W.shared_prefix_unique_bytes(w)
+    line = {
+        "metric": "shared-prefix attention GB/s (distinct K/V pages read once) , 1 MI355X",
+        "value": round(uniq / (ms["shared_prefix"] * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms["shared_prefix"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded)",
+        "config": {"workload": f"{w.name}: 8 groups x 16 decode sequences, 4096-token shared prefix, suffix "
+                               "256..1024, 32/8 heads, head dim 128", "distinct_bytes": uniq,
+                   "plain_algorithmic_bytes": w.algorithmic_bytes()},
+        "plain_attention_ms_per_step": round(ms["plain"], 5),
+        "speedup_vs_plain": round(ms["plain"] / ms["shared_prefix"], 3),
+        "frac_of_hbm_peak": round(uniq / (ms["shared_prefix"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -202,11 +263,13 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--part", default="all", choices=["all", "prefill", "decode"],
                     help="configuration 3 only: time its prefill chunks or its decode rows alone")
-    ap.add_argument("--op", default="attention", choices=["attention", "append", "tree", "fp8"],
+    ap.add_argument("--op", default="attention", choices=["attention", "append", "tree", "fp8", "prefix"],
                     help="attention (default): the attention call; append: the paged KV append of the batch's new "
                          "tokens (pa_append_kv); tree: attention with each window a random draft-token tree "
                          "(pa_attention_tree); fp8: attention over the batch's K/V quantized to FP8 E4M3 pages with "
-                         "per-(page, kv head) scales (pa_attention_fp8kv)")
+                         "per-(page, kv head) scales (pa_attention_fp8kv); prefix: shared-prefix attention "
+                         "(pa_attention_shared_prefix) on the system-prompt decode batch (8 groups x 16 sequences, "
+                         "4096-token shared prefix), --config ignored")
     ap.add_argument("--staged", action="store_true",
                     help="time pa_plan + pa_attention_planned + pa_merge_planned instead of the single launch")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
@@ -240,6 +303,8 @@ def main() -> int:
     from paged_kv_cache_gqa_amd import workloads as W
 
     torch.cuda.set_device(0)
+    if args.op == "prefix":
+        return bench_prefix(args)
     w = W.make_config(args.config)
     if args.part != "all":
         ql = w.q_lens()

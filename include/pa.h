@@ -142,6 +142,32 @@ pa_status pa_attention(const pa_desc* desc, const void* q, const void* k_pool, c
                        size_t workspace_bytes, void* stream);
 
 /*
+ * pa_attention for batches whose sequences share prompt prefixes (the
+ * prefix-reuse attention of the XY-Serve verdict page, load_bearing_attack
+ * and pith_inferences: shared prefix pages; the result is identical to
+ * pa_attention's, up to rounding).  Sequences group_start[g] ..
+ * group_start[g+1]-1 form group g (groups are contiguous runs of sequences,
+ * group_start[0] = 0, group_start[num_groups] = B; a sequence alone is a
+ * group of one).  The first prefix_len[g] keys of every member are the same
+ * physical pages: prefix_len[g] is a multiple of 16 (0 allowed), every member
+ * has prefix_len[g] <= seq_len - q_len (its query window lies after the
+ * prefix) and the same first prefix_len[g] / 16 block-table entries; breaking
+ * these is undefined behaviour.  The shared pages are read once per group and
+ * KV head (all the group's query rows form MFMA tiles over them), each
+ * sequence's remaining keys once; the two partial results are merged by
+ * log-sum-exp.  group_start [num_groups+1] and prefix_len [num_groups] are
+ * int32 device arrays.  Workspace: pa_shared_prefix_workspace_size bytes,
+ * 256-byte aligned, zero arrival counters as for pa_attention (it begins with
+ * the pa_attention workspace).  Enqueues four kernels; 1 <= num_groups <= B.
+ */
+pa_status pa_shared_prefix_workspace_size(const pa_desc* desc, int32_t num_groups, size_t* bytes);
+pa_status pa_attention_shared_prefix(const pa_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                                     const int32_t* block_table, const int32_t* seq_lens,
+                                     const int32_t* query_start_loc, int32_t num_groups, const int32_t* group_start,
+                                     const int32_t* prefix_len, void* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/*
  * pa_attention over FP8 KV pages (a quantized KV cache, as listed among the
  * serving optimizations in the "Arctic Inference with Shift Parallelism"
  * review; MI355X decodes OCP FP8 natively).  k_pool / v_pool hold OCP FP8 E4M3

@@ -11,7 +11,7 @@ _BINDING_NAMES = {
     "attention", "plan", "attention_planned", "merge_planned", "plan_read", "gather_kv", "merge", "validate",
     "check_desc", "workspace_size", "alloc_workspace", "make_desc", "status_string", "abi_version", "lib",
     "PagedAttentionError", "PaDesc", "to_device", "append_kv", "workspace_init", "attention_tree",
-    "attention_fp8kv",
+    "attention_fp8kv", "attention_shared_prefix", "shared_prefix_workspace",
 }
 
 

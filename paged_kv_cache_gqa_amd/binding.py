@@ -82,9 +82,11 @@ def lib():
         L.pa_append_kv.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.pa_attention_tree.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.pa_attention_fp8kv.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.pa_shared_prefix_workspace_size.argtypes = [dp, i32, ctypes.POINTER(sz)]
+        L.pa_attention_shared_prefix.argtypes = [dp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
         for name in ("pa_check_desc", "pa_workspace_size", "pa_workspace_init", "pa_attention", "pa_plan", "pa_attention_planned",
                      "pa_merge_planned", "pa_plan_read", "pa_gather_kv", "pa_merge", "pa_validate", "pa_append_kv", "pa_attention_tree",
-                     "pa_attention_fp8kv"):
+                     "pa_attention_fp8kv", "pa_shared_prefix_workspace_size", "pa_attention_shared_prefix"):
             getattr(L, name).restype = ctypes.c_int
         if L.pa_abi_version() != 1:
             raise PagedAttentionError("load", -1, "ABI version mismatch")
@@ -236,6 +238,42 @@ def attention_fp8kv(q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens, 
            lib().pa_attention_fp8kv(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
                                     _ptr(v_scale), _ptr(block_table), _ptr(seq_lens), _ptr(query_start_loc),
                                     _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def shared_prefix_workspace(desc: PaDesc, num_groups: int, device=None) -> torch.Tensor:
+    """Workspace for pa_attention_shared_prefix (arrival counters initialised)."""
+    n = ctypes.c_size_t(0)
+    _check("pa_shared_prefix_workspace_size",
+           lib().pa_shared_prefix_workspace_size(ctypes.byref(desc), int(num_groups), ctypes.byref(n)))
+    ws = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=device or "cuda")
+    workspace_init(desc, ws)
+    return ws
+
+
+def attention_shared_prefix(q, k_pool, v_pool, block_table, seq_lens, query_start_loc, group_start, prefix_len,
+                            scale: float, out=None, lse=None, workspace=None, stream=None):
+    """pa_attention_shared_prefix: groups of sequences (group_start [G+1], prefix_len [G], int32 device
+    tensors) whose first prefix_len keys are shared pages.  Returns (out, lse)."""
+    _check_inputs(q, k_pool, v_pool, block_table, seq_lens, query_start_loc)
+    for name, t in (("group_start", group_start), ("prefix_len", prefix_len)):
+        if not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    G = prefix_len.shape[0]
+    if group_start.shape != (G + 1,):
+        raise ValueError("group_start must hold num_groups + 1 entries")
+    desc = make_desc(q, k_pool, block_table, seq_lens, scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = shared_prefix_workspace(desc, G, q.device)
+    _check("pa_attention_shared_prefix",
+           lib().pa_attention_shared_prefix(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                            _ptr(seq_lens), _ptr(query_start_loc), int(G), _ptr(group_start),
+                                            _ptr(prefix_len), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                            _stream(stream)))
     return out, lse
 
 

@@ -105,6 +105,7 @@ pa::PlanView plan_view(const pa_desc& d, const int32_t* seq_lens, const int32_t*
   v.num_seqs = d.num_seqs;
   v.num_kv_heads = d.num_kv_heads;
   v.group = d.num_q_heads / d.num_kv_heads;
+  v.full_rows = 0;
   return v;
 }
 
@@ -123,6 +124,8 @@ pa::AttnArgs attn_args(const pa_desc& d, const void* q, const void* k, const voi
   a.tree_mask = nullptr;
   a.k_scale = nullptr;
   a.v_scale = nullptr;
+  a.key_base = nullptr;
+  a.out_f32 = nullptr;
   a.arrive = ws.arrive;
   a.num_q_heads = d.num_q_heads;
   a.max_pages = d.max_pages_per_seq;
@@ -190,6 +193,7 @@ pa_status pa_plan(const pa_desc* desc, const int32_t* seq_lens, const int32_t* q
   a.seq_cost = ws.seq_cost;
   a.slots = ws.slots;
   a.arrive = ws.arrive;
+  a.full_rows = 0;
   a.num_seqs = desc->num_seqs;
   a.num_kv_heads = desc->num_kv_heads;
   a.group = desc->num_q_heads / desc->num_kv_heads;
@@ -255,6 +259,100 @@ pa_status pa_attention(const pa_desc* desc, const void* q, const void* k_pool, c
                        void* workspace, size_t workspace_bytes, void* stream) {
   return single_launch(desc, q, k_pool, v_pool, block_table, seq_lens, qsl, nullptr, out, lse, workspace,
                        workspace_bytes, stream);
+}
+
+namespace {
+// Shared-prefix batches: after the attention workspace come the two passes' derived arrays and
+// their fp32 results (part 0: prefix pass, part 1: suffix pass).
+struct PrefixWs {
+  int32_t *pre_seq_lens, *pre_qsl, *pre_bt, *suf_seq_lens, *key_base;
+  float *part_lse, *part_o;
+  size_t total;
+};
+PrefixWs prefix_layout(const pa_desc& d, int G, size_t base, void* ws) {
+  const size_t B = size_t(d.num_seqs), rows = size_t(d.num_q_tokens) * size_t(d.num_q_heads);
+  size_t off = base;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += pa::align256(bytes > 0 ? bytes : 1);
+    return static_cast<char*>(ws) + o;
+  };
+  PrefixWs p;
+  p.pre_seq_lens = reinterpret_cast<int32_t*>(take(4 * size_t(G)));
+  p.pre_qsl = reinterpret_cast<int32_t*>(take(4 * (size_t(G) + 1)));
+  p.pre_bt = reinterpret_cast<int32_t*>(take(4 * size_t(G) * size_t(d.max_pages_per_seq)));
+  p.suf_seq_lens = reinterpret_cast<int32_t*>(take(4 * B));
+  p.key_base = reinterpret_cast<int32_t*>(take(4 * B));
+  p.part_lse = reinterpret_cast<float*>(take(4 * 2 * rows));
+  p.part_o = reinterpret_cast<float*>(take(4 * 2 * rows * size_t(d.head_dim)));
+  p.total = off;
+  return p;
+}
+}  // namespace
+
+pa_status pa_shared_prefix_workspace_size(const pa_desc* desc, int32_t num_groups, size_t* bytes) {
+  if (!desc || !bytes) return PA_ERR_NULL_POINTER;
+  size_t base = 0;
+  const pa_status st = pa_workspace_size(desc, &base);
+  if (st != PA_OK) return st;
+  if (num_groups < 0 || num_groups > desc->num_seqs) return PA_ERR_BAD_SHAPE;
+  *bytes = prefix_layout(*desc, num_groups, base, nullptr).total;
+  return PA_OK;
+}
+
+pa_status pa_attention_shared_prefix(const pa_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                                     const int32_t* block_table, const int32_t* seq_lens, const int32_t* qsl,
+                                     int32_t num_groups, const int32_t* group_start, const int32_t* prefix_len,
+                                     void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!desc) return PA_ERR_NULL_POINTER;
+  const pa_status st = pa_check_desc(desc);
+  if (st != PA_OK) return st;
+  if (desc->num_q_tokens == 0) return PA_OK;
+  if (num_groups < 1 || num_groups > desc->num_seqs) return PA_ERR_BAD_SHAPE;
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !qsl || !group_start || !prefix_len || !out ||
+      !lse || !workspace)
+    return PA_ERR_NULL_POINTER;
+  int grid = 0;
+  Ws ws;
+  const pa_status ps = prepare(desc, workspace, workspace_bytes, &grid, &ws);
+  if (ps != PA_OK) return ps;
+  const PrefixWs pw = prefix_layout(*desc, num_groups, ws.L.total, workspace);
+  if (workspace_bytes < pw.total) return PA_ERR_WORKSPACE_TOO_SMALL;
+  const int64_t rows = int64_t(desc->num_q_tokens) * desc->num_q_heads;
+  pa::PrefixPrep pp;
+  pp.group_start = group_start;
+  pp.prefix_len = prefix_len;
+  pp.seq_lens = seq_lens;
+  pp.qsl = qsl;
+  pp.block_table = block_table;
+  pp.pre_seq_lens = pw.pre_seq_lens;
+  pp.pre_qsl = pw.pre_qsl;
+  pp.pre_bt = pw.pre_bt;
+  pp.suf_seq_lens = pw.suf_seq_lens;
+  pp.key_base = pw.key_base;
+  pp.pre_o = pw.part_o;
+  pp.pre_lse = pw.part_lse;
+  pp.rows = rows;
+  pp.num_groups = num_groups;
+  pp.max_pages = desc->max_pages_per_seq;
+  pp.head_dim = desc->head_dim;
+  if (pa::launch_prefix_prep(pp, stream) != 0) return PA_ERR_HIP;
+  // prefix pass: one sequence per group, every row sees the whole shared prefix
+  pa_desc dp = *desc;
+  dp.num_seqs = num_groups;
+  pa::AttnArgs a = attn_args(dp, q, k_pool, v_pool, pw.pre_bt, pw.pre_seq_lens, pw.pre_qsl, out, pw.part_lse, ws);
+  a.plan.full_rows = 1;
+  a.out_f32 = pw.part_o;
+  if (pa::launch_attention_fused(a, desc->dtype, desc->head_dim, grid, stream) != 0) return PA_ERR_HIP;
+  // suffix pass: every sequence from the end of its prefix on, causal as usual
+  pa::AttnArgs b = attn_args(*desc, q, k_pool, v_pool, block_table, pw.suf_seq_lens, qsl, out, pw.part_lse + rows, ws);
+  b.key_base = pw.key_base;
+  b.out_f32 = pw.part_o + rows * desc->head_dim;
+  if (pa::launch_attention_fused(b, desc->dtype, desc->head_dim, grid, stream) != 0) return PA_ERR_HIP;
+  // log-sum-exp merge of the two passes into out / lse
+  return pa::launch_merge(2, rows, desc->head_dim, pw.part_o, pw.part_lse, desc->dtype, out, lse, stream) == 0
+             ? PA_OK
+             : PA_ERR_HIP;
 }
 
 pa_status pa_attention_fp8kv(const pa_desc* desc, const void* q, const uint8_t* k_pool, const uint8_t* v_pool,

@@ -69,7 +69,8 @@ struct PlanView {
   const SlotStart* slots;   // [max grains]
   int32_t num_seqs;
   int32_t num_kv_heads;
-  int32_t group;  // Hq / Hkv
+  int32_t group;      // Hq / Hkv
+  int32_t full_rows;  // 1: every row of a sequence sees all its keys (no causal limit)
 };
 
 struct AttnArgs {
@@ -85,6 +86,9 @@ struct AttnArgs {
   const uint64_t* tree_mask;  // [T_q] per-row window masks, or null for the causal rule
   const float* k_scale;       // [NP][Hkv] FP8 pages: scale of each (page, kv head), else null
   const float* v_scale;
+  const int32_t* key_base;    // [B] or null: sequence s's keys start at key key_base[s] (a multiple of 16)
+                              // of its block-table row; seq_lens then count keys from there
+  float* out_f32;             // [T_q][Hq][D] or null: final results go here in fp32 instead of to out
   int32_t* arrive;  // [grains]: pieces of the split unit whose first piece is in grain k that have
                     // finished (single-launch path; zero between calls)
   int32_t num_q_heads;
@@ -104,6 +108,7 @@ struct PlanArgs {
   int32_t group;
   int32_t grid;  // workgroups of the persistent attention launch
   int32_t* arrive;  // zeroed for a following single-launch call
+  int32_t full_rows;
 };
 
 struct MergeArgs {
@@ -126,6 +131,25 @@ struct AppendArgs {
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t max_pages;
+};
+
+struct PrefixPrep {
+  const int32_t* group_start;  // [G+1]
+  const int32_t* prefix_len;   // [G]
+  const int32_t* seq_lens;
+  const int32_t* qsl;
+  const int32_t* block_table;
+  int32_t* pre_seq_lens;  // [G]
+  int32_t* pre_qsl;       // [G+1]
+  int32_t* pre_bt;        // [G][max_pages]
+  int32_t* suf_seq_lens;  // [B]
+  int32_t* key_base;      // [B]
+  float* pre_o;           // [rows][D]
+  float* pre_lse;         // [rows]
+  int64_t rows;           // T_q * Hq
+  int32_t num_groups;
+  int32_t max_pages;
+  int32_t head_dim;
 };
 
 // Workspace: [header | arrival counters | per-sequence cost prefix | grain starts | partial lse |
@@ -186,6 +210,7 @@ int launch_merge(int n_parts, int64_t rows, int D, const float* o_parts, const f
 // pages of one sequence per workgroup of the append kernel
 constexpr int kAppendPages = 2;
 int launch_append_kv(const AppendArgs& a, int dtype, int num_seqs, int num_q_tokens, void* stream);
+int launch_prefix_prep(const PrefixPrep& a, void* stream);
 int launch_validate(const pa_desc& d, const int32_t* block_table, const int32_t* seq_lens,
                     const int32_t* qsl, int32_t* flag, void* stream);
 // Workgroups per CU the attention kernel can hold (occupancy query), or < 0 on error.

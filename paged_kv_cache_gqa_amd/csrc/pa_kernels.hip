@@ -669,7 +669,7 @@ __device__ __forceinline__ RowInfo row_info(const AttnArgs& A, const pa_plan_uni
   const int hh = rr - t * A.plan.group;
   ri.tok = q0 + t;
   ri.head = U.kv_head * A.plan.group + hh;
-  ri.p = ri.valid ? n_seq - qn + t : -1;
+  ri.p = ri.valid ? (A.plan.full_rows ? n_seq - 1 : n_seq - qn + t) : -1;
   return ri;
 }
 
@@ -726,8 +726,9 @@ __device__ __forceinline__ void emit(const AttnArgs& A, const RowInfo& ri, int r
   if (!ri.valid) return;
   const int d = 16 * t + 4 * quad;
   if (part < 0) {
-    char* dst = static_cast<char*>(A.out) + ((int64_t(ri.tok) * A.num_q_heads + ri.head) * TR::D + d) * TR::kEb;
-    TR::store_out(dst, o);
+    const int64_t elem = (int64_t(ri.tok) * A.num_q_heads + ri.head) * TR::D + d;
+    if (A.out_f32) *reinterpret_cast<f32x4_t*>(A.out_f32 + elem) = o;  // cascade pass: fp32 result
+    else TR::store_out(static_cast<char*>(A.out) + elem * TR::kEb, o);
     if (write_lse) A.lse[int64_t(ri.tok) * A.num_q_heads + ri.head] = lse_nat;
   } else {
     const uint32_t prow = uint32_t(part) * kPartRows + r;
@@ -812,7 +813,8 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
   const int n_seq = ro(A.plan.seq_lens)[s];
   const int q0 = ro(A.plan.qsl)[s];
   const int qn = ro(A.plan.qsl)[s + 1] - q0;
-  const cptr<int32_t> bt_row = ro(A.block_table) + int64_t(s) * A.max_pages;
+  const cptr<int32_t> bt_row = ro(A.block_table) + int64_t(s) * A.max_pages +
+                               (A.key_base ? ro(A.key_base)[s] / kPage : 0);
 
   RowInfo ri[RT];
   int p_row[RT];
@@ -821,7 +823,7 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
     ri[rt] = row_info(A, U, 16 * rt + (lane & 15), n_seq, q0, qn);
     p_row[rt] = ri[rt].p;
   }
-  const int min_p = n_seq - qn + U.row0 / A.plan.group;  // first row's last visible key
+  const int min_p = A.plan.full_rows ? n_seq - 1 : n_seq - qn + U.row0 / A.plan.group;  // first row's last key
   TreeMask<RT> tm;
   const int mask_from = tree_setup<RT, kTree>(A, ri, n_seq, qn, min_p, tm);
 
@@ -1020,7 +1022,8 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
   const int n_seq = ro(A.plan.seq_lens)[s];
   const int q0 = ro(A.plan.qsl)[s];
   const int qn = ro(A.plan.qsl)[s + 1] - q0;
-  const cptr<int32_t> bt_row = ro(A.block_table) + int64_t(s) * A.max_pages;
+  const cptr<int32_t> bt_row = ro(A.block_table) + int64_t(s) * A.max_pages +
+                               (A.key_base ? ro(A.key_base)[s] / kPage : 0);
   const bool active = 32 * w < U.n_rows;
 
   RowInfo ri[RT];
@@ -1030,7 +1033,7 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
     ri[rt] = row_info(A, U, 32 * w + 16 * rt + (lane & 15), n_seq, q0, qn);
     p_row[rt] = ri[rt].p;
   }
-  const int min_p = n_seq - qn + (U.row0 + 32 * w) / A.plan.group;
+  const int min_p = A.plan.full_rows ? n_seq - 1 : n_seq - qn + (U.row0 + 32 * w) / A.plan.group;
   TreeMask<RT> tm;
   const int mask_from = tree_setup<RT, kTree>(A, ri, n_seq, qn, min_p, tm);
 
@@ -1127,8 +1130,10 @@ __device__ __forceinline__ int64_t slice_begin(int64_t k, int64_t S, int64_t C) 
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// keys visible to the last row of row block rb of a sequence (n keys, qn tokens, G heads)
-__device__ __forceinline__ int block_keys(int n, int qn, int G, int rb) {
+// keys visible to the last row of row block rb of a sequence (n keys, qn tokens, G heads; with
+// full rows every row sees all n keys)
+__device__ __forceinline__ int block_keys(int n, int qn, int G, int rb, bool full) {
+  if (full) return n;
   const int rows = qn * G;
   const int last = (min(kBlockRows * (rb + 1), rows) - 1) / G;
   return n - qn + last + 1;
@@ -1137,13 +1142,15 @@ __device__ __forceinline__ int block_keys(int n, int qn, int G, int rb) {
 struct SeqUnits {
   int n, qn, rows, nb;
   bool split;        // one key-split unit per kv head
+  bool full;         // every row sees all n keys
   int64_t per_head;  // cost of one kv head's units
 };
 
-__device__ SeqUnits seq_units(int n, int qn, int G) {
+__device__ SeqUnits seq_units(int n, int qn, int G, bool full) {
   SeqUnits q;
   q.n = n;
   q.qn = qn;
+  q.full = full;
   q.rows = qn > 0 ? qn * G : 0;
   q.split = q.rows <= kSplitRows;
   if (qn <= 0) {
@@ -1155,7 +1162,7 @@ __device__ SeqUnits seq_units(int n, int qn, int G) {
   } else {
     q.nb = ceil_div(q.rows, kBlockRows);
     int64_t ch = 0;
-    for (int rb = 0; rb < q.nb; ++rb) ch += ceil_div(block_keys(n, qn, G, rb), kChunkKeys);
+    for (int rb = 0; rb < q.nb; ++rb) ch += ceil_div(block_keys(n, qn, G, rb, full), kChunkKeys);
     q.per_head = int64_t(q.nb) * kCostUnitStart + ch * kCostRowSplit;
   }
   return q;
@@ -1176,7 +1183,7 @@ __device__ pa_plan_unit make_unit(int s, const SeqUnits& q, int G, int g, int rb
   U.kv_head = g;
   U.row0 = q.split ? 0 : rb * kBlockRows;
   U.n_rows = q.split ? q.rows : min(kBlockRows, q.rows - rb * kBlockRows);
-  U.n_keys = q.split ? q.n : block_keys(q.n, q.qn, G, rb);
+  U.n_keys = q.split ? q.n : block_keys(q.n, q.qn, G, rb, q.full);
   U.n_chunks = ceil_div(U.n_keys, kChunkKeys);
   U.kind = q.split ? 0 : 1;
   U.cost_weight = q.split ? kCostKeySplit : kCostRowSplit;
@@ -1196,7 +1203,7 @@ struct UnitCursor {
 
 template <class P>
 __device__ void cursor_load_seq(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl) {
-  cu.q = seq_units(seq_lens[cu.s], qsl[cu.s + 1] - qsl[cu.s], v.group);
+  cu.q = seq_units(seq_lens[cu.s], qsl[cu.s + 1] - qsl[cu.s], v.group, v.full_rows != 0);
 }
 
 // Position the cursor on the unit of sequence s (n keys, qn queries, starting at cost seq_base)
@@ -1204,7 +1211,7 @@ __device__ void cursor_load_seq(UnitCursor& cu, const PlanView& v, P seq_lens, P
 __device__ void cursor_place(UnitCursor& cu, const PlanView& v, int s, int64_t seq_base, int n, int qn, int64_t c) {
   cu.s = s;
   cu.seq_base = seq_base;
-  cu.q = seq_units(n, qn, v.group);
+  cu.q = seq_units(n, qn, v.group, v.full_rows != 0);
   const int64_t off = c - cu.seq_base;
   cu.g = int(off / cu.q.per_head);
   int64_t acc = cu.seq_base + int64_t(cu.g) * cu.q.per_head;
@@ -1212,7 +1219,8 @@ __device__ void cursor_place(UnitCursor& cu, const PlanView& v, int s, int64_t s
   if (!cu.q.split) {
     for (; cu.rb < cu.q.nb - 1; ++cu.rb) {
       const int64_t wgt =
-          kCostUnitStart + int64_t(ceil_div(block_keys(cu.q.n, cu.q.qn, v.group, cu.rb), kChunkKeys)) * kCostRowSplit;
+          kCostUnitStart +
+          int64_t(ceil_div(block_keys(cu.q.n, cu.q.qn, v.group, cu.rb, cu.q.full), kChunkKeys)) * kCostRowSplit;
       if (c < acc + wgt) break;
       acc += wgt;
     }
@@ -1252,7 +1260,7 @@ __device__ __forceinline__ void cursor_from_slot(UnitCursor& cu, const PlanView&
   cu.g = st.g;
   cu.rb = st.rb;
   cu.seq_base = st.seq_base;
-  cu.q = seq_units(st.n, st.qn, v.group);
+  cu.q = seq_units(st.n, st.qn, v.group, v.full_rows != 0);
   cu.U = make_unit(st.s, cu.q, v.group, st.g, st.rb, st.unit_cost0);
 }
 
@@ -1294,8 +1302,9 @@ __device__ bool cursor_next(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl
 // All kThreads threads of the workgroup take part.  A thread takes kInFlight of its rows at a time
 // and loads kPieces pieces of them together before folding them in, in piece order.
 template <class TR, int kInFlight, int kPieces>
-__device__ void merge_unit(const float* part_o, const float* part_lse, void* out, float* lse, cptr<int32_t> qsl,
-                           int num_q_heads, int group, const pa_plan_unit& U, int64_t first, int n_pieces) {
+__device__ void merge_unit(const float* part_o, const float* part_lse, void* out, float* out_f32, float* lse,
+                           cptr<int32_t> qsl, int num_q_heads, int group, const pa_plan_unit& U, int64_t first,
+                           int n_pieces) {
   constexpr int kLanesPerRow = TR::D / 4;
   constexpr int kRowsPerPass = kThreads / kLanesPerRow;
   const int q0 = qsl[U.seq];
@@ -1349,7 +1358,9 @@ __device__ void merge_unit(const float* part_o, const float* part_lse, void* out
       const int head = U.kv_head * group + (rr - tk * group);
       const int64_t orow = int64_t(q0 + tk) * num_q_heads + head;
       // a row that saw no key at all (possible under a tree mask) gets out = 0, lse = -inf
-      TR::store_out(static_cast<char*>(out) + (orow * TR::D + 4 * d4) * TR::kEb, O[i] * (L[i] > 0.f ? 1.f / L[i] : 0.f));
+      const f32x4_t res = O[i] * (L[i] > 0.f ? 1.f / L[i] : 0.f);
+      if (out_f32) *reinterpret_cast<f32x4_t*>(out_f32 + orow * TR::D + 4 * d4) = res;
+      else TR::store_out(static_cast<char*>(out) + (orow * TR::D + 4 * d4) * TR::kEb, res);
       if (d4 == 0) lse[orow] = L[i] > 0.f ? M[i] + fast_log2(L[i]) * kLn2 : -INFINITY;
     }
   }
@@ -1381,8 +1392,8 @@ __device__ void arrive_and_merge(const AttnArgs& A, const pa_plan_unit& U, int64
   const bool last = *flag;
   __syncthreads();  // flag read by every thread before it is reused
   if (!last) return;
-  merge_unit<TR, 4, 4>(A.part_o, A.part_lse, A.out, A.lse, ro(A.plan.qsl), A.num_q_heads, A.plan.group, U, first,
-                    n_pieces);
+  merge_unit<TR, 4, 4>(A.part_o, A.part_lse, A.out, A.out_f32, A.lse, ro(A.plan.qsl), A.num_q_heads, A.plan.group,
+                       U, first, n_pieces);
   if (threadIdx.x == 0) __hip_atomic_store(A.arrive + first, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -1489,7 +1500,7 @@ __device__ __forceinline__ int64_t block_seq_costs(const PlanView& v, cptr<int32
     if (s < v.num_seqs) {
       n[e] = sl[s];
       qn[e] = qsl[s + 1] - qsl[s];
-      const SeqUnits q = seq_units(n[e], qn[e], v.group);
+      const SeqUnits q = seq_units(n[e], qn[e], v.group, v.full_rows != 0);
       c[e] = int64_t(v.num_kv_heads) * q.per_head;
       if (!q.split) row += c[e];
     }
@@ -1597,7 +1608,7 @@ __global__ __launch_bounds__(kScanThreads) void plan_kernel(PlanArgs a) {
     int64_t cost = 0, nu = 0;
     bool split = true;
     if (s < a.num_seqs) {
-      const SeqUnits q = seq_units(a.seq_lens[s], a.qsl[s + 1] - a.qsl[s], a.group);
+      const SeqUnits q = seq_units(a.seq_lens[s], a.qsl[s + 1] - a.qsl[s], a.group, a.full_rows != 0);
       cost = int64_t(a.num_kv_heads) * q.per_head;
       nu = int64_t(a.num_kv_heads) * q.nb;
       split = q.split;
@@ -1637,6 +1648,7 @@ __global__ __launch_bounds__(kScanThreads) void plan_kernel(PlanArgs a) {
   v.num_seqs = a.num_seqs;
   v.num_kv_heads = a.num_kv_heads;
   v.group = a.group;
+  v.full_rows = a.full_rows;
   for (int k = threadIdx.x; k < S; k += kScanThreads) {
     SlotStart r;
     r.c0 = slice_begin(k, S, C);
@@ -1703,8 +1715,8 @@ __global__ __launch_bounds__(kThreads) void merge_planned_kernel(MergeArgs a) {
   const int64_t first = first_grain(U, S, C);
   const int64_t last = last_grain(U, S, C);
   if (first != k - 1 || last < k) return;  // boundary k does not open this unit's split
-  merge_unit<TR, 4, 4>(a.part_o, a.part_lse, a.out, a.lse, ro(v.qsl), a.num_q_heads, v.group, U, first,
-                    int(last - first + 1));
+  merge_unit<TR, 4, 4>(a.part_o, a.part_lse, a.out, nullptr, a.lse, ro(v.qsl), a.num_q_heads, v.group, U, first,
+                       int(last - first + 1));
 }
 
 // Stand-alone merge: rows of n_parts partial results (o_parts [P][rows][D], lse_parts [P][rows]).
@@ -2002,6 +2014,44 @@ int launch_append_kv(const AppendArgs& a, int dtype, int num_seqs, int num_q_tok
     hipLaunchKernelGGL(append_kv_kernel<uint16_t>, grid, dim3(256), 0, as_stream(stream), a);
   else
     hipLaunchKernelGGL(append_kv_kernel<uint32_t>, grid, dim3(256), 0, as_stream(stream), a);
+  return int(hipGetLastError());
+}
+
+// ---------------------------------------------------------------------------
+// Shared-prefix batches: derive the two passes of the cascade.  Group g (sequences
+// group_start[g] .. group_start[g+1]-1, contiguous, whose block tables agree on their first
+// prefix_len[g] / 16 entries) becomes one sequence of the prefix pass: prefix_len[g] keys (the
+// first member's pages) and all the group's query tokens, every row seeing every key.  Every
+// sequence of the suffix pass keeps its queries and sees its keys from prefix_len onwards.
+// ---------------------------------------------------------------------------
+__global__ void prefix_prep_kernel(PrefixPrep a) {
+  const int64_t tid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t nthreads = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t g = tid; g < a.num_groups; g += nthreads) {
+    const int s0 = a.group_start[g], s1 = a.group_start[g + 1];
+    const int P = a.prefix_len[g];
+    a.pre_seq_lens[g] = P;
+    a.pre_qsl[g] = a.qsl[s0];
+    if (g == a.num_groups - 1) a.pre_qsl[a.num_groups] = a.qsl[s1];
+    for (int j = 0; j < a.max_pages; ++j)
+      a.pre_bt[g * a.max_pages + j] = j < P / kPage ? a.block_table[int64_t(s0) * a.max_pages + j] : -1;
+    for (int s = s0; s < s1; ++s) {
+      a.suf_seq_lens[s] = a.seq_lens[s] - P;
+      a.key_base[s] = P;
+    }
+  }
+  // rows of a group without a shared prefix are never written by the prefix pass: they count as
+  // having seen no key there
+  for (int64_t i = tid; i < a.rows; i += nthreads) a.pre_lse[i] = -INFINITY;
+  for (int64_t i = tid; i < a.rows * a.head_dim; i += nthreads) a.pre_o[i] = 0.f;
+}
+
+int launch_prefix_prep(const PrefixPrep& a, void* stream) {
+  const int64_t work = a.rows * a.head_dim > a.num_groups ? a.rows * a.head_dim : a.num_groups;
+  int64_t grid = (work + 255) / 256;
+  if (grid > 2048) grid = 2048;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(prefix_prep_kernel, dim3(unsigned(grid)), dim3(256), 0, as_stream(stream), a);
   return int(hipGetLastError());
 }
 

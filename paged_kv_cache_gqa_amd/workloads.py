@@ -352,3 +352,79 @@ def to_fp8(w: Workload) -> Workload:
     return Workload(name=w.name + "-fp8kv", dtype="fp8", num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
                     head_dim=w.head_dim, scale=w.scale, seq_lens=w.seq_lens, query_start_loc=w.query_start_loc,
                     block_table=w.block_table, q=q, k_pool=kc, v_pool=vc, meta=meta)
+
+
+def make_shared_prefix(seed: int, group_sizes, prefix_lens, suffix_max: int, max_q: int, num_q_heads: int,
+                       num_kv_heads: int, head_dim: int, dtype: str, suffix_min: int = 1, slack_pages: int = 3,
+                       name: str | None = None) -> Workload:
+    """Groups of sequences that share their first prefix_lens[g] keys (a multiple of 16) as the same
+    physical pages, then a private suffix of suffix_min..suffix_max keys holding the query window
+    (0..max_q tokens, never longer than the suffix).  meta["group_start"] ([G+1], CSR over the
+    sequences) and meta["prefix_len"] ([G]) describe the groups."""
+    rng = np.random.default_rng(seed)
+    group_sizes = [int(g) for g in group_sizes]
+    prefix_lens = [int(p) for p in prefix_lens]
+    assert len(group_sizes) == len(prefix_lens) and all(p % PAGE_SIZE == 0 for p in prefix_lens)
+    suf, ql = [], []
+    for m in group_sizes:
+        for _ in range(m):
+            u = int(rng.integers(suffix_min, suffix_max, endpoint=True))
+            suf.append(u)
+            ql.append(min(u, int(rng.integers(0, max_q, endpoint=True))))
+    used = sum(p // PAGE_SIZE for p in prefix_lens) + sum((u + PAGE_SIZE - 1) // PAGE_SIZE for u in suf)
+    num_pages = used + slack_pages
+    perm = rng.permutation(num_pages).astype(np.int32)
+    lens, rows = [], []
+    cursor, s = 0, 0
+    for m, P in zip(group_sizes, prefix_lens):
+        shared = perm[cursor:cursor + P // PAGE_SIZE]
+        cursor += P // PAGE_SIZE
+        for _ in range(m):
+            own = perm[cursor:cursor + (suf[s] + PAGE_SIZE - 1) // PAGE_SIZE]
+            cursor += len(own)
+            rows.append(np.concatenate([shared, own]))
+            lens.append(P + suf[s])
+            s += 1
+    max_pages = max(len(r) for r in rows)
+    bt = np.full((len(rows), max_pages), -1, dtype=np.int32)
+    for i, r in enumerate(rows):
+        bt[i, :len(r)] = r
+    qsl = np.zeros(len(rows) + 1, dtype=np.int32)
+    qsl[1:] = np.cumsum(ql)
+    d = head_dim
+    q = _draw_normal_bits([seed, 1], int(qsl[-1]) * num_q_heads * d, dtype).reshape(int(qsl[-1]), num_q_heads, d)
+    page_elems = num_kv_heads * PAGE_SIZE * d
+    k = _draw_pool(seed, 2, num_pages, page_elems, dtype).reshape(num_pages, num_kv_heads, PAGE_SIZE, d)
+    v = _draw_pool(seed, 3, num_pages, page_elems, dtype).reshape(num_pages, num_kv_heads, d, PAGE_SIZE)
+    gs = np.zeros(len(group_sizes) + 1, dtype=np.int32)
+    gs[1:] = np.cumsum(group_sizes)
+    meta = {"seed": seed, "pages_used": used, "group_start": gs, "prefix_len": np.array(prefix_lens, dtype=np.int32)}
+    return Workload(name=name or f"shared-prefix-{seed}", dtype=dtype, num_q_heads=num_q_heads,
+                    num_kv_heads=num_kv_heads, head_dim=d, scale=1.0 / math.sqrt(d),
+                    seq_lens=np.array(lens, dtype=np.int32), query_start_loc=qsl, block_table=bt, q=q, k_pool=k,
+                    v_pool=v, meta=meta)
+
+
+def shared_prefix_unique_bytes(w: Workload) -> int:
+    """Bytes a shared-prefix batch must move at least once: every distinct (page, kv head) row of
+    K and V that some sequence reads (the shared prefix once per group), Q, out, LSE and the
+    block-table entries of the prefix pass and of every sequence's suffix."""
+    gs, pl = w.meta["group_start"], w.meta["prefix_len"]
+    n = w.seq_lens.astype(np.int64)
+    hkv, hq, d, eb = w.num_kv_heads, w.num_q_heads, w.head_dim, w.elem_bytes
+    keys = int(pl.astype(np.int64).sum()) + int(sum(n[gs[g]:gs[g + 1]].sum() - (gs[g + 1] - gs[g]) * pl[g]
+                                                   for g in range(len(pl))))
+    tq = w.num_q_tokens
+    pages = int((pl // PAGE_SIZE).sum()) + int(sum(((n[gs[g]:gs[g + 1]] - pl[g] + PAGE_SIZE - 1) // PAGE_SIZE).sum()
+                                                  for g in range(len(pl))))
+    return keys * hkv * d * w.kv_elem_bytes * 2 + 2 * tq * hq * d * eb + 4 * tq * hq + 4 * pages
+
+
+SHARED_PREFIX_NAME = "shared-prefix-decode-bf16"
+
+
+def make_shared_prefix_config(seed: int = 1006) -> Workload:
+    """System-prompt decode: 8 groups of 16 sequences sharing a 4096-token prefix, private suffixes of
+    256..1024 tokens, one query token each; Llama-3-8B attention shape (32 / 8 heads, head dim 128)."""
+    return make_shared_prefix(seed, [16] * 8, [4096] * 8, 1024, 1, 32, 8, 128, "bf16", suffix_min=256,
+                              name=SHARED_PREFIX_NAME)

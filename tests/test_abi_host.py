@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("pa_attention", "pa_attention_tree", "pa_attention_fp8kv", "pa_workspace_size", "pa_workspace_init", "pa_append_kv", "pa_plan", "pa_attention_planned", "pa_merge_planned",
+    for n in ("pa_attention", "pa_attention_tree", "pa_attention_fp8kv", "pa_attention_shared_prefix", "pa_workspace_size", "pa_workspace_init", "pa_append_kv", "pa_plan", "pa_attention_planned", "pa_merge_planned",
               "pa_merge", "pa_gather_kv", "pa_validate", "pa_check_desc", "pa_status_string", "pa_abi_version",
               "pa_plan_read"):
         assert n in names
