@@ -1139,6 +1139,45 @@ __device__ __forceinline__ int block_keys(int n, int qn, int G, int rb, bool ful
   return n - qn + last + 1;
 }
 
+// sum over i in [0, n) of floor((a * i + b) / m), for m > 0 and a * n + b + 2 * m < 2^32: split
+// off the whole parts of a / m and b / m, then count the remaining lattice points under the line
+// from the other axis (the Euclid-like reduction of floor sums; O(log m) rounds).
+__device__ __forceinline__ int64_t floor_sum(uint32_t n, uint32_t m, uint32_t a, uint32_t b) {
+  int64_t s = 0;
+  while (n > 0) {
+    if (a >= m) {
+      s += int64_t(n) * int64_t(n - 1) / 2 * int64_t(a / m);
+      a %= m;
+    }
+    if (b >= m) {
+      s += int64_t(n) * int64_t(b / m);
+      b %= m;
+    }
+    const uint32_t y = a * n + b;
+    if (y < m) break;
+    n = y / m;
+    b = y % m;
+    const uint32_t t = m;
+    m = a;
+    a = t;
+  }
+  return s;
+}
+
+// Chunks of row blocks 0 .. r-1 of a sequence, r < nb (none of them the last block).  Block rb's
+// last row is token floor((128 rb + 127) / G), so it sees keys(rb) = c + floor((128 rb + 127) / G)
+// keys, c = n - qn + 1, and ceil(keys / 32) = floor((128 rb + G (c + 31) + 127) / (32 G)) (a
+// floor of a floor is one floor of the product).  That numerator's constant B splits into
+// 32 G h + b with h = floor((c + 31 + floor(127 / G)) / 32) and 0 <= b < 32 G, which leaves a
+// floor sum over rb with small coefficients.
+__device__ __forceinline__ int64_t block_chunks_before(int n, int qn, int G, bool full, int r) {
+  if (full) return int64_t(r) * ceil_div(n, kChunkKeys);
+  const int x = n - qn + kChunkKeys;  // c + 31
+  const int h = (x + (kBlockRows - 1) / G) / kChunkKeys;
+  const int b = G * (x - kChunkKeys * h) + kBlockRows - 1;
+  return int64_t(r) * h + floor_sum(uint32_t(r), uint32_t(kChunkKeys * G), kBlockRows, uint32_t(b));
+}
+
 struct SeqUnits {
   int n, qn, rows, nb;
   bool split;        // one key-split unit per kv head
@@ -1161,8 +1200,8 @@ __device__ SeqUnits seq_units(int n, int qn, int G, bool full) {
     q.per_head = kCostUnitStart + int64_t(ceil_div(n, kChunkKeys)) * kCostKeySplit;
   } else {
     q.nb = ceil_div(q.rows, kBlockRows);
-    int64_t ch = 0;
-    for (int rb = 0; rb < q.nb; ++rb) ch += ceil_div(block_keys(n, qn, G, rb, full), kChunkKeys);
+    // the last block's last row is the window's last token: it sees all n keys
+    const int64_t ch = block_chunks_before(n, qn, G, full, q.nb - 1) + ceil_div(n, kChunkKeys);
     q.per_head = int64_t(q.nb) * kCostUnitStart + ch * kCostRowSplit;
   }
   return q;
@@ -1175,6 +1214,11 @@ __device__ __forceinline__ int64_t unit_cost(const pa_plan_unit& U) {
 }
 __device__ __forceinline__ int64_t chunk_start(const pa_plan_unit& U, int i) {
   return U.cost0 + kCostUnitStart + int64_t(i) * U.cost_weight;
+}
+
+// Cost from the start of a kv head's row blocks to the start of block rb (rb < nb).
+__device__ __forceinline__ int64_t block_start(const SeqUnits& q, int G, int rb) {
+  return int64_t(rb) * kCostUnitStart + block_chunks_before(q.n, q.qn, G, q.full, rb) * kCostRowSplit;
 }
 
 __device__ pa_plan_unit make_unit(int s, const SeqUnits& q, int G, int g, int rb, int64_t cost0) {
@@ -1217,13 +1261,14 @@ __device__ void cursor_place(UnitCursor& cu, const PlanView& v, int s, int64_t s
   int64_t acc = cu.seq_base + int64_t(cu.g) * cu.q.per_head;
   cu.rb = 0;
   if (!cu.q.split) {
-    for (; cu.rb < cu.q.nb - 1; ++cu.rb) {
-      const int64_t wgt =
-          kCostUnitStart +
-          int64_t(ceil_div(block_keys(cu.q.n, cu.q.qn, v.group, cu.rb, cu.q.full), kChunkKeys)) * kCostRowSplit;
-      if (c < acc + wgt) break;
-      acc += wgt;
+    // the last row block whose start cost is <= c; start costs rise with rb
+    int lo = 0, hi = cu.q.nb - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (acc + block_start(cu.q, v.group, mid) <= c) lo = mid; else hi = mid - 1;
     }
+    cu.rb = lo;
+    acc += block_start(cu.q, v.group, lo);
   }
   cu.U = make_unit(cu.s, cu.q, v.group, cu.g, cu.rb, acc);
 }
