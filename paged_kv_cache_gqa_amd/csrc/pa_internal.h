@@ -42,7 +42,10 @@ constexpr int kCostUnitStart = 12;
 // 128-row unit leaves 64 KiB of partial state to merge).  Grain boundaries --
 // and so every split of a unit's keys and its partial-result slots -- depend
 // only on the batch shape and the grid.
-constexpr int kRowGrainChunks = 8;
+#ifndef PA_ROW_GRAIN_CHUNKS
+#define PA_ROW_GRAIN_CHUNKS 8
+#endif
+constexpr int kRowGrainChunks = PA_ROW_GRAIN_CHUNKS;
 inline __host__ __device__ int64_t grain_count(int64_t ck, int64_t cr, int grid) {
   int64_t s = ck / kCostKeySplit + cr / (int64_t(kRowGrainChunks) * kCostRowSplit);
   if (s > grid) s = grid;
@@ -57,7 +60,8 @@ struct SlotStart {
   int64_t unit_cost0;  // cost at which unit (s, g, rb) starts
   int32_t s, g, rb;
   int32_t n, qn;       // seq_lens[s], query count of s
-  int32_t pad[3];
+  int32_t q0;          // query_start_loc[s]
+  int32_t pad[2];
 };
 
 // Arguments shared by the kernels that walk the plan.

@@ -66,18 +66,27 @@ __device__ __forceinline__ f32x4_t as_f32x4(u32x4_t v) { return __builtin_bit_ca
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = (__bf16)a, y = (__bf16)b;  // v_cvt_pk_bf16_f32, round to nearest even
-  return uint32_t(__builtin_bit_cast(uint16_t, x)) | (uint32_t(__builtin_bit_cast(uint16_t, y)) << 16);
+  // one v_cvt_pk_bf16_f32 (round to nearest even): a in the low half, b in the high half
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
+
+// Maxima of scores and running maxima (never NaN, -inf for masked keys): NaN-propagating maxima,
+// which gfx950 does in one v_maximum3_f32 for up to three operands.  fmaxf would first quiet
+// possible signalling NaNs in every operand the compiler cannot prove canonical -- MFMA results
+// and cross-lane moves -- at one extra instruction per operand.
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float max3(float a, float b, float c) { return max2(max2(a, b), c); }
 
 // Reductions over the 4 lanes (one per quad) that hold the same query row: a
 // butterfly over lane ^ 32 and lane ^ 16 with the gfx950 permlane swaps.
 __device__ __forceinline__ float quad_max(float v) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = max2(__uint_as_float(a[0]), __uint_as_float(a[1]));
   auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max2(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float quad_sum(float v) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -169,6 +178,39 @@ __device__ __forceinline__ void lds_read_b128(const uint32_t (&a)[N], u32x4_t (&
 // operand slot (bf16: 8 values; fp32: 4 values).
 // ---------------------------------------------------------------------------
 
+// V fragments of a bf16 chunk in the LDS ring (head dim D): 2 * D / 16 8-byte reads from one base
+// address, pages at byte 2 * 32 D and 3 * 32 D of the slot, tile t at + 512 t.
+#define PA_V8(P, B, T) "ds_read_b64 %" #P ", %" #B " offset:" #T "\n"
+template <int D>
+__device__ __forceinline__ void lds_read_v_imm(uint32_t base, u32x4_t* vf);
+template <>
+__device__ __forceinline__ void lds_read_v_imm<128>(uint32_t base, u32x4_t* vf) {
+  u32x2_t x[16];
+  asm volatile(PA_V8(0, 16, 8192) PA_V8(1, 16, 12288) PA_V8(2, 16, 8704) PA_V8(3, 16, 12800)
+               PA_V8(4, 16, 9216) PA_V8(5, 16, 13312) PA_V8(6, 16, 9728) PA_V8(7, 16, 13824)
+               PA_V8(8, 16, 10240) PA_V8(9, 16, 14336) PA_V8(10, 16, 10752) PA_V8(11, 16, 14848)
+               PA_V8(12, 16, 11264) PA_V8(13, 16, 15360) PA_V8(14, 16, 11776) PA_V8(15, 16, 15872)
+               "s_waitcnt lgkmcnt(0)"
+               : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]),
+                 "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]), "=&v"(x[12]), "=&v"(x[13]),
+                 "=&v"(x[14]), "=&v"(x[15])
+               : "v"(base));
+#pragma unroll
+  for (int t = 0; t < 8; ++t) vf[t] = u32x4_t{x[2 * t][0], x[2 * t][1], x[2 * t + 1][0], x[2 * t + 1][1]};
+}
+template <>
+__device__ __forceinline__ void lds_read_v_imm<64>(uint32_t base, u32x4_t* vf) {
+  u32x2_t x[8];
+  asm volatile(PA_V8(0, 8, 4096) PA_V8(1, 8, 6144) PA_V8(2, 8, 4608) PA_V8(3, 8, 6656)
+               PA_V8(4, 8, 5120) PA_V8(5, 8, 7168) PA_V8(6, 8, 5632) PA_V8(7, 8, 7680) "s_waitcnt lgkmcnt(0)"
+               : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]),
+                 "=&v"(x[7])
+               : "v"(base));
+#pragma unroll
+  for (int t = 0; t < 4; ++t) vf[t] = u32x4_t{x[2 * t][0], x[2 * t][1], x[2 * t + 1][0], x[2 * t + 1][1]};
+}
+#undef PA_V8
+
 template <int D_>
 struct Bf16 {
   static constexpr int D = D_;
@@ -248,6 +290,14 @@ struct Bf16 {
   template <class RG>
   __device__ static void lds_read_v(const char* slot, int lane, u32x4_t (&vf)[kVF]) {
     const int m = lane & 15, quad = lane >> 4;
+    if constexpr (RG::kPitchV == 32 && RG::kBlk == 32 * D) {
+      // V^T row d = 16 t + m sits at d * 32 bytes with the same swizzled column for every t, so
+      // the 2 * kVF addresses are one per-lane base plus immediate offsets (page 0 at 2 * kBlk,
+      // page 1 at 3 * kBlk, tile t at + 512 t), all read under one wait.
+      const uint32_t base = lds_addr(slot + m * RG::kPitchV + RG::swz_v(m, quad >> 1) * 16 + 8 * (quad & 1));
+      lds_read_v_imm<D>(base, vf);
+      return;
+    }
 #pragma unroll
     for (int t0 = 0; t0 < kVF; t0 += 2) {
       uint32_t a[4];
@@ -482,15 +532,20 @@ struct ChunkPages {
 struct PageIds {
   int a, b;
 };
-__device__ __forceinline__ PageIds page_ids(cptr<int32_t> bt_row, int c, int n_seq) {
+// The block-table loads of chunk c (every lane loads the same two entries) ...
+__device__ __forceinline__ PageIds page_ids_load(cptr<int32_t> bt_row, int c, int n_seq) {
   // both loads unconditional (no wait at a branch join); the second index is clamped to the
   // sequence's last page, so it never reads past the pages the sequence owns
   const bool two = c * kChunkKeys + kPage < n_seq;
   const int ib = two ? 2 * c + 1 : 2 * c;
-  PageIds p;
-  p.a = __builtin_amdgcn_readfirstlane(bt_row[2 * c]);
-  p.b = __builtin_amdgcn_readfirstlane(bt_row[ib]);
-  return p;
+  return PageIds{bt_row[2 * c], bt_row[ib]};
+}
+// ... and their values as wave-uniform page ids (waits for the loads).
+__device__ __forceinline__ PageIds uniform_ids(PageIds p) {
+  return PageIds{__builtin_amdgcn_readfirstlane(p.a), __builtin_amdgcn_readfirstlane(p.b)};
+}
+__device__ __forceinline__ PageIds page_ids(cptr<int32_t> bt_row, int c, int n_seq) {
+  return uniform_ids(page_ids_load(bt_row, c, n_seq));
 }
 
 template <class TR>
@@ -608,11 +663,11 @@ __device__ __forceinline__ void softmax_chunk(State<TR, RT>& st, GetQ getq, cons
         x[j] = vis ? x[j] : -INFINITY;
       }
     }
-    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    float mx = max3(max3(x[0], x[1], x[2]), max3(x[3], x[4], x[5]), max2(x[6], x[7]));
     mx = quad_max(mx);
     const float mx2 = mx == -INFINITY ? -INFINITY : mx * sl2;  // row maximum in the base-2 domain
     if (__any(mx2 > st.m[rt] + kLazy)) {
-      const float m_new = fmaxf(st.m[rt], mx2);
+      const float m_new = max2(st.m[rt], mx2);
       const float alpha = fast_exp2(st.m[rt] - (m_new == -INFINITY ? 0.f : m_new));
       st.l[rt] *= alpha;
 #pragma unroll
@@ -653,6 +708,15 @@ __device__ __forceinline__ void pv_chunk(State<TR, RT>& st, const u32x4_t (&vf)[
 }
 
 // Where the rows of one unit go.
+// One sequence's units: n keys, qn query tokens from row q0, G query heads per kv head.
+struct SeqUnits {
+  int n, qn, rows, nb;
+  int q0;            // row of q / out of the sequence's first query token
+  bool split;        // one key-split unit per kv head
+  bool full;         // every row sees all n keys
+  int64_t per_head;  // cost of one kv head's units
+};
+
 struct RowInfo {
   int tok;    // global query token (row of q / out), valid rows only
   int head;   // query head
@@ -804,15 +868,14 @@ __device__ __forceinline__ void lds_barrier() {
 // Key-split unit (decode / verify, <= 32 rows): wave w takes chunks i0+w, i0+w+4, ...
 // ---------------------------------------------------------------------------
 template <class TR, int RT, bool kTree>
-__device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, int i0, int i1, int part, Smem<TR>& sm) {
+__device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, const SeqUnits& sq, int i0, int i1, int part,
+                             Smem<TR>& sm) {
   int lane = threadIdx.x & 63;
   asm volatile("" : "+v"(lane));  // lane-derived values are recomputed per unit, not held across the unit loop
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int quad = lane >> 4;
   const int s = U.seq;
-  const int n_seq = ro(A.plan.seq_lens)[s];
-  const int q0 = ro(A.plan.qsl)[s];
-  const int qn = ro(A.plan.qsl)[s + 1] - q0;
+  const int n_seq = sq.n, q0 = sq.q0, qn = sq.qn;
   const cptr<int32_t> bt_row = ro(A.block_table) + int64_t(s) * A.max_pages +
                                (A.key_base ? ro(A.key_base)[s] / kPage : 0);
 
@@ -1011,7 +1074,8 @@ __device__ __forceinline__ void ring_step(char* fill, const char* cur, Issue iss
 // chunks ahead of the one being computed; every wave issues 1/4 of each chunk.
 // ---------------------------------------------------------------------------
 template <class TR, bool kTree>
-__device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, int i0, int i1, int part, Smem<TR>& sm) {
+__device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, const SeqUnits& sq, int i0, int i1, int part,
+                             Smem<TR>& sm) {
   using RG = Ring<TR>;
   constexpr int RT = 2;
   int lane = threadIdx.x & 63;
@@ -1019,9 +1083,7 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int quad = lane >> 4;
   const int s = U.seq;
-  const int n_seq = ro(A.plan.seq_lens)[s];
-  const int q0 = ro(A.plan.qsl)[s];
-  const int qn = ro(A.plan.qsl)[s + 1] - q0;
+  const int n_seq = sq.n, q0 = sq.q0, qn = sq.qn;
   const cptr<int32_t> bt_row = ro(A.block_table) + int64_t(s) * A.max_pages +
                                (A.key_base ? ro(A.key_base)[s] / kPage : 0);
   const bool active = 32 * w < U.n_rows;
@@ -1037,6 +1099,11 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
   TreeMask<RT> tm;
   const int mask_from = tree_setup<RT, kTree>(A, ri, n_seq, qn, min_p, tm);
 
+  // Unit start: the page ids of the first kNB chunks are loaded before Q, so that the DMAs of the
+  // first kNB - 1 chunks wait for one round trip only and Q arrives behind them.
+  PageIds ids0[RG::kNB];
+#pragma unroll
+  for (int j = 0; j < RG::kNB; ++j) ids0[j] = page_ids_load(bt_row, min(i0 + j, i1 - 1), n_seq);
   u32x4_t qreg[RT][TR::kQF];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
@@ -1079,9 +1146,9 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, int i0, i
 
 #pragma unroll
   for (int j = 0; j < RG::kNB - 1; ++j)
-    scl[j] = i0 + j < i1 ? issue(page_ids(bt_row, i0 + j, n_seq), ring + j * RG::kChunk) : 0.f;
+    scl[j] = i0 + j < i1 ? issue(uniform_ids(ids0[j]), ring + j * RG::kChunk) : 0.f;
   // page ids of the chunk issued in the next iteration, loaded one iteration ahead
-  PageIds nx = page_ids(bt_row, min(i0 + RG::kNB - 1, i1 - 1), n_seq);
+  PageIds nx = uniform_ids(ids0[RG::kNB - 1]);
   for (int c = i0; c < i1; ++c) {
     const int j = c - i0;
     const int ahead = min(RG::kNB - 2, i1 - 1 - c);  // chunks this wave issued after chunk c
@@ -1178,16 +1245,10 @@ __device__ __forceinline__ int64_t block_chunks_before(int n, int qn, int G, boo
   return int64_t(r) * h + floor_sum(uint32_t(r), uint32_t(kChunkKeys * G), kBlockRows, uint32_t(b));
 }
 
-struct SeqUnits {
-  int n, qn, rows, nb;
-  bool split;        // one key-split unit per kv head
-  bool full;         // every row sees all n keys
-  int64_t per_head;  // cost of one kv head's units
-};
-
-__device__ SeqUnits seq_units(int n, int qn, int G, bool full) {
+__device__ SeqUnits seq_units(int n, int q0, int qn, int G, bool full) {
   SeqUnits q;
   q.n = n;
+  q.q0 = q0;
   q.qn = qn;
   q.full = full;
   q.rows = qn > 0 ? qn * G : 0;
@@ -1247,15 +1308,17 @@ struct UnitCursor {
 
 template <class P>
 __device__ void cursor_load_seq(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl) {
-  cu.q = seq_units(seq_lens[cu.s], qsl[cu.s + 1] - qsl[cu.s], v.group, v.full_rows != 0);
+  const int q0 = qsl[cu.s];
+  cu.q = seq_units(seq_lens[cu.s], q0, qsl[cu.s + 1] - q0, v.group, v.full_rows != 0);
 }
 
-// Position the cursor on the unit of sequence s (n keys, qn queries, starting at cost seq_base)
-// whose cost range holds c.
-__device__ void cursor_place(UnitCursor& cu, const PlanView& v, int s, int64_t seq_base, int n, int qn, int64_t c) {
+// Position the cursor on the unit of sequence s (n keys, queries q0 .. q0 + qn - 1, starting at
+// cost seq_base) whose cost range holds c.
+__device__ void cursor_place(UnitCursor& cu, const PlanView& v, int s, int64_t seq_base, int n, int q0, int qn,
+                             int64_t c) {
   cu.s = s;
   cu.seq_base = seq_base;
-  cu.q = seq_units(n, qn, v.group, v.full_rows != 0);
+  cu.q = seq_units(n, q0, qn, v.group, v.full_rows != 0);
   const int64_t off = c - cu.seq_base;
   cu.g = int(off / cu.q.per_head);
   int64_t acc = cu.seq_base + int64_t(cu.g) * cu.q.per_head;
@@ -1281,7 +1344,8 @@ __device__ void cursor_find(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl
     const int mid = (lo + hi + 1) >> 1;
     if (seq_cost[mid] <= c) lo = mid; else hi = mid - 1;
   }
-  cursor_place(cu, v, lo, seq_cost[lo], seq_lens[lo], qsl[lo + 1] - qsl[lo], c);
+  const int q0 = qsl[lo];
+  cursor_place(cu, v, lo, seq_cost[lo], seq_lens[lo], q0, qsl[lo + 1] - q0, c);
 }
 
 __device__ __forceinline__ SlotStart slot_from_cursor(const UnitCursor& cu, int64_t c0, int64_t c1) {
@@ -1295,7 +1359,8 @@ __device__ __forceinline__ SlotStart slot_from_cursor(const UnitCursor& cu, int6
   r.rb = cu.rb;
   r.n = cu.q.n;
   r.qn = cu.q.qn;
-  r.pad[0] = r.pad[1] = r.pad[2] = 0;
+  r.q0 = cu.q.q0;
+  r.pad[0] = r.pad[1] = 0;
   return r;
 }
 
@@ -1305,7 +1370,7 @@ __device__ __forceinline__ void cursor_from_slot(UnitCursor& cu, const PlanView&
   cu.g = st.g;
   cu.rb = st.rb;
   cu.seq_base = st.seq_base;
-  cu.q = seq_units(st.n, st.qn, v.group, v.full_rows != 0);
+  cu.q = seq_units(st.n, st.q0, st.qn, v.group, v.full_rows != 0);
   cu.U = make_unit(st.s, cu.q, v.group, st.g, st.rb, st.unit_cost0);
 }
 
@@ -1320,6 +1385,7 @@ __device__ __forceinline__ SlotStart load_slot(cptr<SlotStart> p) {
   r.rb = p->rb;
   r.n = p->n;
   r.qn = p->qn;
+  r.q0 = p->q0;
   return r;
 }
 
@@ -1347,7 +1413,7 @@ __device__ bool cursor_next(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl
 // All kThreads threads of the workgroup take part.  A thread takes kInFlight of its rows at a time
 // and loads kPieces pieces of them together before folding them in, in piece order.
 template <class TR, int kInFlight, int kPieces>
-__device__ void merge_unit(const float* part_o, const float* part_lse, void* out, float* out_f32, float* lse,
+__device__ void merge_unit_stream(const float* part_o, const float* part_lse, void* out, float* out_f32, float* lse,
                            cptr<int32_t> qsl, int num_q_heads, int group, const pa_plan_unit& U, int64_t first,
                            int n_pieces) {
   constexpr int kLanesPerRow = TR::D / 4;
@@ -1411,6 +1477,91 @@ __device__ void merge_unit(const float* part_o, const float* part_lse, void* out
   }
 }
 
+// Pieces a unit merge takes in one pass (more go through merge_unit_stream).
+constexpr int kMergeFastPieces = 8;
+
+// Log-sum-exp merge of a split unit's n_pieces partial results (piece j sits in grain first + j:
+// position 1 for j = 0, position 0 after) into out / lse, with every load of a stage in flight
+// at once: first one thread per row loads the row's n_pieces lse values and puts the pieces'
+// weights exp(lse_j - lse) in LDS (wbuf, kMergeFastPieces * kPartRows floats) and writes the
+// merged lse; then every thread folds kP pieces of all its rows per round trip.  All kThreads
+// threads take part.
+template <class TR>
+__device__ void merge_unit(const float* part_o, const float* part_lse, void* out, float* out_f32, float* lse,
+                           cptr<int32_t> qsl, int num_q_heads, int group, const pa_plan_unit& U, int64_t first,
+                           int n_pieces, float* wbuf) {
+  // key-split units (<= 32 rows) take one round trip for up to 4 pieces in the streaming form
+  if (n_pieces > kMergeFastPieces || U.n_rows <= kSplitRows) {
+    merge_unit_stream<TR, 4, 4>(part_o, part_lse, out, out_f32, lse, qsl, num_q_heads, group, U, first, n_pieces);
+    return;
+  }
+  const int q0 = qsl[U.seq];
+  auto pbase = [&](int j) { return uint32_t((2 * (first + j) + (j == 0 ? 1 : 0)) * kPartRows); };
+  auto out_row = [&](int r) {
+    const int rr = U.row0 + r;
+    const int tk = rr / group;
+    return int64_t(q0 + tk) * num_q_heads + U.kv_head * group + (rr - tk * group);
+  };
+  for (int r = threadIdx.x; r < U.n_rows; r += kThreads) {
+    float lj[kMergeFastPieces];
+#pragma unroll
+    for (int j = 0; j < kMergeFastPieces; ++j)
+      lj[j] = j < n_pieces ? load_coherent(part_lse, (pbase(j) + r) * 4) : -INFINITY;
+    float M = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kMergeFastPieces; ++j) M = fmaxf(M, lj[j]);
+    float e[kMergeFastPieces], L = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMergeFastPieces; ++j) {  // a piece that saw no key of this row adds nothing
+      e[j] = lj[j] == -INFINITY ? 0.f : fast_exp2((lj[j] - M) * kLog2e);
+      L += e[j];
+    }
+    // a row that saw no key at all (possible under a tree mask) gets out = 0, lse = -inf
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+    for (int j = 0; j < kMergeFastPieces; ++j)
+      if (j < n_pieces) wbuf[j * kPartRows + r] = e[j] * inv;
+    lse[out_row(r)] = L > 0.f ? M + fast_log2(L) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
+  constexpr int kLanesPerRow = TR::D / 4;
+  constexpr int kRowsPerPass = kThreads / kLanesPerRow;
+  constexpr int kRows = kPartRows / kRowsPerPass;  // rows of each thread
+  constexpr int kP = 32 / kRows;                   // pieces per round trip
+  const int d4 = threadIdx.x % kLanesPerRow, r0 = threadIdx.x / kLanesPerRow;
+  f32x4_t acc[kRows];
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < n_pieces; j0 += kP) {
+    f32x4_t oj[kP][kRows];
+#pragma unroll
+    for (int p = 0; p < kP; ++p)
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) {
+        const int r = r0 + i * kRowsPerPass;
+        oj[p][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (j0 + p < n_pieces && r < U.n_rows)
+          oj[p][i] = load_coherent4(part_o, ((pbase(j0 + p) + r) * TR::D + 4 * d4) * 4);
+      }
+#pragma unroll
+    for (int p = 0; p < kP; ++p)
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) {
+        const int r = r0 + i * kRowsPerPass;
+        if (j0 + p < n_pieces && r < U.n_rows) acc[i] += oj[p][i] * wbuf[(j0 + p) * kPartRows + r];
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    const int r = r0 + i * kRowsPerPass;
+    if (r >= U.n_rows) continue;
+    const int64_t orow = out_row(r);
+    if (out_f32) *reinterpret_cast<f32x4_t*>(out_f32 + orow * TR::D + 4 * d4) = acc[i];
+    else TR::store_out(static_cast<char*>(out) + (orow * TR::D + 4 * d4) * TR::kEb, acc[i]);
+  }
+  __syncthreads();  // wbuf is read by every thread before the caller reuses LDS
+}
+
 // Grains holding the first and the last chunk of a unit.
 __device__ __forceinline__ int64_t first_grain(const pa_plan_unit& U, int64_t S, int64_t C) {
   return slot_of(chunk_start(U, 0), S, C);
@@ -1424,7 +1575,8 @@ __device__ __forceinline__ int64_t last_grain(const pa_plan_unit& U, int64_t S, 
 // The pieces are agent-coherent stores that have completed (vmcnt(0)) before the count, and the
 // merging workgroup reads them with agent-coherent loads issued after it saw the count.
 template <class TR>
-__device__ void arrive_and_merge(const AttnArgs& A, const pa_plan_unit& U, int64_t S, int64_t C, int* flag) {
+__device__ void arrive_and_merge(const AttnArgs& A, const pa_plan_unit& U, int64_t S, int64_t C, int* flag,
+                                 float* wbuf) {
   const int64_t first = first_grain(U, S, C);
   const int n_pieces = int(last_grain(U, S, C) - first + 1);
   wait_all_loads();  // this wave's partial stores are done
@@ -1437,8 +1589,8 @@ __device__ void arrive_and_merge(const AttnArgs& A, const pa_plan_unit& U, int64
   const bool last = *flag;
   __syncthreads();  // flag read by every thread before it is reused
   if (!last) return;
-  merge_unit<TR, 4, 4>(A.part_o, A.part_lse, A.out, A.out_f32, A.lse, ro(A.plan.qsl), A.num_q_heads, A.plan.group,
-                       U, first, n_pieces);
+  merge_unit<TR>(A.part_o, A.part_lse, A.out, A.out_f32, A.lse, ro(A.plan.qsl), A.num_q_heads, A.plan.group, U,
+                 first, n_pieces, wbuf);
   if (threadIdx.x == 0) __hip_atomic_store(A.arrive + first, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -1468,13 +1620,13 @@ __device__ void run_grain(const AttnArgs& A, int grain, const SlotStart& st, int
       // and the one it ends inside (position 1)
       const int part = (i0 > 0 || i1 < U.n_chunks) ? 2 * grain + (cs < c0 ? 0 : 1) : -1;
       if (U.kind == 0) {
-        if (U.n_rows <= 16) run_keysplit<TR, 1, kTree>(A, U, i0, i1, part, sm);
-        else run_keysplit<TR, 2, kTree>(A, U, i0, i1, part, sm);
+        if (U.n_rows <= 16) run_keysplit<TR, 1, kTree>(A, U, cu.q, i0, i1, part, sm);
+        else run_keysplit<TR, 2, kTree>(A, U, cu.q, i0, i1, part, sm);
       } else {
-        run_rowsplit<TR, kTree>(A, U, i0, i1, part, sm);
+        run_rowsplit<TR, kTree>(A, U, cu.q, i0, i1, part, sm);
       }
       if constexpr (kFused) {
-        if (part >= 0) arrive_and_merge<TR>(A, U, S, C, flag);
+        if (part >= 0) arrive_and_merge<TR>(A, U, S, C, flag, reinterpret_cast<float*>(sm.buf));
       }
     }
   } while (cursor_next(cu, v, seq_lens, qsl));
@@ -1535,17 +1687,19 @@ struct PreLds {
 // Cost of the kPreSeqs sequences of this thread in the block of kThreads * kPreSeqs at `base`
 // (c), and the part of their sum that is row-split work (returned).
 __device__ __forceinline__ int64_t block_seq_costs(const PlanView& v, cptr<int32_t> sl, cptr<int32_t> qsl, int base,
-                                                   int64_t (&c)[kPreSeqs], int (&n)[kPreSeqs], int (&qn)[kPreSeqs]) {
+                                                   int64_t (&c)[kPreSeqs], int (&n)[kPreSeqs], int (&q0)[kPreSeqs],
+                                                   int (&qn)[kPreSeqs]) {
   int64_t row = 0;
 #pragma unroll
   for (int e = 0; e < kPreSeqs; ++e) {
     const int s = base + threadIdx.x * kPreSeqs + e;
-    n[e] = qn[e] = 0;
+    n[e] = q0[e] = qn[e] = 0;
     c[e] = 0;
     if (s < v.num_seqs) {
       n[e] = sl[s];
-      qn[e] = qsl[s + 1] - qsl[s];
-      const SeqUnits q = seq_units(n[e], qn[e], v.group, v.full_rows != 0);
+      q0[e] = qsl[s];
+      qn[e] = qsl[s + 1] - q0[e];
+      const SeqUnits q = seq_units(n[e], q0[e], qn[e], v.group, v.full_rows != 0);
       c[e] = int64_t(v.num_kv_heads) * q.per_head;
       if (!q.split) row += c[e];
     }
@@ -1565,13 +1719,13 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fused_kernel(AttnArgs A
   const cptr<int32_t> sl = ro(v.seq_lens), qsl = ro(v.qsl);
   constexpr int kBlock = kThreads * kPreSeqs;
   int64_t c[kPreSeqs];
-  int n[kPreSeqs], qn[kPreSeqs];
-  const int64_t row0 = block_seq_costs(v, sl, qsl, 0, c, n, qn);  // kept for the search when B <= kBlock
+  int n[kPreSeqs], q0[kPreSeqs], qn[kPreSeqs];
+  const int64_t row0 = block_seq_costs(v, sl, qsl, 0, c, n, q0, qn);  // kept for the search when B <= kBlock
   int64_t C = 0, Cr = 0;
   for (int base = 0; base < v.num_seqs; base += kBlock) {
     int64_t c2[kPreSeqs];
-    int n2[kPreSeqs], qn2[kPreSeqs];
-    const int64_t row = base > 0 ? block_seq_costs(v, sl, qsl, base, c2, n2, qn2) : row0;
+    int n2[kPreSeqs], q02[kPreSeqs], qn2[kPreSeqs];
+    const int64_t row = base > 0 ? block_seq_costs(v, sl, qsl, base, c2, n2, q02, qn2) : row0;
     int64_t x = 0;
 #pragma unroll
     for (int e = 0; e < kPreSeqs; ++e) x += base > 0 ? c2[e] : c[e];
@@ -1584,7 +1738,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fused_kernel(AttnArgs A
   const int64_t c0 = slice_begin(k, S, C), c1 = slice_begin(k + 1, S, C);
   int64_t carry = 0;
   for (int base = 0; base < v.num_seqs; base += kBlock) {
-    if (base > 0) block_seq_costs(v, sl, qsl, base, c, n, qn);
+    if (base > 0) block_seq_costs(v, sl, qsl, base, c, n, q0, qn);
     int64_t x = 0;
 #pragma unroll
     for (int e = 0; e < kPreSeqs; ++e) x += c[e];
@@ -1595,7 +1749,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fused_kernel(AttnArgs A
       for (int e = 0; e < kPreSeqs; ++e) {
         if (c0 >= pre && c0 < pre + c[e]) {
           UnitCursor cu;
-          cursor_place(cu, v, base + int(threadIdx.x) * kPreSeqs + e, pre, n[e], qn[e], c0);
+          cursor_place(cu, v, base + int(threadIdx.x) * kPreSeqs + e, pre, n[e], q0[e], qn[e], c0);
           pl.st = slot_from_cursor(cu, c0, c1);
         }
         pre += c[e];
@@ -1653,7 +1807,7 @@ __global__ __launch_bounds__(kScanThreads) void plan_kernel(PlanArgs a) {
     int64_t cost = 0, nu = 0;
     bool split = true;
     if (s < a.num_seqs) {
-      const SeqUnits q = seq_units(a.seq_lens[s], a.qsl[s + 1] - a.qsl[s], a.group, a.full_rows != 0);
+      const SeqUnits q = seq_units(a.seq_lens[s], 0, a.qsl[s + 1] - a.qsl[s], a.group, a.full_rows != 0);
       cost = int64_t(a.num_kv_heads) * q.per_head;
       nu = int64_t(a.num_kv_heads) * q.nb;
       split = q.split;
@@ -1760,8 +1914,9 @@ __global__ __launch_bounds__(kThreads) void merge_planned_kernel(MergeArgs a) {
   const int64_t first = first_grain(U, S, C);
   const int64_t last = last_grain(U, S, C);
   if (first != k - 1 || last < k) return;  // boundary k does not open this unit's split
-  merge_unit<TR, 4, 4>(a.part_o, a.part_lse, a.out, nullptr, a.lse, ro(v.qsl), a.num_q_heads, v.group, U, first,
-                       int(last - first + 1));
+  __shared__ float wbuf[kMergeFastPieces * kPartRows];
+  merge_unit<TR>(a.part_o, a.part_lse, a.out, nullptr, a.lse, ro(v.qsl), a.num_q_heads, v.group, U, first,
+                 int(last - first + 1), wbuf);
 }
 
 // Stand-alone merge: rows of n_parts partial results (o_parts [P][rows][D], lse_parts [P][rows]).
