@@ -1598,7 +1598,7 @@ __device__ void arrive_and_merge(const AttnArgs& A, const pa_plan_unit& U, int64
 // single-launch kernel (S grains over total cost C; split units are merged here), else the staged
 // kernel (split units are left as partial results for the merge kernel).
 template <class TR, bool kFused, bool kTree>
-__device__ void run_grain(const AttnArgs& A, int grain, const SlotStart& st, int64_t S, int64_t C, Smem<TR>& sm,
+__device__ __forceinline__ void run_grain(const AttnArgs& A, int grain, const SlotStart& st, int64_t S, int64_t C, Smem<TR>& sm,
                           int* flag) {
   const PlanView& v = A.plan;
   const int64_t c0 = st.c0, c1 = st.c1;
@@ -1642,7 +1642,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs A) {
 }
 
 // Sums and scans of one int64 per thread over the kThreads threads of a workgroup.
-__device__ int64_t wg_sum(int64_t x, int64_t* red) {
+__device__ __forceinline__ int64_t wg_sum(int64_t x, int64_t* red) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
@@ -1654,7 +1654,7 @@ __device__ int64_t wg_sum(int64_t x, int64_t* red) {
   __syncthreads();
   return t;
 }
-__device__ int64_t wg_exclusive_scan(int64_t x, int64_t* red, int64_t* total) {
+__device__ __forceinline__ int64_t wg_exclusive_scan(int64_t x, int64_t* red, int64_t* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   int64_t incl = x;
 #pragma unroll
