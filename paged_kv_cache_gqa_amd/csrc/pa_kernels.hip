@@ -1707,6 +1707,19 @@ __device__ __forceinline__ int64_t block_seq_costs(const PlanView& v, cptr<int32
   return row;
 }
 
+// Grain run by workgroup b of a grid of `grid` (S <= grid grains; S or more means none).
+// Workgroups are dealt to the 8 XCDs (each with its own L2) round-robin, so workgroup b runs on
+// XCD b % 8; grains adjacent on the cost axis -- the units of one sequence, which read the same
+// K/V pages, and the pieces of one split unit -- go to one XCD: with n = ceil(S / 8), XCD x runs
+// grains x * n .. x * n + n - 1.  Any placement is correct (grains are independent and pieces are
+// exchanged coherently); this one keeps a sequence's pages in one L2.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int64_t grain_of_block(int b, int grid, int64_t S) {
+  if (grid % kXcds != 0) return b;
+  const int64_t n = (S + kXcds - 1) / kXcds, j = b / kXcds;
+  return j < n ? int64_t(b % kXcds) * n + j : S;
+}
+
 // Single launch.  Every workgroup derives the plan's total cost C and grain count S from
 // seq_lens and query_start_loc (the same numbers the staged planner writes), finds where its grain
 // starts with a workgroup-wide scan of the per-sequence costs, then runs the grain and merges the
@@ -1733,7 +1746,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fused_kernel(AttnArgs A
     Cr += wg_sum(row, pl.red);
   }
   const int64_t S = grain_count(C - Cr, Cr, int(gridDim.x));
-  const int64_t k = blockIdx.x;
+  const int64_t k = grain_of_block(int(blockIdx.x), int(gridDim.x), S);
   if (k >= S) return;
   const int64_t c0 = slice_begin(k, S, C), c1 = slice_begin(k + 1, S, C);
   int64_t carry = 0;
