@@ -104,7 +104,7 @@ pa_status pa_check_desc(const pa_desc* desc);
 /*
  * Bytes of device workspace pa_attention needs for `desc` on the current HIP
  * device (per workgroup of the persistent launch: an arrival counter and room
- * for two partial results of up to 128 rows; the staged plan).  The size
+ * for two partial results of up to 64 rows; the staged plan).  The size
  * depends only on the descriptor and on the device's compute-unit count.
  * Writes *bytes; returns PA_ERR_NULL_POINTER, a descriptor error or PA_ERR_HIP.
  *
@@ -231,11 +231,11 @@ pa_status pa_merge_planned(const pa_desc* desc, const int32_t* seq_lens, const i
  * `kv_head` (row index = window token * (Hq/Hkv) + head within the group)
  * against keys [0, n_keys), cut into ceil(n_keys / 32) chunks of 32 keys.
  * Units lie on one cost axis in (sequence, kv head, row block) order (cost0 =
- * prefix of n_chunks * cost_weight); the persistent launch's workgroup k takes
- * the chunks whose start lies in [floor(k*C/S), floor((k+1)*C/S)), C =
- * total_cost, S = n_slots.  kind 0: rows <= 32, the four waves of a workgroup
- * split the chunks; kind 1: rows <= 128, each wave takes 32 rows and the
- * chunks are shared.  n_pieces > 1 means the unit's chunks fall into slots
+ * prefix of n_chunks * cost_weight); grain k -- run by one workgroup of the
+ * persistent launch -- takes the chunks whose start lies in
+ * [floor(k*C/S), floor((k+1)*C/S)), C = total_cost, S = n_slots.  kind 0:
+ * rows <= 32, the four waves of a workgroup split the chunks; kind 1:
+ * rows <= 64, each wave takes 16 rows and the chunks are shared.  n_pieces > 1 means the unit's chunks fall into slots
  * first_slot .. first_slot + n_pieces - 1 and their partial results are merged.
  */
 typedef struct pa_plan_unit {

@@ -14,16 +14,27 @@ constexpr int kChunkKeys = 32;       // keys per chunk = two pages = one 16x16x3
 constexpr int kWaves = 4;            // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSplitRows = 32;       // a unit with <= 32 rows splits its chunks across the 4 waves
-constexpr int kBlockRows = 128;      // a larger unit is cut into blocks of 4 waves x 32 rows
+// Row tiles (16 rows) of each wave in a row-split unit.  One (64-row units) measured 14% faster
+// on prefill windows than two: twice the units means half the pieces per split unit, so half
+// the partial results written and merged, which outweighs the K/V fragments read per MFMA.
+#ifndef PA_ROW_TILES
+#define PA_ROW_TILES 1
+#endif
+constexpr int kRowTiles = PA_ROW_TILES;
+constexpr int kBlockRows = 64 * kRowTiles;  // a larger unit is cut into blocks of 4 waves x 16 kRowTiles rows
 constexpr int kPlanThreads = 1024;
 
 // Cost weights per 32-key chunk on the planner's balancing axis, fitted to
-// measured wall time on MI355X: a chunk of a row-split unit (prefill: up to 128
-// rows of MFMA work on one chunk staged in LDS) takes a little longer than a
-// chunk of a key-split unit (decode / verify: one wave streams 8 KiB of K and
-// 8 KiB of V from HBM for a few rows).
+// measured wall time on MI355X (mixed prefill + decode batch): a chunk of a
+// row-split unit (prefill: up to 64 rows of MFMA work on one chunk staged in
+// LDS) takes about as long as a chunk of a key-split unit (decode / verify:
+// one wave streams 8 KiB of K and 8 KiB of V from HBM for a few rows).  With
+// 128-row units (two row tiles per wave) the row-split weight was 5.
 constexpr int kCostKeySplit = 4;
-constexpr int kCostRowSplit = 5;
+#ifndef PA_COST_ROW
+#define PA_COST_ROW (kRowTiles == 1 ? 4 : 5)
+#endif
+constexpr int kCostRowSplit = PA_COST_ROW;
 // Fixed cost charged at the start of every unit (row and page-table loads, the
 // pipeline fill), so that grains that start many units get fewer chunks.
 constexpr int kCostUnitStart = 12;

@@ -32,7 +32,7 @@
 //  * Decode/verify units (<= 32 rows) let the 4 waves take alternate chunks and
 //    merge in LDS.  Each wave keeps one chunk in flight: V straight to
 //    registers, K (bf16) by global->LDS DMA into the wave's own slot.  Prefill
-//    units (<= 128 rows) give each wave 32 rows; the 4 waves DMA the 4 page
+//    units (<= 64 rows) give each wave 16 rows; the 4 waves DMA the 4 page
 //    blocks of a chunk into a ring of LDS slots shared by all of them (XOR-
 //    swizzled rows, so the MFMA fragment reads are conflict-free).
 #include <hip/hip_runtime.h>
@@ -1069,7 +1069,7 @@ __device__ __forceinline__ void ring_step(char* fill, const char* cur, Issue iss
 }
 
 // ---------------------------------------------------------------------------
-// Row-split unit (prefill, <= 128 rows): wave w owns rows [32w, 32w+32).  The
+// Row-split unit (prefill, <= 64 rows): wave w owns rows [16w, 16w+16).  The
 // workgroup streams chunks through an LDS ring with global->LDS DMA, kNB - 1
 // chunks ahead of the one being computed; every wave issues 1/4 of each chunk.
 // ---------------------------------------------------------------------------
@@ -1077,7 +1077,8 @@ template <class TR, bool kTree>
 __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, const SeqUnits& sq, int i0, int i1, int part,
                              Smem<TR>& sm) {
   using RG = Ring<TR>;
-  constexpr int RT = 2;
+  constexpr int RT = kRowTiles;
+  constexpr int kWaveRows = 16 * RT;  // rows of each wave
   int lane = threadIdx.x & 63;
   asm volatile("" : "+v"(lane));  // lane-derived values are recomputed per unit, not held across the unit loop
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1086,16 +1087,16 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, const Seq
   const int n_seq = sq.n, q0 = sq.q0, qn = sq.qn;
   const cptr<int32_t> bt_row = ro(A.block_table) + int64_t(s) * A.max_pages +
                                (A.key_base ? ro(A.key_base)[s] / kPage : 0);
-  const bool active = 32 * w < U.n_rows;
+  const bool active = kWaveRows * w < U.n_rows;
 
   RowInfo ri[RT];
   int p_row[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    ri[rt] = row_info(A, U, 32 * w + 16 * rt + (lane & 15), n_seq, q0, qn);
+    ri[rt] = row_info(A, U, kWaveRows * w + 16 * rt + (lane & 15), n_seq, q0, qn);
     p_row[rt] = ri[rt].p;
   }
-  const int min_p = A.plan.full_rows ? n_seq - 1 : n_seq - qn + (U.row0 + 32 * w) / A.plan.group;
+  const int min_p = A.plan.full_rows ? n_seq - 1 : n_seq - qn + (U.row0 + kWaveRows * w) / A.plan.group;
   TreeMask<RT> tm;
   const int mask_from = tree_setup<RT, kTree>(A, ri, n_seq, qn, min_p, tm);
 
@@ -1179,7 +1180,7 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, const Seq
       const float lse_nat = l > 0.f ? (st.m[rt] + fast_log2(l)) * kLn2 : -INFINITY;
 #pragma unroll
       for (int t = 0; t < TR::kTiles; ++t)
-        emit<TR>(A, ri[rt], 32 * w + 16 * rt + (lane & 15), part, t, quad, st.o[rt][t] * inv, lse_nat,
+        emit<TR>(A, ri[rt], kWaveRows * w + 16 * rt + (lane & 15), part, t, quad, st.o[rt][t] * inv, lse_nat,
                  t == 0 && quad == 0);
     }
   }
@@ -1191,7 +1192,7 @@ __device__ __forceinline__ int64_t slice_begin(int64_t k, int64_t S, int64_t C) 
 
 // ---------------------------------------------------------------------------
 // The plan.  Sequence s contributes Hkv groups of nb units (nb = 1 when its
-// q_len * G rows fit one key-split unit, else ceil(rows / 128) row blocks);
+// q_len * G rows fit one key-split unit, else ceil(rows / kBlockRows) row blocks);
 // units are ordered (sequence, kv head, row block) on one cost axis.  Only the
 // per-sequence cost prefix is stored; units are rebuilt from it on the fly.
 // ---------------------------------------------------------------------------
@@ -1231,12 +1232,12 @@ __device__ __forceinline__ int64_t floor_sum(uint32_t n, uint32_t m, uint32_t a,
   return s;
 }
 
-// Chunks of row blocks 0 .. r-1 of a sequence, r < nb (none of them the last block).  Block rb's
-// last row is token floor((128 rb + 127) / G), so it sees keys(rb) = c + floor((128 rb + 127) / G)
-// keys, c = n - qn + 1, and ceil(keys / 32) = floor((128 rb + G (c + 31) + 127) / (32 G)) (a
-// floor of a floor is one floor of the product).  That numerator's constant B splits into
-// 32 G h + b with h = floor((c + 31 + floor(127 / G)) / 32) and 0 <= b < 32 G, which leaves a
-// floor sum over rb with small coefficients.
+// Chunks of row blocks 0 .. r-1 of a sequence, r < nb (none of them the last block).  With
+// R = kBlockRows rows per block, block rb's last row is token floor((R rb + R - 1) / G), so it sees
+// keys(rb) = c + floor((R rb + R - 1) / G) keys, c = n - qn + 1, and ceil(keys / 32) =
+// floor((R rb + G (c + 31) + R - 1) / (32 G)) (a floor of a floor is one floor of the product).
+// That numerator's constant B splits into 32 G h + b with h = floor((c + 31 + floor((R - 1) / G))
+// / 32) and 0 <= b < 32 G, which leaves a floor sum over rb with small coefficients.
 __device__ __forceinline__ int64_t block_chunks_before(int n, int qn, int G, bool full, int r) {
   if (full) return int64_t(r) * ceil_div(n, kChunkKeys);
   const int x = n - qn + kChunkKeys;  // c + 31

@@ -45,7 +45,7 @@ CASES = [
     # seed, B, max_len, Hq, Hkv, D, max_q
     (111, 7, 900, 32, 8, 128, 1),     # decode: key-split units
     (112, 6, 700, 32, 8, 128, 5),     # verify windows
-    (113, 4, 800, 8, 1, 128, 300),    # prefill chunks: 128-row units through the LDS ring
+    (113, 4, 800, 8, 1, 128, 300),    # prefill chunks: 64-row units through the LDS ring
     (114, 9, 300, 8, 2, 64, 20),
     (115, 5, 500, 64, 8, 128, 1),
 ]

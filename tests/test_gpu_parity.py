@@ -236,9 +236,10 @@ def test_gather_kv_bit_exact(dt, D):
 
 def cpu_plan(w, grid):
     """The plan's units re-derived on the CPU from the stated rules (sequence, kv head, row block order;
-    key-split units for q_len*G <= 32 rows, else 128-row blocks; a unit costs 12 + chunks * weight
-    (weight 4 key-split, 5 row-split) and its chunk i starts at cost0 + 12 + i * weight; the cost axis
-    is cut into min(grid, key-split cost // 4 + row-split cost // 40) equal grains, one per workgroup)."""
+    key-split units for q_len*G <= 32 rows, else 64-row blocks; a unit costs 12 + chunks * weight
+    (weight 4 for both kinds) and its chunk i starts at cost0 + 12 + i * weight; the cost axis
+    is cut into min(grid, key-split cost // 4 + row-split cost // 32) equal grains, one per workgroup)."""
+    BLOCK, W_ROW = 64, 4
     G = w.num_q_heads // w.num_kv_heads
     units, cost, row_cost = [], 0, 0
     for s in range(w.num_seqs):
@@ -247,19 +248,19 @@ def cpu_plan(w, grid):
             continue
         rows = qn * G
         split = rows <= 32
-        nb = 1 if split else -(-rows // 128)
+        nb = 1 if split else -(-rows // BLOCK)
         for g in range(w.num_kv_heads):
             for rb in range(nb):
-                r0 = 0 if split else rb * 128
-                nr = rows if split else min(128, rows - r0)
+                r0 = 0 if split else rb * BLOCK
+                nr = rows if split else min(BLOCK, rows - r0)
                 nk = n if split else n - qn + (r0 + nr - 1) // G + 1
                 nch = -(-nk // 32)
-                wgt = 4 if split else 5
+                wgt = 4 if split else W_ROW
                 units.append(dict(seq=s, kv_head=g, row0=r0, n_rows=nr, n_keys=nk, n_chunks=nch,
                                   kind=0 if split else 1, cost_weight=wgt, cost0=cost))
                 cost += 12 + nch * wgt
                 row_cost += 0 if split else 12 + nch * wgt
-    S = max(1, min(grid, (cost - row_cost) // 4 + row_cost // 40))
+    S = max(1, min(grid, (cost - row_cost) // 4 + row_cost // (8 * W_ROW)))
     bounds = [k * cost // S for k in range(S + 1)]
     for u in units:
         owners = [bisect.bisect_right(bounds, u["cost0"] + 12 + i * u["cost_weight"]) - 1

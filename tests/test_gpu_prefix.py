@@ -46,7 +46,7 @@ CASES = [
     # seed, group sizes, prefix lens, suffix max, max q, Hq, Hkv, D, dtype
     (121, [3, 1, 4, 2], [64, 0, 128, 16], 200, 5, 8, 2, 64, "f32"),
     (122, [5, 3], [512, 256], 300, 1, 32, 8, 128, "bf16"),      # decode groups: key-split prefix units
-    (123, [2, 3], [512, 1024], 400, 300, 8, 1, 128, "bf16"),    # prefill windows: 128-row units in both passes
+    (123, [2, 3], [512, 1024], 400, 300, 8, 1, 128, "bf16"),    # prefill windows: 64-row units in both passes
     (124, [16], [2048], 500, 4, 32, 8, 128, "bf16"),            # one big group, verify-sized windows
     (125, [1, 1, 1, 1], [0, 0, 0, 0], 300, 6, 12, 3, 64, "bf16"),  # no sharing at all
 ]

@@ -55,7 +55,7 @@ def test_causal_masks_equal_plain_attention_bitwise():
 CASES = [
     # seed, B, max_len, Hq, Hkv, D, dtype, max_q
     (92, 12, 900, 32, 8, 128, "bf16", 5),    # verify windows: key-split units (q * G <= 32)
-    (93, 6, 700, 8, 1, 128, "bf16", 64),     # up to 64-token trees: 128-row units
+    (93, 6, 700, 8, 1, 128, "bf16", 64),     # up to 64-token trees: 64-row units
     (94, 7, 300, 8, 2, 64, "f32", 16),
     (95, 5, 400, 12, 3, 64, "bf16", 100),    # some windows longer than 64: causal there
 ]
