@@ -1655,6 +1655,27 @@ __device__ __forceinline__ int64_t wg_sum(int64_t x, int64_t* red) {
   __syncthreads();
   return t;
 }
+// Both sums of two int64 per thread, with one exchange through LDS (red: 2 * kWaves slots).
+__device__ __forceinline__ void wg_sum2(int64_t x, int64_t y, int64_t* red, int64_t& sx, int64_t& sy) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    x += __shfl_xor(x, off);
+    y += __shfl_xor(y, off);
+  }
+  if (lane == 0) {
+    red[wid] = x;
+    red[kWaves + wid] = y;
+  }
+  __syncthreads();
+  sx = sy = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    sx += red[i];
+    sy += red[kWaves + i];
+  }
+  __syncthreads();
+}
 __device__ __forceinline__ int64_t wg_exclusive_scan(int64_t x, int64_t* red, int64_t* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   int64_t incl = x;
@@ -1676,24 +1697,22 @@ __device__ __forceinline__ int64_t wg_exclusive_scan(int64_t x, int64_t* red, in
   return incl - x + before;
 }
 
-// Sequences per thread in one pass of the in-kernel planner.
-constexpr int kPreSeqs = 4;
-
 struct PreLds {
-  int64_t red[kWaves];
+  int64_t red[2 * kWaves];
   SlotStart st;
   int flag;
 };
 
-// Cost of the kPreSeqs sequences of this thread in the block of kThreads * kPreSeqs at `base`
+// Cost of the kPer sequences of this thread in the block of kThreads * kPer at `base`
 // (c), and the part of their sum that is row-split work (returned).
+template <int kPer>
 __device__ __forceinline__ int64_t block_seq_costs(const PlanView& v, cptr<int32_t> sl, cptr<int32_t> qsl, int base,
-                                                   int64_t (&c)[kPreSeqs], int (&n)[kPreSeqs], int (&q0)[kPreSeqs],
-                                                   int (&qn)[kPreSeqs]) {
+                                                   int64_t (&c)[kPer], int (&n)[kPer], int (&q0)[kPer],
+                                                   int (&qn)[kPer]) {
   int64_t row = 0;
 #pragma unroll
-  for (int e = 0; e < kPreSeqs; ++e) {
-    const int s = base + threadIdx.x * kPreSeqs + e;
+  for (int e = 0; e < kPer; ++e) {
+    const int s = base + threadIdx.x * kPer + e;
     n[e] = q0[e] = qn[e] = 0;
     c[e] = 0;
     if (s < v.num_seqs) {
@@ -1721,49 +1740,51 @@ __device__ __forceinline__ int64_t grain_of_block(int b, int grid, int64_t S) {
   return j < n ? int64_t(b % kXcds) * n + j : S;
 }
 
-// Single launch.  Every workgroup derives the plan's total cost C and grain count S from
-// seq_lens and query_start_loc (the same numbers the staged planner writes), finds where its grain
-// starts with a workgroup-wide scan of the per-sequence costs, then runs the grain and merges the
-// split units it completes.
-template <class TR, bool kTree>
-__global__ __launch_bounds__(kThreads, 2) void attention_fused_kernel(AttnArgs A) {
-  __shared__ Smem<TR> sm;
-  __shared__ PreLds pl;
-  const PlanView& v = A.plan;
+// The single launch's plan, in every workgroup: the total cost C and the grain count S from
+// seq_lens and query_start_loc (the same numbers the staged planner writes), then -- for this
+// workgroup's grain, found with a workgroup-wide scan of the per-sequence costs -- the grain's
+// start in pl.st.  Each thread takes kPer sequences per pass of kThreads * kPer (one when the
+// batch fits one pass, so that no thread computes several sequences' costs in a row).  Returns
+// the grain index; S or more means the workgroup has none.
+template <int kPer>
+__device__ __forceinline__ int64_t plan_grain(const PlanView& v, PreLds& pl, int64_t& S, int64_t& C) {
   const cptr<int32_t> sl = ro(v.seq_lens), qsl = ro(v.qsl);
-  constexpr int kBlock = kThreads * kPreSeqs;
-  int64_t c[kPreSeqs];
-  int n[kPreSeqs], q0[kPreSeqs], qn[kPreSeqs];
-  const int64_t row0 = block_seq_costs(v, sl, qsl, 0, c, n, q0, qn);  // kept for the search when B <= kBlock
-  int64_t C = 0, Cr = 0;
+  constexpr int kBlock = kThreads * kPer;
+  int64_t c[kPer];
+  int n[kPer], q0[kPer], qn[kPer];
+  const int64_t row0 = block_seq_costs<kPer>(v, sl, qsl, 0, c, n, q0, qn);  // kept for the search below
+  C = 0;
+  int64_t Cr = 0;
   for (int base = 0; base < v.num_seqs; base += kBlock) {
-    int64_t c2[kPreSeqs];
-    int n2[kPreSeqs], q02[kPreSeqs], qn2[kPreSeqs];
-    const int64_t row = base > 0 ? block_seq_costs(v, sl, qsl, base, c2, n2, q02, qn2) : row0;
+    int64_t c2[kPer];
+    int n2[kPer], q02[kPer], qn2[kPer];
+    const int64_t row = base > 0 ? block_seq_costs<kPer>(v, sl, qsl, base, c2, n2, q02, qn2) : row0;
     int64_t x = 0;
 #pragma unroll
-    for (int e = 0; e < kPreSeqs; ++e) x += base > 0 ? c2[e] : c[e];
-    C += wg_sum(x, pl.red);
-    Cr += wg_sum(row, pl.red);
+    for (int e = 0; e < kPer; ++e) x += base > 0 ? c2[e] : c[e];
+    int64_t sx, sy;
+    wg_sum2(x, row, pl.red, sx, sy);
+    C += sx;
+    Cr += sy;
   }
-  const int64_t S = grain_count(C - Cr, Cr, int(gridDim.x));
+  S = grain_count(C - Cr, Cr, int(gridDim.x));
   const int64_t k = grain_of_block(int(blockIdx.x), int(gridDim.x), S);
-  if (k >= S) return;
+  if (k >= S) return k;
   const int64_t c0 = slice_begin(k, S, C), c1 = slice_begin(k + 1, S, C);
   int64_t carry = 0;
   for (int base = 0; base < v.num_seqs; base += kBlock) {
-    if (base > 0) block_seq_costs(v, sl, qsl, base, c, n, q0, qn);
+    if (base > 0) block_seq_costs<kPer>(v, sl, qsl, base, c, n, q0, qn);
     int64_t x = 0;
 #pragma unroll
-    for (int e = 0; e < kPreSeqs; ++e) x += c[e];
+    for (int e = 0; e < kPer; ++e) x += c[e];
     int64_t tot;
     int64_t pre = carry + wg_exclusive_scan(x, pl.red, &tot);
     if (c0 >= pre && c0 < pre + x) {  // exactly one thread holds the sequence of cost c0
 #pragma unroll
-      for (int e = 0; e < kPreSeqs; ++e) {
+      for (int e = 0; e < kPer; ++e) {
         if (c0 >= pre && c0 < pre + c[e]) {
           UnitCursor cu;
-          cursor_place(cu, v, base + int(threadIdx.x) * kPreSeqs + e, pre, n[e], q0[e], qn[e], c0);
+          cursor_place(cu, v, base + int(threadIdx.x) * kPer + e, pre, n[e], q0[e], qn[e], c0);
           pl.st = slot_from_cursor(cu, c0, c1);
         }
         pre += c[e];
@@ -1773,6 +1794,18 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fused_kernel(AttnArgs A
     if (c0 < carry) break;  // uniform: every thread holds the same carry
   }
   __syncthreads();
+  return k;
+}
+
+// Single launch: every workgroup plans (plan_grain), then runs its grain and merges the split
+// units it completes.
+template <class TR, bool kTree>
+__global__ __launch_bounds__(kThreads, 2) void attention_fused_kernel(AttnArgs A) {
+  __shared__ Smem<TR> sm;
+  __shared__ PreLds pl;
+  int64_t S, C;
+  const int64_t k = A.plan.num_seqs <= kThreads ? plan_grain<1>(A.plan, pl, S, C) : plan_grain<4>(A.plan, pl, S, C);
+  if (k >= S) return;
   const SlotStart st = pl.st;
   run_grain<TR, true, kTree>(A, int(k), st, S, C, sm, &pl.flag);
 }

@@ -204,9 +204,11 @@ def test_workspace_reused_across_batches():
             assert torch.equal(o, ref_o) and torch.equal(l, ref_l), (rep, i, w.name)
 
 
-def test_many_sequences_single_launch():
-    """More sequences than one pass of the in-kernel planner covers (1024 per pass)."""
-    w = W.make_random(64, 2500, 90, 8, 2, 64, "bf16", max_q=4)
+@pytest.mark.parametrize("B", [2500, 600, 257])
+def test_many_sequences_single_launch(B):
+    """Batches the in-kernel planner covers with several sequences per thread: one pass of 1024
+    sequences (600, 257: one more than one per thread) and several passes (2500)."""
+    w = W.make_random(64, B, 90, 8, 2, 64, "bf16", max_q=4)
     t = pa.to_device(w)
     o, l = run_gpu(w)
     so, sl = _staged(w, t)
