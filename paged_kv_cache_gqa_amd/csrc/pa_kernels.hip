@@ -1337,6 +1337,37 @@ __device__ void cursor_place(UnitCursor& cu, const PlanView& v, int s, int64_t s
   cu.U = make_unit(cu.s, cu.q, v.group, cu.g, cu.rb, acc);
 }
 
+// cursor_place done by all 64 lanes of a wave together (every lane gets the same cursor): the
+// row block is found by lanes evaluating 64 block starts at once and a ballot of which ones lie
+// at or below c -- one round for up to 64 blocks, two for up to 4096 -- instead of a serial
+// binary search of floor sums.
+__device__ void cursor_place_wave(UnitCursor& cu, const PlanView& v, int s, int64_t seq_base, int n, int q0, int qn,
+                                  int64_t c, int lane) {
+  cu.s = s;
+  cu.seq_base = seq_base;
+  cu.q = seq_units(n, q0, qn, v.group, v.full_rows != 0);
+  const int64_t off = c - cu.seq_base;
+  cu.g = int(off / cu.q.per_head);
+  int64_t acc = cu.seq_base + int64_t(cu.g) * cu.q.per_head;
+  cu.rb = 0;
+  if (!cu.q.split) {
+    int lo = 0, hi = cu.q.nb - 1;  // the block holding c lies in [lo, hi]; block lo starts at or below c
+    while (lo < hi) {
+      const int step = (hi - lo + 64) / 64;  // candidates lo, lo + step, ... cover [lo, hi]
+      const int r = min(lo + lane * step, hi);
+      const uint64_t below = __ballot(acc + block_start(cu.q, v.group, r) <= c);  // a prefix of the lanes
+      const int last = 63 - __builtin_clzll(below);
+      const int r_last = min(lo + last * step, hi);
+      hi = min(r_last + step - 1, hi);
+      lo = r_last;
+      if (step == 1) break;
+    }
+    cu.rb = lo;
+    acc += block_start(cu.q, v.group, lo);
+  }
+  cu.U = make_unit(cu.s, cu.q, v.group, cu.g, cu.rb, acc);
+}
+
 // Position the cursor on the unit whose cost range holds c (0 <= c < total).
 template <class P, class Q>
 __device__ void cursor_find(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl, Q seq_cost, int64_t c) {
@@ -1699,6 +1730,8 @@ __device__ __forceinline__ int64_t wg_exclusive_scan(int64_t x, int64_t* red, in
 
 struct PreLds {
   int64_t red[2 * kWaves];
+  int64_t hold_base;  // the sequence holding the grain start: its first cost, index, lengths
+  int32_t hold_s, hold_n, hold_q0, hold_qn;
   SlotStart st;
   int flag;
 };
@@ -1783,15 +1816,23 @@ __device__ __forceinline__ int64_t plan_grain(const PlanView& v, PreLds& pl, int
 #pragma unroll
       for (int e = 0; e < kPer; ++e) {
         if (c0 >= pre && c0 < pre + c[e]) {
-          UnitCursor cu;
-          cursor_place(cu, v, base + int(threadIdx.x) * kPer + e, pre, n[e], q0[e], qn[e], c0);
-          pl.st = slot_from_cursor(cu, c0, c1);
+          pl.hold_base = pre;
+          pl.hold_s = base + int(threadIdx.x) * kPer + e;
+          pl.hold_n = n[e];
+          pl.hold_q0 = q0[e];
+          pl.hold_qn = qn[e];
         }
         pre += c[e];
       }
     }
     carry += tot;
     if (c0 < carry) break;  // uniform: every thread holds the same carry
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {  // wave 0 places the cursor
+    UnitCursor cu;
+    cursor_place_wave(cu, v, pl.hold_s, pl.hold_base, pl.hold_n, pl.hold_q0, pl.hold_qn, c0, int(threadIdx.x));
+    if (threadIdx.x == 0) pl.st = slot_from_cursor(cu, c0, c1);
   }
   __syncthreads();
   return k;
