@@ -63,6 +63,11 @@ SMALL = [
     (8, 4, 400, 64, 1, 128, "bf16", 2),
     (9, 6, 333, 8, 2, 128, "f32", 17),
     (10, 8, 64, 12, 3, 64, "bf16", 64),
+    # group sizes that do not divide a 64-row block: row blocks end mid-token
+    (11, 5, 600, 28, 4, 128, "bf16", 150),   # G = 7
+    (12, 4, 400, 24, 8, 64, "f32", 90),      # G = 3
+    (13, 3, 900, 40, 8, 128, "bf16", 300),   # G = 5
+    (14, 3, 500, 96, 8, 128, "bf16", 70),    # G = 12
 ]
 
 
@@ -166,6 +171,15 @@ def test_deterministic_and_staged_equals_one_shot():
     pa.merge_planned(desc, t["seq_lens"], t["query_start_loc"], out, lse, ws)
     torch.cuda.synchronize()
     assert torch.equal(o1, out) and torch.equal(l1, lse)
+
+
+def test_staged_equals_one_shot_odd_group():
+    """Row blocks that end mid-token (G = 7): the in-kernel plan and the staged planner agree bitwise."""
+    w = W.make_random(15, 5, 700, 28, 4, 128, "bf16", max_q=200)
+    t = pa.to_device(w)
+    o1, l1 = run_gpu(w)
+    o2, l2 = _staged(w, t)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 def _staged(w, t, ws=None):
