@@ -254,7 +254,8 @@ def cpu_plan(w, grid):
     """The plan's units re-derived on the CPU from the stated rules (sequence, kv head, row block order;
     key-split units for q_len*G <= 32 rows, else 64-row blocks; a unit costs 12 + chunks * weight
     (weight 4 for both kinds) and its chunk i starts at cost0 + 12 + i * weight; the cost axis
-    is cut into min(grid, key-split cost // 4 + row-split cost // 32) equal grains, one per workgroup)."""
+    is cut into min(g, key-split cost // 4 + row-split cost // 32) equal grains, one per workgroup, where
+    g is the grid, halved -- one workgroup per CU -- for a batch without row-split work)."""
     BLOCK, W_ROW = 64, 4
     G = w.num_q_heads // w.num_kv_heads
     units, cost, row_cost = [], 0, 0
@@ -276,7 +277,8 @@ def cpu_plan(w, grid):
                                   kind=0 if split else 1, cost_weight=wgt, cost0=cost))
                 cost += 12 + nch * wgt
                 row_cost += 0 if split else 12 + nch * wgt
-    S = max(1, min(grid, (cost - row_cost) // 4 + row_cost // (8 * W_ROW)))
+    g = grid // 2 if row_cost == 0 and grid % 16 == 0 else grid
+    S = max(1, min(g, (cost - row_cost) // 4 + row_cost // (8 * W_ROW)))
     bounds = [k * cost // S for k in range(S + 1)]
     for u in units:
         owners = [bisect.bisect_right(bounds, u["cost0"] + 12 + i * u["cost_weight"]) - 1
