@@ -37,7 +37,10 @@ constexpr int kCostKeySplit = 4;
 constexpr int kCostRowSplit = PA_COST_ROW;
 // Fixed cost charged at the start of every unit (row and page-table loads, the
 // pipeline fill), so that grains that start many units get fewer chunks.
-constexpr int kCostUnitStart = 12;
+#ifndef PA_COST_UNIT_START
+#define PA_COST_UNIT_START 12
+#endif
+constexpr int kCostUnitStart = PA_COST_UNIT_START;
 
 // bf16 decode: K of a chunk by global->LDS DMA (1) or straight to registers (0)
 #ifndef PA_K_VIA_LDS

@@ -161,6 +161,9 @@ __device__ __forceinline__ void lds_read4_b32(const uint32_t (&a)[4], uint32_t& 
 __device__ __forceinline__ void lds_write_b128(uint32_t a, u32x4_t v) {
   asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(v) : "memory");
 }
+__device__ __forceinline__ void lds_write_b64(uint32_t a, u32x2_t v) {
+  asm volatile("ds_write_b64 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
 // N 16-byte reads (N even), in blocks of four and two.
 template <int N>
 __device__ __forceinline__ void lds_read_b128(const uint32_t (&a)[N], u32x4_t (&r)[N]) {
@@ -856,6 +859,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
+
+// s_waitcnt lgkmcnt(0): this wave's LDS accesses written as inline asm are done; global loads and
+// DMAs in flight are not waited for.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Workgroup barrier that orders LDS accesses for the compiler without waiting on global memory.
 __device__ __forceinline__ void lds_barrier() {
@@ -1626,6 +1633,242 @@ __device__ void arrive_and_merge(const AttnArgs& A, const pa_plan_unit& U, int64
   if (threadIdx.x == 0) __hip_atomic_store(A.arrive + first, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The chunks [i0, i1) of a unit that lie in the grain [c0, c1), and where their result goes:
+// part < 0 -- the whole unit, final output; else the partial position (grain * 2 + 0 for the piece
+// the grain starts inside, + 1 for the one it ends inside).
+struct Piece {
+  int i0, i1, part;
+};
+__device__ __forceinline__ Piece piece_of(const pa_plan_unit& U, int64_t c0, int64_t c1, int grain) {
+  const int64_t w = U.cost_weight;
+  const int64_t cs = chunk_start(U, 0);
+  Piece p;
+  p.i0 = int(c0 > cs ? (c0 - cs + w - 1) / w : 0);
+  const int64_t e = c1 > cs ? (c1 - cs + w - 1) / w : 0;
+  p.i1 = int(e < U.n_chunks ? e : U.n_chunks);
+  // a grain holds at most two pieces of split units: the one it starts inside (position 0)
+  // and the one it ends inside (position 1)
+  p.part = (p.i0 > 0 || p.i1 < U.n_chunks) ? 2 * grain + (cs < c0 ? 0 : 1) : -1;
+  return p;
+}
+
+#ifndef PA_KS_STREAM
+#define PA_KS_STREAM 1
+#endif
+
+// Key-split units of RT row tiles (bf16 pages, K by DMA) run back to back: the cursor's unit and
+// the units after it in the grain while they are of that kind.  In a wave's last step of a unit,
+// its one load in flight is already its first chunk of the next unit (page ids loaded at the unit
+// start), and for one row tile the next unit's Q is in registers by then too, so the unit's end --
+// the cross-wave merge and the output -- overlaps those loads instead of adding two dependent
+// round trips (page ids, then K/V) to every unit start.  The merge goes through the Q slices only
+// (the K slots may be receiving a DMA), one row tile at a time, with LDS accesses that do not wait
+// for global loads.  Leaves the cursor on the last unit it ran.
+template <class TR, int RT>
+__device__ void run_keysplit_stream(const AttnArgs& A, UnitCursor& cu, Piece p, int64_t c0, int64_t c1, int grain,
+                                    Smem<TR>& sm) {
+  using RG = Ring<TR>;
+  static_assert(TR::kBf16 && PA_K_VIA_LDS, "bf16 pages with K by DMA");
+  constexpr bool kPreQ = RT == 1;  // two row tiles of Q held across a unit would spill
+  const PlanView& v = A.plan;
+  const cptr<int32_t> seq_lens = ro(v.seq_lens);
+  const cptr<int32_t> qsl = ro(v.qsl);
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int quad = lane >> 4;
+  const int n = lane & 15;
+  constexpr int kQRegion = kWaves * 2 * TR::kQF * 64;  // u32x4 slots of the Q slices
+  static_assert(kWaves * TR::kTiles * 64 <= kQRegion, "one row tile's merge buffer inside the Q slices");
+  static_assert(kQRegion * 16 + kWaves * 2 * RG::kBlk <= Smem<TR>::kBytes, "LDS budget");
+  u32x4_t* qlds = sm.buf + w * (RT * TR::kQF * 64);
+  char* kslot = reinterpret_cast<char*>(sm.buf + kQRegion) + w * 2 * RG::kBlk;
+  f32x4_t* obuf = reinterpret_cast<f32x4_t*>(sm.buf);
+  float* stat = &sm.stat[0][0][0][0];  // (m, l) of wave i, row r at 2 * (16 i + r)
+  const uint32_t vl = TR::v_lane(lane);
+  auto dma_k = [&](const ChunkPages& cp) {
+    constexpr int kPer = RG::kBlk / 1024;  // DMA instructions per page
+    const __amdgpu_buffer_rsrc_t r0 = block_rsrc(cp.k0, RG::kBlk), r1 = block_rsrc(cp.k1, RG::kBlk);
+#pragma unroll
+    for (int i = 0; i < 2 * kPer; ++i) {
+      const int o = (i % kPer) * 1024 + 16 * lane;
+      const int r = o / RG::kPitchK, cc = (o % RG::kPitchK) / 16;
+      dma16(i < kPer ? r0 : r1, uint32_t(r * RG::kPitchK + RG::swz_k(r, cc) * 16),
+            kslot + (i / kPer) * RG::kBlk + (i % kPer) * 1024);
+    }
+  };
+  auto bt_of = [&](int s) {
+    return ro(A.block_table) + int64_t(s) * A.max_pages + (A.key_base ? ro(A.key_base)[s] / kPage : 0);
+  };
+  auto same_kind = [&](const pa_plan_unit& N) {
+    return N.kind == 0 && (RT == 1 ? N.n_rows <= 16 : N.n_rows > 16);
+  };
+  typename TR::VRaw vr[TR::kVF];
+  u32x4_t qnext[kPreQ ? TR::kQF : 1];  // Q of the next unit, loaded during this one
+  bool pre = false;  // this wave's first load (and Q, for one row tile) of the unit were issued before
+  for (;;) {
+    const pa_plan_unit& U = cu.U;
+    const int n_seq = cu.q.n, qn = cu.q.qn;
+    const cptr<int32_t> bt_row = bt_of(U.seq);
+    RowInfo ri[RT];
+    int p_row[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      ri[rt] = row_info(A, U, 16 * rt + n, n_seq, cu.q.q0, qn);
+      p_row[rt] = ri[rt].p;
+    }
+    u32x4_t qtmp[RT][TR::kQF];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int f = 0; f < TR::kQF; ++f) {
+        if constexpr (kPreQ) qtmp[rt][f] = pre ? qnext[f] : load_q_frag<TR>(A, ri[rt], f, quad);
+        else qtmp[rt][f] = load_q_frag<TR>(A, ri[rt], f, quad);
+      }
+    // Does the stream go on?  Only the next unit's kv head, this wave's first page ids in it and
+    // (one row tile) its Q rows are kept; the cursor is advanced again after the unit.
+    bool nxt;
+    int nkvh = 0;
+    PageIds held{0, 0};
+    RowInfo rnext{0, 0, -1, false};
+    {
+      UnitCursor nc = cu;
+      nxt = cursor_next(nc, v, seq_lens, qsl) && nc.U.cost0 < c1 && same_kind(nc.U);
+      if (nxt) {
+        const Piece np = piece_of(nc.U, c0, c1, grain);
+        nxt = np.i0 < np.i1;
+        if (nxt) {
+          held = page_ids_load(bt_of(nc.U.seq), np.i0 + w < np.i1 ? np.i0 + w : np.i0, nc.q.n);
+          if constexpr (kPreQ) rnext = row_info(A, nc.U, n, nc.q.n, nc.q.q0, nc.q.qn);
+        }
+        nkvh = nc.U.kv_head;
+      }
+    }
+    // The next unit's Q is loaded in this unit's first step, after the wait for its first chunk
+    // (so that wait does not also cover it) and before the next DMA (so the next wait does not).
+    auto load_qnext = [&] {
+      if constexpr (kPreQ) {
+        if (nxt) {
+#pragma unroll
+          for (int f = 0; f < TR::kQF; ++f) qnext[f] = load_q_frag<TR>(A, rnext, f, quad);
+        }
+      }
+    };
+    const int c = p.i0 + w;
+    const int mine = p.i1 > c ? (p.i1 - c + kWaves - 1) / kWaves : 0;  // chunks of this wave
+    TreeMask<RT> tm;
+    tm.win0 = 0;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) tm.m[rt] = ~uint64_t(0);
+    const int min_p = v.full_rows ? n_seq - 1 : n_seq - qn + U.row0 / v.group;  // first row's last key
+    if (!pre) {
+      const ChunkPages cp = pages_of<TR>(A, U.kv_head, page_ids(bt_row, c < p.i1 ? c : p.i0, n_seq));
+      dma_k(cp);
+      load_v<TR>(cp, vl, vr);
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int f = 0; f < TR::kQF; ++f) lds_write_b128(lds_addr(qlds + (rt * TR::kQF + f) * 64 + lane), qtmp[rt][f]);
+    // the next unit's page ids: waited for here only on the stream's first unit (issued after
+    // this unit's Q); later they were issued one unit ahead
+    const PageIds nid = uniform_ids(held);
+    State<TR, RT> st;
+    state_init(st);
+    if (mine == 0) load_qnext();
+    if (mine == 0 && nxt) {
+      // no chunk of this unit for this wave: its load in flight is a dummy; replace it by its first
+      // chunk of the next unit once the dummy's DMA into the slot has landed
+      wait_all_loads();
+      const ChunkPages cp = pages_of<TR>(A, nkvh, nid);
+      dma_k(cp);
+      load_v<TR>(cp, vl, vr);
+    }
+    PageIds nx = page_ids(bt_row, min(c + kWaves, p.i1 - 1), n_seq);
+    for (int j = 0; j < mine; ++j) {
+      const int cc = c + j * kWaves;
+      const int key0 = cc * kChunkKeys;
+      const int cn = cc + kWaves;
+      // the wave's next load: its next chunk, else its first chunk of the next unit, else a dummy
+      // (the pool's first page: an L2 hit) that keeps one load in flight on every path
+      const ChunkPages ncp = pages_of<TR>(A, cn < p.i1 ? U.kv_head : nkvh,
+                                          cn < p.i1 ? nx : (nxt ? nid : PageIds{0, 0}));
+      typename TR::PFrag pf[RT];
+      u32x4_t kf[TR::kKF];
+      wait_vmcnt<TR::kVLoads>();  // the K DMA of this chunk has landed (only V was issued after it)
+      asm volatile("" ::: "memory");
+      TR::template lds_read_k<RG>(kslot, lane, kf);  // completes before the slot is refilled
+      asm volatile("" ::: "memory");
+      if (j == 0) load_qnext();
+      dma_k(ncp);
+      auto getq_asm = [&](int rt, u32x4_t (&qf)[TR::kQF]) {
+        uint32_t a[TR::kQF];
+#pragma unroll
+        for (int f = 0; f < TR::kQF; ++f) a[f] = lds_addr(qlds + (rt * TR::kQF + f) * 64 + lane);
+        lds_read_b128<TR::kQF>(a, qf);
+      };
+      softmax_chunk<TR, RT, false>(st, getq_asm, kf, key0, p_row, tm, ChunkScale{1.f, 1.f, 1.f, 1.f},
+                                   key0 + kChunkKeys - 1 > min_p, A.scale_log2, lane, pf);
+      asm volatile("" ::: "memory");
+      nx = page_ids(bt_row, min(cn + kWaves, p.i1 - 1), n_seq);
+      u32x4_t vf[TR::kVF];
+#pragma unroll
+      for (int f = 0; f < TR::kVF; ++f) vf[f] = TR::v_convert(vr[f]);
+      TR::sanitize_v(vf, quad, n_seq - key0);
+      pv_chunk<TR, RT>(st, vf, pf);
+      load_v<TR>(ncp, vl, vr);
+    }
+    if (!nxt) wait_all_loads();  // the stream ends: nothing of it left in flight
+    wait_lds();
+    lds_barrier();  // every wave is done with its Q slice before the merge buffer overwrites it
+
+    // merge the 4 waves' states through LDS, one row tile at a time
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float l = quad_sum(st.l[rt]);
+      if (quad == 0)
+        lds_write_b64(lds_addr(stat + 2 * (16 * w + n)), u32x2_t{__float_as_uint(st.m[rt]), __float_as_uint(l)});
+#pragma unroll
+      for (int t = 0; t < TR::kTiles; ++t)
+        lds_write_b128(lds_addr(obuf + (w * TR::kTiles + t) * 64 + lane), __builtin_bit_cast(u32x4_t, st.o[rt][t]));
+      wait_lds();
+      lds_barrier();
+      uint32_t a[kWaves];
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) a[i] = lds_addr(stat + 2 * (16 * i + n));
+      u32x2_t ml[kWaves];
+      lds_read4_b64(a, ml[0], ml[1], ml[2], ml[3]);
+      float M = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) M = fmaxf(M, __uint_as_float(ml[i][0]));
+      float sc[kWaves], L = 0.f;
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) {
+        const float mw = __uint_as_float(ml[i][0]);
+        sc[i] = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+        L += __uint_as_float(ml[i][1]) * sc[i];
+      }
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      const float lse_nat = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+      for (int t = w; t < TR::kTiles; t += kWaves) {
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) a[i] = lds_addr(obuf + (i * TR::kTiles + t) * 64 + lane);
+        u32x4_t x[kWaves];
+        lds_read4_b128(a, x[0], x[1], x[2], x[3]);
+        f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) o += as_f32x4(x[i]) * sc[i];
+        emit<TR>(A, ri[rt], 16 * rt + n, p.part, t, quad, o * inv, lse_nat, t == 0 && quad == 0);
+      }
+      lds_barrier();  // the merge reads are done (each waited in place) before the region is rewritten
+    }
+    if (!nxt) return;
+    cursor_next(cu, v, seq_lens, qsl);
+    p = piece_of(cu.U, c0, c1, grain);
+    pre = true;
+  }
+}
+
 // One grain: the chunks whose start cost lies in [st.c0, st.c1), unit by unit.  kFused: the
 // single-launch kernel (S grains over total cost C; split units are merged here), else the staged
 // kernel (split units are left as partial results for the merge kernel).
@@ -1642,23 +1885,30 @@ __device__ __forceinline__ void run_grain(const AttnArgs& A, int grain, const Sl
   do {
     const pa_plan_unit& U = cu.U;
     if (U.cost0 >= c1) break;
-    const int64_t w = U.cost_weight;
-    const int64_t cs = chunk_start(U, 0);
-    const int i0 = int(c0 > cs ? (c0 - cs + w - 1) / w : 0);
-    const int64_t e = c1 > cs ? (c1 - cs + w - 1) / w : 0;
-    const int i1 = int(e < U.n_chunks ? e : U.n_chunks);
+    const Piece pc = piece_of(U, c0, c1, grain);
+    const int i0 = pc.i0, i1 = pc.i1, part = pc.part;
     if (i0 < i1) {
-      // a grain holds at most two pieces of split units: the one it starts inside (position 0)
-      // and the one it ends inside (position 1)
-      const int part = (i0 > 0 || i1 < U.n_chunks) ? 2 * grain + (cs < c0 ? 0 : 1) : -1;
-      if (U.kind == 0) {
-        if (U.n_rows <= 16) run_keysplit<TR, 1, kTree>(A, U, cu.q, i0, i1, part, sm);
-        else run_keysplit<TR, 2, kTree>(A, U, cu.q, i0, i1, part, sm);
-      } else {
-        run_rowsplit<TR, kTree>(A, U, cu.q, i0, i1, part, sm);
+      bool streamed = false;
+      if constexpr (PA_KS_STREAM && TR::kBf16 && !TR::kScaled && PA_K_VIA_LDS && !kTree) {
+        // a stream never holds the piece the grain starts inside (its arrival would wait for the
+        // next unit's loads); the one it ends inside can only be the stream's last unit
+        // (units of two row tiles streamed ~1% slower: their Q cannot be held across a unit)
+        if (U.kind == 0 && U.n_rows <= 16 && (part < 0 || (part & 1))) {
+          run_keysplit_stream<TR, 1>(A, cu, pc, c0, c1, grain, sm);  // moves the cursor to its last unit
+          streamed = true;
+        }
       }
-      if constexpr (kFused) {
-        if (part >= 0) arrive_and_merge<TR>(A, U, S, C, flag, reinterpret_cast<float*>(sm.buf));
+      if (!streamed) {
+        if (U.kind == 0) {
+          if (U.n_rows <= 16) run_keysplit<TR, 1, kTree>(A, U, cu.q, i0, i1, part, sm);
+          else run_keysplit<TR, 2, kTree>(A, U, cu.q, i0, i1, part, sm);
+        } else {
+          run_rowsplit<TR, kTree>(A, U, cu.q, i0, i1, part, sm);
+        }
+      }
+      if constexpr (kFused) {  // cu.U: the unit just run (the stream's last one)
+        if ((streamed ? piece_of(cu.U, c0, c1, grain).part : part) >= 0)
+          arrive_and_merge<TR>(A, cu.U, S, C, flag, reinterpret_cast<float*>(sm.buf));
       }
     }
   } while (cursor_next(cu, v, seq_lens, qsl));

@@ -230,6 +230,21 @@ def test_many_sequences_single_launch(B):
     check(w, o, l)
 
 
+@pytest.mark.parametrize("maxq", [1, 4, 6])
+def test_streamed_short_decode_units(maxq):
+    """Many short key-split units back to back in each workgroup (bf16, D = 128): units of one
+    to seven chunks, so some waves have no chunk of a unit, consecutive units of one sequence and
+    of the next, and (max_q = 6) units of one and of two row tiles interleaved."""
+    w = W.make_random(65, 300, 200, 32, 8, 128, "bf16", max_q=maxq)
+    t = pa.to_device(w)
+    o, l = run_gpu(w)
+    o2, l2 = run_gpu(w)
+    assert torch.equal(o, o2) and torch.equal(l, l2)
+    so, sl = _staged(w, t)
+    assert torch.equal(o, so) and torch.equal(l, sl)
+    check(w, o, l)
+
+
 # ---------------------------------------------------------------------------
 # integer / indexing outputs (bit-exact)
 # ---------------------------------------------------------------------------
