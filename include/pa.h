@@ -231,7 +231,10 @@ pa_status pa_merge_planned(const pa_desc* desc, const int32_t* seq_lens, const i
  * `kv_head` (row index = window token * (Hq/Hkv) + head within the group)
  * against keys [0, n_keys), cut into ceil(n_keys / 32) chunks of 32 keys.
  * Units lie on one cost axis in (sequence, kv head, row block) order (cost0 =
- * prefix of n_chunks * cost_weight); grain k -- run by one workgroup of the
+ * prefix of the unit costs; a unit costs a fixed start cost -- 48 for kind 0
+ * with more than 16 rows, else 32 -- plus
+ * n_chunks * cost_weight, and its chunk i starts at cost0 + start + i *
+ * cost_weight); grain k -- run by one workgroup of the
  * persistent launch -- takes the chunks whose start lies in
  * [floor(k*C/S), floor((k+1)*C/S)), C = total_cost, S = n_slots.  kind 0:
  * rows <= 32, the four waves of a workgroup split the chunks; kind 1:

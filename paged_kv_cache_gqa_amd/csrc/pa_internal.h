@@ -36,11 +36,17 @@ constexpr int kCostKeySplit = 4;
 #endif
 constexpr int kCostRowSplit = PA_COST_ROW;
 // Fixed cost charged at the start of every unit (row and page-table loads, the
-// pipeline fill), so that grains that start many units get fewer chunks.
-#ifndef PA_COST_UNIT_START
-#define PA_COST_UNIT_START 12
-#endif
-constexpr int kCostUnitStart = PA_COST_UNIT_START;
+// pipeline fill, the cross-wave merge and the output), so that grains that start
+// many units get fewer chunks.  Fitted on MI355X (bench.py, configurations 2-5):
+// a key-split unit of one row tile (decode; units stream back to back) and a
+// 64-row block cost about 8 chunks more than their chunks, a key-split unit of
+// two row tiles (verify) about 12.
+constexpr int kCostStartKs1 = 32;
+constexpr int kCostStartKs2 = 48;
+constexpr int kCostStartRow = 32;
+inline __host__ __device__ int unit_start_cost(bool key_split, int rows) {
+  return key_split ? (rows <= 16 ? kCostStartKs1 : kCostStartKs2) : kCostStartRow;
+}
 
 // bf16 decode: K of a chunk by global->LDS DMA (1) or straight to registers (0)
 #ifndef PA_K_VIA_LDS

@@ -1266,28 +1266,28 @@ __device__ SeqUnits seq_units(int n, int q0, int qn, int G, bool full) {
     q.per_head = 0;
   } else if (q.split) {
     q.nb = 1;
-    q.per_head = kCostUnitStart + int64_t(ceil_div(n, kChunkKeys)) * kCostKeySplit;
+    q.per_head = unit_start_cost(true, q.rows) + int64_t(ceil_div(n, kChunkKeys)) * kCostKeySplit;
   } else {
     q.nb = ceil_div(q.rows, kBlockRows);
     // the last block's last row is the window's last token: it sees all n keys
     const int64_t ch = block_chunks_before(n, qn, G, full, q.nb - 1) + ceil_div(n, kChunkKeys);
-    q.per_head = int64_t(q.nb) * kCostUnitStart + ch * kCostRowSplit;
+    q.per_head = int64_t(q.nb) * kCostStartRow + ch * kCostRowSplit;
   }
   return q;
 }
 
-// A unit occupies [cost0, cost0 + kCostUnitStart + n_chunks * weight) on the cost axis;
-// chunk i starts at cost0 + kCostUnitStart + i * weight.
+// A unit occupies [cost0, cost0 + start + n_chunks * weight) on the cost axis (start: its fixed
+// start cost); chunk i starts at cost0 + start + i * weight.
 __device__ __forceinline__ int64_t unit_cost(const pa_plan_unit& U) {
-  return kCostUnitStart + int64_t(U.n_chunks) * U.cost_weight;
+  return unit_start_cost(U.kind == 0, U.n_rows) + int64_t(U.n_chunks) * U.cost_weight;
 }
 __device__ __forceinline__ int64_t chunk_start(const pa_plan_unit& U, int i) {
-  return U.cost0 + kCostUnitStart + int64_t(i) * U.cost_weight;
+  return U.cost0 + unit_start_cost(U.kind == 0, U.n_rows) + int64_t(i) * U.cost_weight;
 }
 
 // Cost from the start of a kv head's row blocks to the start of block rb (rb < nb).
 __device__ __forceinline__ int64_t block_start(const SeqUnits& q, int G, int rb) {
-  return int64_t(rb) * kCostUnitStart + block_chunks_before(q.n, q.qn, G, q.full, rb) * kCostRowSplit;
+  return int64_t(rb) * kCostStartRow + block_chunks_before(q.n, q.qn, G, q.full, rb) * kCostRowSplit;
 }
 
 __device__ pa_plan_unit make_unit(int s, const SeqUnits& q, int G, int g, int rb, int64_t cost0) {

@@ -267,8 +267,9 @@ def test_gather_kv_bit_exact(dt, D):
 
 def cpu_plan(w, grid):
     """The plan's units re-derived on the CPU from the stated rules (sequence, kv head, row block order;
-    key-split units for q_len*G <= 32 rows, else 64-row blocks; a unit costs 12 + chunks * weight
-    (weight 4 for both kinds) and its chunk i starts at cost0 + 12 + i * weight; the cost axis
+    key-split units for q_len*G <= 32 rows, else 64-row blocks; a unit costs start + chunks * weight
+    (weight 4 for both kinds; start 48 for a key-split unit of more than 16 rows, else 32) and its
+    chunk i starts at cost0 + start + i * weight; the cost axis
     is cut into min(g, key-split cost // 4 + row-split cost // 32) equal grains, one per workgroup, where
     g is the grid, halved -- one workgroup per CU -- for a batch without row-split work)."""
     BLOCK, W_ROW = 64, 4
@@ -288,15 +289,17 @@ def cpu_plan(w, grid):
                 nk = n if split else n - qn + (r0 + nr - 1) // G + 1
                 nch = -(-nk // 32)
                 wgt = 4 if split else W_ROW
+                start = 48 if split and nr > 16 else 32
                 units.append(dict(seq=s, kv_head=g, row0=r0, n_rows=nr, n_keys=nk, n_chunks=nch,
                                   kind=0 if split else 1, cost_weight=wgt, cost0=cost))
-                cost += 12 + nch * wgt
-                row_cost += 0 if split else 12 + nch * wgt
+                cost += start + nch * wgt
+                row_cost += 0 if split else start + nch * wgt
     g = grid // 2 if row_cost == 0 and grid % 16 == 0 else grid
     S = max(1, min(g, (cost - row_cost) // 4 + row_cost // (8 * W_ROW)))
     bounds = [k * cost // S for k in range(S + 1)]
     for u in units:
-        owners = [bisect.bisect_right(bounds, u["cost0"] + 12 + i * u["cost_weight"]) - 1
+        start = 48 if u["kind"] == 0 and u["n_rows"] > 16 else 32
+        owners = [bisect.bisect_right(bounds, u["cost0"] + start + i * u["cost_weight"]) - 1
                   for i in range(u["n_chunks"])]
         assert sorted(set(owners)) == list(range(owners[0], owners[-1] + 1))  # contiguous pieces, no gaps
         u["first_slot"], u["n_pieces"] = owners[0], owners[-1] - owners[0] + 1
