@@ -12,7 +12,12 @@ serve them); no flush kernel runs inside the timed region.
 Default workload: Llama-3-8B-shaped decode (64 sequences, context uniform in
 [512, 4096], 32 query / 8 KV heads, head dim 128, bf16, 16-slot pages).
 `value` is algorithmic bytes (every valid K/V row once per KV head, Q, out,
-LSE, block-table entries) divided by the wall time per step.
+LSE, block-table entries) divided by the wall time per step over K steps issued
+back to back.  The roofline's kernel duration is the span of two HIP events on
+the launch stream bracketing those K launches, divided by K.  A second pass over
+the same K steps records events around each launch for the spread (and for the
+staged path's attention kernel); its event packets add a few microseconds per
+launch, so it gives neither `value` nor the single launch's mean.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C]
 """
@@ -164,8 +169,19 @@ def bench_append(args, w) -> int:
     for _ in range(args.warmup):
         L.pa_append_kv(*cargs)
     torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # timed region: K launches back to back, bracketed by two HIP events on the launch stream
+    bracket = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     t0 = time.perf_counter()
+    bracket[0].record(stream)
+    for _ in range(args.steps):
+        if L.pa_append_kv(*cargs):
+            raise RuntimeError("append launch failed")
+    bracket[1].record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    kmean = bracket[0].elapsed_time(bracket[1]) / args.steps
+    # spread: a second pass with HIP events around each launch (their packets lengthen each launch)
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for a, b in events:
         a.record(stream)
         rc = L.pa_append_kv(*cargs)
@@ -173,9 +189,7 @@ def bench_append(args, w) -> int:
         if rc:
             raise RuntimeError(f"launch failed: {B.status_string(rc)}")
     torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     ks = [a.elapsed_time(b) for a, b in events]
-    kmean = statistics.fmean(ks)
     name = w.name
     line = {
         "metric": "paged KV append GB/s (new K/V rows read + written, block-table entries), 1 MI355X",
@@ -187,8 +201,9 @@ def bench_append(args, w) -> int:
         "roofline": {"bound": "hbm", "achieved": round(alg_bytes / (kmean * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(alg_bytes / (kmean * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
                      "traffic": None, "kernel": "pa::append_kv_kernel", "kernel_ms_mean": round(kmean, 5),
-                     "kernel_ms_p10_p90": [round(float(np.percentile(ks, 10)), 5),
-                                           round(float(np.percentile(ks, 90)), 5)]},
+                     "kernel_ms_source": "two events bracketing the timed region, divided by the steps",
+                     "kernel_ms_p10_p90_events_each": [round(float(np.percentile(ks, 10)), 5),
+                                                       round(float(np.percentile(ks, 90)), 5)]},
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -373,16 +388,32 @@ def main() -> int:
         step(i)
     torch.cuda.synchronize()
 
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # Timed region: K steps back to back, as a caller issues them, bracketed by two HIP events on
+    # the launch stream.  With one launch per step, the events' span over K is the kernel's average
+    # launch duration (including the gap to the next launch, ~1 us).
+    bracket = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    bracket[0].record(stream)
     for i in range(args.steps):
-        step(i, events[i])
+        step(i)
+    bracket[1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    bracket_ms = bracket[0].elapsed_time(bracket[1]) / args.steps
+    # Spread of single launches: the same K steps again with HIP events around each attention launch
+    # (the staged path's attention kernel is timed this way too).  The event packets add a few
+    # microseconds per launch, so this pass gives neither `value` nor, for one launch per step, the mean.
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    te0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    ms_per_step_events = (time.perf_counter() - te0) * 1e3 / args.steps
     attn_ms = [a.elapsed_time(b) for a, b in events]
-    attn_mean = statistics.fmean(attn_ms)
+    attn_mean = statistics.fmean(attn_ms) if args.staged else bracket_ms
 
     if args.copy_calibration:  # a plain copy of known size, for scaling the HBM counters
         src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
@@ -418,9 +449,12 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name + ("-tree" if tree else ""), kernel),
                      "kernel": f"pa::{kernel}", "kernel_ms_mean": round(attn_mean, 5),
-                     "kernel_ms_p10_p90": [round(float(np.percentile(attn_ms, 10)), 5),
-                                           round(float(np.percentile(attn_ms, 90)), 5)],
-                     "per_launch": "algorithmic bytes of the whole batch (one launch covers the batch)"},
+                     "kernel_ms_source": ("events around each attention launch (second pass)" if args.staged
+                                          else "two events bracketing the timed region, divided by the steps"),
+                     "kernel_ms_p10_p90_events_each": [round(float(np.percentile(attn_ms, 10)), 5),
+                                                       round(float(np.percentile(attn_ms, 90)), 5)],
+                     "per_launch": "algorithmic bytes of the whole batch (one launch covers the batch)",
+                     "events_pass_ms_per_step": round(ms_per_step_events, 5)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, alg_bytes)
