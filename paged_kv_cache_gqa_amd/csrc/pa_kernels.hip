@@ -1541,6 +1541,25 @@ __device__ void merge_unit(const float* part_o, const float* part_lse, void* out
     const int tk = rr / group;
     return int64_t(q0 + tk) * num_q_heads + U.kv_head * group + (rr - tk * group);
   };
+  constexpr int kLanesPerRow = TR::D / 4;
+  constexpr int kRowsPerPass = kThreads / kLanesPerRow;
+  constexpr int kRows = kPartRows / kRowsPerPass;  // rows of each thread
+  constexpr int kP = 16 / kRows;                   // pieces per round trip
+  const int d4 = threadIdx.x % kLanesPerRow, r0 = threadIdx.x / kLanesPerRow;
+  f32x4_t oj[kP][kRows];
+  auto load_pieces = [&](int j0) {
+#pragma unroll
+    for (int p = 0; p < kP; ++p)
+#pragma unroll
+      for (int i = 0; i < kRows; ++i) {
+        const int r = r0 + i * kRowsPerPass;
+        oj[p][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (j0 + p < n_pieces && r < U.n_rows)
+          oj[p][i] = load_coherent4(part_o, ((pbase(j0 + p) + r) * TR::D + 4 * d4) * 4);
+      }
+  };
+  // the first pieces' o rows are loaded before the lse round trip, so the two latencies overlap
+  load_pieces(0);
   for (int r = threadIdx.x; r < U.n_rows; r += kThreads) {
     float lj[kMergeFastPieces];
 #pragma unroll
@@ -1562,26 +1581,13 @@ __device__ void merge_unit(const float* part_o, const float* part_lse, void* out
       if (j < n_pieces) wbuf[j * kPartRows + r] = e[j] * inv;
     lse[out_row(r)] = L > 0.f ? M + fast_log2(L) * kLn2 : -INFINITY;
   }
-  __syncthreads();
-  constexpr int kLanesPerRow = TR::D / 4;
-  constexpr int kRowsPerPass = kThreads / kLanesPerRow;
-  constexpr int kRows = kPartRows / kRowsPerPass;  // rows of each thread
-  constexpr int kP = 32 / kRows;                   // pieces per round trip
-  const int d4 = threadIdx.x % kLanesPerRow, r0 = threadIdx.x / kLanesPerRow;
+  wait_lds();
+  lds_barrier();  // wbuf written (a full __syncthreads would also wait for the o loads in flight)
   f32x4_t acc[kRows];
 #pragma unroll
   for (int i = 0; i < kRows; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int j0 = 0; j0 < n_pieces; j0 += kP) {
-    f32x4_t oj[kP][kRows];
-#pragma unroll
-    for (int p = 0; p < kP; ++p)
-#pragma unroll
-      for (int i = 0; i < kRows; ++i) {
-        const int r = r0 + i * kRowsPerPass;
-        oj[p][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (j0 + p < n_pieces && r < U.n_rows)
-          oj[p][i] = load_coherent4(part_o, ((pbase(j0 + p) + r) * TR::D + 4 * d4) * 4);
-      }
+    if (j0 > 0) load_pieces(j0);
 #pragma unroll
     for (int p = 0; p < kP; ++p)
 #pragma unroll
