@@ -1929,12 +1929,31 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs A) {
     run_grain<TR, false, false>(A, int(g), load_slot(ro(A.plan.slots) + g), 0, 0, sm, nullptr);
 }
 
+// Inclusive sum of one int64 per lane over a wave (lane l gets lanes 0..l) in DPP moves: shifts by
+// 1, 2, 4, 8 within each 16-lane row (lanes shifted in from outside the row read 0), then lane 15
+// broadcast into rows 1 and 3 and lane 31 into rows 2 and 3 -- the classic GCN wave scan, without
+// the LDS round trips of ds_bpermute shuffles.  The 64-bit value moves as two 32-bit halves.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ int64_t dpp_add64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, uint32_t(uint64_t(x)), kCtrl, kRowMask, 0xF, true);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, uint32_t(uint64_t(x) >> 32), kCtrl, kRowMask, 0xF, true);
+  return x + int64_t((uint64_t(hi) << 32) | lo);
+}
+__device__ __forceinline__ int64_t wave_incl_scan64(int64_t x) {
+  x = dpp_add64<0x111, 0xF>(x);  // row_shr:1
+  x = dpp_add64<0x112, 0xF>(x);  // row_shr:2
+  x = dpp_add64<0x114, 0xF>(x);  // row_shr:4
+  x = dpp_add64<0x118, 0xF>(x);  // row_shr:8
+  x = dpp_add64<0x142, 0xA>(x);  // row_bcast:15 into rows 1, 3
+  x = dpp_add64<0x143, 0xC>(x);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 // Sums and scans of one int64 per thread over the kThreads threads of a workgroup.
 __device__ __forceinline__ int64_t wg_sum(int64_t x, int64_t* red) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  if (lane == 0) red[wid] = x;
+  x = wave_incl_scan64(x);
+  if (lane == 63) red[wid] = x;
   __syncthreads();
   int64_t t = 0;
 #pragma unroll
@@ -1945,12 +1964,9 @@ __device__ __forceinline__ int64_t wg_sum(int64_t x, int64_t* red) {
 // Both sums of two int64 per thread, with one exchange through LDS (red: 2 * kWaves slots).
 __device__ __forceinline__ void wg_sum2(int64_t x, int64_t y, int64_t* red, int64_t& sx, int64_t& sy) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    x += __shfl_xor(x, off);
-    y += __shfl_xor(y, off);
-  }
-  if (lane == 0) {
+  x = wave_incl_scan64(x);
+  y = wave_incl_scan64(y);
+  if (lane == 63) {
     red[wid] = x;
     red[kWaves + wid] = y;
   }
@@ -1965,12 +1981,7 @@ __device__ __forceinline__ void wg_sum2(int64_t x, int64_t y, int64_t* red, int6
 }
 __device__ __forceinline__ int64_t wg_exclusive_scan(int64_t x, int64_t* red, int64_t* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  int64_t incl = x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int64_t y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
+  const int64_t incl = wave_incl_scan64(x);
   if (lane == 63) red[wid] = incl;
   __syncthreads();
   int64_t before = 0, all = 0;
@@ -2132,21 +2143,11 @@ constexpr int kScanThreads = 1024;
 __device__ int64_t block_exclusive_scan(int64_t x, int64_t* wave_tot, int64_t* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   constexpr int kNW = kScanThreads / 64;
-  int64_t incl = x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int64_t y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
+  const int64_t incl = wave_incl_scan64(x);
   if (lane == 63) wave_tot[wid] = incl;
   __syncthreads();
   if (wid == 0) {
-    int64_t t = lane < kNW ? wave_tot[lane] : 0;
-#pragma unroll
-    for (int off = 1; off < kNW; off <<= 1) {
-      const int64_t y = __shfl_up(t, off);
-      if (lane >= off) t += y;
-    }
+    const int64_t t = wave_incl_scan64(lane < kNW ? wave_tot[lane] : 0);
     if (lane < kNW) wave_tot[lane] = t;
   }
   __syncthreads();
