@@ -1979,6 +1979,28 @@ __device__ __forceinline__ void wg_sum2(int64_t x, int64_t y, int64_t* red, int6
   }
   __syncthreads();
 }
+// Exclusive scan of x and the sums of x and y over the workgroup, with one exchange through LDS
+// (red: 2 * kWaves slots).
+__device__ __forceinline__ int64_t wg_scan_sum(int64_t x, int64_t y, int64_t* red, int64_t& sx, int64_t& sy) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int64_t incl = wave_incl_scan64(x);
+  y = wave_incl_scan64(y);
+  if (lane == 63) {
+    red[wid] = incl;
+    red[kWaves + wid] = y;
+  }
+  __syncthreads();
+  int64_t before = 0;
+  sx = sy = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    if (i < wid) before += red[i];
+    sx += red[i];
+    sy += red[kWaves + i];
+  }
+  __syncthreads();
+  return incl - x + before;
+}
 __device__ __forceinline__ int64_t wg_exclusive_scan(int64_t x, int64_t* red, int64_t* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int64_t incl = wave_incl_scan64(x);
@@ -2064,7 +2086,16 @@ __device__ __forceinline__ int64_t plan_grain(const PlanView& v, PreLds& pl, int
   const int64_t row0 = block_seq_costs<kPer>(v, sl, qsl, 0, c, n, q0, qn);  // kept for the search below
   C = 0;
   int64_t Cr = 0;
-  for (int base = 0; base < v.num_seqs; base += kBlock) {
+  // one block of sequences: the totals and this block's prefix come from one exchange
+  const bool one = v.num_seqs <= kBlock;
+  int64_t pre0 = 0;
+  if (one) {
+    int64_t x = 0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) x += c[e];
+    pre0 = wg_scan_sum(x, row0, pl.red, C, Cr);
+  }
+  for (int base = 0; !one && base < v.num_seqs; base += kBlock) {
     int64_t c2[kPer];
     int n2[kPer], q02[kPer], qn2[kPer];
     const int64_t row = base > 0 ? block_seq_costs<kPer>(v, sl, qsl, base, c2, n2, q02, qn2) : row0;
@@ -2091,8 +2122,8 @@ __device__ __forceinline__ int64_t plan_grain(const PlanView& v, PreLds& pl, int
     int64_t x = 0;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) x += c[e];
-    int64_t tot;
-    int64_t pre = carry + wg_exclusive_scan(x, pl.red, &tot);
+    int64_t tot = C;
+    int64_t pre = one ? pre0 : carry + wg_exclusive_scan(x, pl.red, &tot);
     if (c0 >= pre && c0 < pre + x) {  // exactly one thread holds the sequence of cost c0
 #pragma unroll
       for (int e = 0; e < kPer; ++e) {
