@@ -95,6 +95,26 @@ __device__ __forceinline__ float quad_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Inclusive sum of one int64 per lane over a wave (lane l gets lanes 0..l) in DPP moves: shifts by
+// 1, 2, 4, 8 within each 16-lane row (lanes shifted in from outside the row read 0), then lane 15
+// broadcast into rows 1 and 3 and lane 31 into rows 2 and 3 -- the classic GCN wave scan, without
+// the LDS round trips of ds_bpermute shuffles.  The 64-bit value moves as two 32-bit halves.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ int64_t dpp_add64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, uint32_t(uint64_t(x)), kCtrl, kRowMask, 0xF, true);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, uint32_t(uint64_t(x) >> 32), kCtrl, kRowMask, 0xF, true);
+  return x + int64_t((uint64_t(hi) << 32) | lo);
+}
+__device__ __forceinline__ int64_t wave_incl_scan64(int64_t x) {
+  x = dpp_add64<0x111, 0xF>(x);  // row_shr:1
+  x = dpp_add64<0x112, 0xF>(x);  // row_shr:2
+  x = dpp_add64<0x114, 0xF>(x);  // row_shr:4
+  x = dpp_add64<0x118, 0xF>(x);  // row_shr:8
+  x = dpp_add64<0x142, 0xA>(x);  // row_bcast:15 into rows 1, 3
+  x = dpp_add64<0x143, 0xC>(x);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 // The running maximum that P is scaled against is only moved when a row's new
 // maximum exceeds it by more than this many powers of two; in between, P may
 // reach 2^kLazy (exact for the sums, same relative precision for bf16 P).
@@ -1346,8 +1366,9 @@ __device__ void cursor_place(UnitCursor& cu, const PlanView& v, int s, int64_t s
 
 // cursor_place done by all 64 lanes of a wave together (every lane gets the same cursor): the
 // row block is found by lanes evaluating 64 block starts at once and a ballot of which ones lie
-// at or below c -- one round for up to 64 blocks, two for up to 4096 -- instead of a serial
-// binary search of floor sums.
+// at or below c.  Up to 64 blocks: lane r takes block r's chunk count and a wave scan of the
+// counts gives every start; more blocks: lanes evaluate floor-sum starts of 64 candidates per
+// round (two rounds for up to 4096) -- instead of a serial binary search of floor sums.
 __device__ void cursor_place_wave(UnitCursor& cu, const PlanView& v, int s, int64_t seq_base, int n, int q0, int qn,
                                   int64_t c, int lane) {
   cu.s = s;
@@ -1357,7 +1378,17 @@ __device__ void cursor_place_wave(UnitCursor& cu, const PlanView& v, int s, int6
   cu.g = int(off / cu.q.per_head);
   int64_t acc = cu.seq_base + int64_t(cu.g) * cu.q.per_head;
   cu.rb = 0;
-  if (!cu.q.split) {
+  if (!cu.q.split && cu.q.nb <= 64) {
+    // one block per lane: its chunk count, and a wave scan of the counts gives every block's start
+    const int64_t ch = lane < cu.q.nb ? ceil_div(block_keys(n, qn, v.group, lane, cu.q.full), kChunkKeys) : 0;
+    const int64_t start = int64_t(lane) * kCostStartRow + (wave_incl_scan64(ch) - ch) * kCostRowSplit;
+    const uint64_t below = __ballot(lane < cu.q.nb && acc + start <= c);  // a prefix of the lanes
+    const int rb = 63 - __builtin_clzll(below);
+    cu.rb = rb;
+    const uint64_t st = uint64_t(start);
+    acc += int64_t((uint64_t(uint32_t(__builtin_amdgcn_readlane(int(uint32_t(st >> 32)), rb))) << 32) |
+                   uint32_t(__builtin_amdgcn_readlane(int(uint32_t(st)), rb)));
+  } else if (!cu.q.split) {
     int lo = 0, hi = cu.q.nb - 1;  // the block holding c lies in [lo, hi]; block lo starts at or below c
     while (lo < hi) {
       const int step = (hi - lo + 64) / 64;  // candidates lo, lo + step, ... cover [lo, hi]
@@ -1927,26 +1958,6 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs A) {
   const int64_t S = ro(A.plan.hdr)->n_slots;
   for (int64_t g = blockIdx.x; g < S; g += gridDim.x)
     run_grain<TR, false, false>(A, int(g), load_slot(ro(A.plan.slots) + g), 0, 0, sm, nullptr);
-}
-
-// Inclusive sum of one int64 per lane over a wave (lane l gets lanes 0..l) in DPP moves: shifts by
-// 1, 2, 4, 8 within each 16-lane row (lanes shifted in from outside the row read 0), then lane 15
-// broadcast into rows 1 and 3 and lane 31 into rows 2 and 3 -- the classic GCN wave scan, without
-// the LDS round trips of ds_bpermute shuffles.  The 64-bit value moves as two 32-bit halves.
-template <int kCtrl, int kRowMask>
-__device__ __forceinline__ int64_t dpp_add64(int64_t x) {
-  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, uint32_t(uint64_t(x)), kCtrl, kRowMask, 0xF, true);
-  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, uint32_t(uint64_t(x) >> 32), kCtrl, kRowMask, 0xF, true);
-  return x + int64_t((uint64_t(hi) << 32) | lo);
-}
-__device__ __forceinline__ int64_t wave_incl_scan64(int64_t x) {
-  x = dpp_add64<0x111, 0xF>(x);  // row_shr:1
-  x = dpp_add64<0x112, 0xF>(x);  // row_shr:2
-  x = dpp_add64<0x114, 0xF>(x);  // row_shr:4
-  x = dpp_add64<0x118, 0xF>(x);  // row_shr:8
-  x = dpp_add64<0x142, 0xA>(x);  // row_bcast:15 into rows 1, 3
-  x = dpp_add64<0x143, 0xC>(x);  // row_bcast:31 into rows 2, 3
-  return x;
 }
 
 // Sums and scans of one int64 per thread over the kThreads threads of a workgroup.
