@@ -179,7 +179,10 @@ pa_status pa_attention_shared_prefix(const pa_desc* desc, const void* q, const v
  * through the bf16 MFMAs; the K scale multiplies a page's scores and the V
  * scale its softmax weights before those are rounded to bf16.  Same single
  * launch, workspace (sized by pa_workspace_size for the bf16 descriptor) and
- * errors as pa_attention.
+ * errors as pa_attention.  The grains are cut as in pa_plan's description
+ * except that a chunk of a row-split unit weighs 10 instead of 4 (its K and V
+ * are widened to bf16 on the way to the MFMAs, while a decode chunk moves half
+ * the bytes), so that pa_plan does not describe this call's grains.
  */
 pa_status pa_attention_fp8kv(const pa_desc* desc, const void* q, const uint8_t* k_pool, const uint8_t* v_pool,
                              const float* k_scale, const float* v_scale, const int32_t* block_table,

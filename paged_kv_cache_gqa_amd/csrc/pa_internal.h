@@ -35,6 +35,14 @@ constexpr int kCostKeySplit = 4;
 #define PA_COST_ROW (kRowTiles == 1 ? 4 : 5)
 #endif
 constexpr int kCostRowSplit = PA_COST_ROW;
+// FP8 pages change the ratio: a key-split chunk moves half the bytes, while a row-split chunk also
+// widens its K and V fragments to bf16 before the MFMAs.  Fitted on MI355X (the mixed prefill +
+// decode batch with FP8 pages, µs per launch): row-split weight 4: 90.9, 8: 74.6, 10: 70.9,
+// 12: 72.4, 14: 75.3, 16: 79.8.
+#ifndef PA_COST_ROW_FP8
+#define PA_COST_ROW_FP8 10
+#endif
+constexpr int kCostRowSplitFp8 = PA_COST_ROW_FP8;
 // Fixed cost charged at the start of every unit (row and page-table loads, the
 // pipeline fill, the cross-wave merge and the output), so that grains that start
 // many units get fewer chunks.  Fitted on MI355X (bench.py, configurations 2-5):
@@ -55,8 +63,9 @@ inline __host__ __device__ int unit_start_cost(bool key_split, int rows) {
 
 // The cost axis is cut into S equal grains, one per workgroup (measured on
 // MI355X: more, smaller grains per workgroup only added merge work), with
-//   S = min(grid, Ck / kCostKeySplit + Cr / (kRowGrainChunks * kCostRowSplit))
-// for Ck, Cr the total cost of key-split and of row-split units: decode work
+//   S = min(grid, Ck / kCostKeySplit + Cr / (kRowGrainChunks * rw))
+// for Ck, Cr the total cost of key-split and of row-split units (rw: the row-split chunk weight of
+// the page format): decode work
 // may be cut down to one chunk per grain (its partial results are a few rows),
 // prefill work no finer than kRowGrainChunks chunks per grain (a piece of a
 // 128-row unit leaves 64 KiB of partial state to merge).  Grain boundaries --
@@ -66,8 +75,8 @@ inline __host__ __device__ int unit_start_cost(bool key_split, int rows) {
 #define PA_ROW_GRAIN_CHUNKS 8
 #endif
 constexpr int kRowGrainChunks = PA_ROW_GRAIN_CHUNKS;
-inline __host__ __device__ int64_t grain_count(int64_t ck, int64_t cr, int grid) {
-  int64_t s = ck / kCostKeySplit + cr / (int64_t(kRowGrainChunks) * kCostRowSplit);
+inline __host__ __device__ int64_t grain_count(int64_t ck, int64_t cr, int grid, int rw = kCostRowSplit) {
+  int64_t s = ck / kCostKeySplit + cr / (int64_t(kRowGrainChunks) * rw);
   if (s > grid) s = grid;
   if (s < 1 && ck + cr > 0) s = 1;
   return s;

@@ -247,6 +247,7 @@ struct Bf16 {
   static constexpr int kVLoads = 2 * kVF;  // global load instructions per chunk of V (two pages per tile)
   static constexpr int kEbKV = kEb;        // bytes per K/V pool element
   static constexpr bool kScaled = false;   // per-(page, head) K/V scales
+  static constexpr int kCostRow = kCostRowSplit;  // planner weight of a row-split chunk
   using VRaw = u32x4_t;                    // a V fragment as loaded
 
   __device__ static int q_off(int f, int quad) { return (32 * f + 8 * quad) * kEb; }
@@ -358,6 +359,7 @@ struct F32 {
   static constexpr int kVLoads = kVF;
   static constexpr int kEbKV = kEb;
   static constexpr bool kScaled = false;
+  static constexpr int kCostRow = kCostRowSplit;
   using VRaw = u32x4_t;
 
   __device__ static int q_off(int f, int quad) { return (16 * f + 4 * quad) * kEb; }
@@ -458,6 +460,7 @@ struct Fp8Kv {
   static constexpr bool kBf16 = true;
   static constexpr int kVLoads = 2 * kVF;
   static constexpr bool kScaled = true;
+  static constexpr int kCostRow = kCostRowSplitFp8;
   using VRaw = u32x2_t;  // 4 codes of page 0 (keys 4q..4q+3), 4 codes of page 1
 
   __device__ static int q_off(int f, int quad) { return (32 * f + 8 * quad) * kEb; }
@@ -1273,6 +1276,7 @@ __device__ __forceinline__ int64_t block_chunks_before(int n, int qn, int G, boo
   return int64_t(r) * h + floor_sum(uint32_t(r), uint32_t(kChunkKeys * G), kBlockRows, uint32_t(b));
 }
 
+template <int kRw = kCostRowSplit>
 __device__ SeqUnits seq_units(int n, int q0, int qn, int G, bool full) {
   SeqUnits q;
   q.n = n;
@@ -1291,7 +1295,7 @@ __device__ SeqUnits seq_units(int n, int q0, int qn, int G, bool full) {
     q.nb = ceil_div(q.rows, kBlockRows);
     // the last block's last row is the window's last token: it sees all n keys
     const int64_t ch = block_chunks_before(n, qn, G, full, q.nb - 1) + ceil_div(n, kChunkKeys);
-    q.per_head = int64_t(q.nb) * kCostStartRow + ch * kCostRowSplit;
+    q.per_head = int64_t(q.nb) * kCostStartRow + ch * kRw;
   }
   return q;
 }
@@ -1306,10 +1310,12 @@ __device__ __forceinline__ int64_t chunk_start(const pa_plan_unit& U, int i) {
 }
 
 // Cost from the start of a kv head's row blocks to the start of block rb (rb < nb).
+template <int kRw>
 __device__ __forceinline__ int64_t block_start(const SeqUnits& q, int G, int rb) {
-  return int64_t(rb) * kCostStartRow + block_chunks_before(q.n, q.qn, G, q.full, rb) * kCostRowSplit;
+  return int64_t(rb) * kCostStartRow + block_chunks_before(q.n, q.qn, G, q.full, rb) * kRw;
 }
 
+template <int kRw>
 __device__ pa_plan_unit make_unit(int s, const SeqUnits& q, int G, int g, int rb, int64_t cost0) {
   pa_plan_unit U;
   U.seq = s;
@@ -1319,7 +1325,7 @@ __device__ pa_plan_unit make_unit(int s, const SeqUnits& q, int G, int g, int rb
   U.n_keys = q.split ? q.n : block_keys(q.n, q.qn, G, rb, q.full);
   U.n_chunks = ceil_div(U.n_keys, kChunkKeys);
   U.kind = q.split ? 0 : 1;
-  U.cost_weight = q.split ? kCostKeySplit : kCostRowSplit;
+  U.cost_weight = q.split ? kCostKeySplit : kRw;
   U.cost0 = cost0;
   U.first_slot = 0;
   U.n_pieces = 0;
@@ -1334,19 +1340,20 @@ struct UnitCursor {
   pa_plan_unit U;
 };
 
-template <class P>
+template <int kRw, class P>
 __device__ void cursor_load_seq(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl) {
   const int q0 = qsl[cu.s];
-  cu.q = seq_units(seq_lens[cu.s], q0, qsl[cu.s + 1] - q0, v.group, v.full_rows != 0);
+  cu.q = seq_units<kRw>(seq_lens[cu.s], q0, qsl[cu.s + 1] - q0, v.group, v.full_rows != 0);
 }
 
 // Position the cursor on the unit of sequence s (n keys, queries q0 .. q0 + qn - 1, starting at
 // cost seq_base) whose cost range holds c.
+template <int kRw>
 __device__ void cursor_place(UnitCursor& cu, const PlanView& v, int s, int64_t seq_base, int n, int q0, int qn,
                              int64_t c) {
   cu.s = s;
   cu.seq_base = seq_base;
-  cu.q = seq_units(n, q0, qn, v.group, v.full_rows != 0);
+  cu.q = seq_units<kRw>(n, q0, qn, v.group, v.full_rows != 0);
   const int64_t off = c - cu.seq_base;
   cu.g = int(off / cu.q.per_head);
   int64_t acc = cu.seq_base + int64_t(cu.g) * cu.q.per_head;
@@ -1356,12 +1363,12 @@ __device__ void cursor_place(UnitCursor& cu, const PlanView& v, int s, int64_t s
     int lo = 0, hi = cu.q.nb - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (acc + block_start(cu.q, v.group, mid) <= c) lo = mid; else hi = mid - 1;
+      if (acc + block_start<kRw>(cu.q, v.group, mid) <= c) lo = mid; else hi = mid - 1;
     }
     cu.rb = lo;
-    acc += block_start(cu.q, v.group, lo);
+    acc += block_start<kRw>(cu.q, v.group, lo);
   }
-  cu.U = make_unit(cu.s, cu.q, v.group, cu.g, cu.rb, acc);
+  cu.U = make_unit<kRw>(cu.s, cu.q, v.group, cu.g, cu.rb, acc);
 }
 
 // cursor_place done by all 64 lanes of a wave together (every lane gets the same cursor): the
@@ -1369,11 +1376,12 @@ __device__ void cursor_place(UnitCursor& cu, const PlanView& v, int s, int64_t s
 // at or below c.  Up to 64 blocks: lane r takes block r's chunk count and a wave scan of the
 // counts gives every start; more blocks: lanes evaluate floor-sum starts of 64 candidates per
 // round (two rounds for up to 4096) -- instead of a serial binary search of floor sums.
+template <int kRw>
 __device__ void cursor_place_wave(UnitCursor& cu, const PlanView& v, int s, int64_t seq_base, int n, int q0, int qn,
                                   int64_t c, int lane) {
   cu.s = s;
   cu.seq_base = seq_base;
-  cu.q = seq_units(n, q0, qn, v.group, v.full_rows != 0);
+  cu.q = seq_units<kRw>(n, q0, qn, v.group, v.full_rows != 0);
   const int64_t off = c - cu.seq_base;
   cu.g = int(off / cu.q.per_head);
   int64_t acc = cu.seq_base + int64_t(cu.g) * cu.q.per_head;
@@ -1381,7 +1389,7 @@ __device__ void cursor_place_wave(UnitCursor& cu, const PlanView& v, int s, int6
   if (!cu.q.split && cu.q.nb <= 64) {
     // one block per lane: its chunk count, and a wave scan of the counts gives every block's start
     const int64_t ch = lane < cu.q.nb ? ceil_div(block_keys(n, qn, v.group, lane, cu.q.full), kChunkKeys) : 0;
-    const int64_t start = int64_t(lane) * kCostStartRow + (wave_incl_scan64(ch) - ch) * kCostRowSplit;
+    const int64_t start = int64_t(lane) * kCostStartRow + (wave_incl_scan64(ch) - ch) * kRw;
     const uint64_t below = __ballot(lane < cu.q.nb && acc + start <= c);  // a prefix of the lanes
     const int rb = 63 - __builtin_clzll(below);
     cu.rb = rb;
@@ -1393,7 +1401,7 @@ __device__ void cursor_place_wave(UnitCursor& cu, const PlanView& v, int s, int6
     while (lo < hi) {
       const int step = (hi - lo + 64) / 64;  // candidates lo, lo + step, ... cover [lo, hi]
       const int r = min(lo + lane * step, hi);
-      const uint64_t below = __ballot(acc + block_start(cu.q, v.group, r) <= c);  // a prefix of the lanes
+      const uint64_t below = __ballot(acc + block_start<kRw>(cu.q, v.group, r) <= c);  // a prefix of the lanes
       const int last = 63 - __builtin_clzll(below);
       const int r_last = min(lo + last * step, hi);
       hi = min(r_last + step - 1, hi);
@@ -1401,13 +1409,13 @@ __device__ void cursor_place_wave(UnitCursor& cu, const PlanView& v, int s, int6
       if (step == 1) break;
     }
     cu.rb = lo;
-    acc += block_start(cu.q, v.group, lo);
+    acc += block_start<kRw>(cu.q, v.group, lo);
   }
-  cu.U = make_unit(cu.s, cu.q, v.group, cu.g, cu.rb, acc);
+  cu.U = make_unit<kRw>(cu.s, cu.q, v.group, cu.g, cu.rb, acc);
 }
 
 // Position the cursor on the unit whose cost range holds c (0 <= c < total).
-template <class P, class Q>
+template <int kRw = kCostRowSplit, class P, class Q>
 __device__ void cursor_find(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl, Q seq_cost, int64_t c) {
   int lo = 0, hi = v.num_seqs - 1;  // last s with seq_cost[s] <= c
   while (lo < hi) {
@@ -1415,7 +1423,7 @@ __device__ void cursor_find(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl
     if (seq_cost[mid] <= c) lo = mid; else hi = mid - 1;
   }
   const int q0 = qsl[lo];
-  cursor_place(cu, v, lo, seq_cost[lo], seq_lens[lo], q0, qsl[lo + 1] - q0, c);
+  cursor_place<kRw>(cu, v, lo, seq_cost[lo], seq_lens[lo], q0, qsl[lo + 1] - q0, c);
 }
 
 __device__ __forceinline__ SlotStart slot_from_cursor(const UnitCursor& cu, int64_t c0, int64_t c1) {
@@ -1435,13 +1443,14 @@ __device__ __forceinline__ SlotStart slot_from_cursor(const UnitCursor& cu, int6
 }
 
 // Position the cursor as the planner recorded for one slot.
+template <int kRw = kCostRowSplit>
 __device__ __forceinline__ void cursor_from_slot(UnitCursor& cu, const PlanView& v, const SlotStart& st) {
   cu.s = st.s;
   cu.g = st.g;
   cu.rb = st.rb;
   cu.seq_base = st.seq_base;
-  cu.q = seq_units(st.n, st.q0, st.qn, v.group, v.full_rows != 0);
-  cu.U = make_unit(st.s, cu.q, v.group, st.g, st.rb, st.unit_cost0);
+  cu.q = seq_units<kRw>(st.n, st.q0, st.qn, v.group, v.full_rows != 0);
+  cu.U = make_unit<kRw>(st.s, cu.q, v.group, st.g, st.rb, st.unit_cost0);
 }
 
 __device__ __forceinline__ SlotStart load_slot(cptr<SlotStart> p) {
@@ -1460,7 +1469,7 @@ __device__ __forceinline__ SlotStart load_slot(cptr<SlotStart> p) {
 }
 
 // Advance to the next unit; returns false past the last one.
-template <class P>
+template <int kRw = kCostRowSplit, class P>
 __device__ bool cursor_next(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl) {
   const int64_t next_cost = cu.U.cost0 + unit_cost(cu.U);
   if (++cu.rb >= cu.q.nb) {
@@ -1470,11 +1479,11 @@ __device__ bool cursor_next(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl
       do {
         cu.seq_base += int64_t(v.num_kv_heads) * cu.q.per_head;
         if (++cu.s >= v.num_seqs) return false;
-        cursor_load_seq(cu, v, seq_lens, qsl);
+        cursor_load_seq<kRw>(cu, v, seq_lens, qsl);
       } while (cu.q.nb == 0);
     }
   }
-  cu.U = make_unit(cu.s, cu.q, v.group, cu.g, cu.rb, next_cost);
+  cu.U = make_unit<kRw>(cu.s, cu.q, v.group, cu.g, cu.rb, next_cost);
   return true;
 }
 
@@ -1770,7 +1779,7 @@ __device__ void run_keysplit_stream(const AttnArgs& A, UnitCursor& cu, Piece p, 
     RowInfo rnext{0, 0, -1, false};
     {
       UnitCursor nc = cu;
-      nxt = cursor_next(nc, v, seq_lens, qsl) && nc.U.cost0 < c1 && same_kind(nc.U);
+      nxt = cursor_next<TR::kCostRow>(nc, v, seq_lens, qsl) && nc.U.cost0 < c1 && same_kind(nc.U);
       if (nxt) {
         const Piece np = piece_of(nc.U, c0, c1, grain);
         nxt = np.i0 < np.i1;
@@ -1900,7 +1909,7 @@ __device__ void run_keysplit_stream(const AttnArgs& A, UnitCursor& cu, Piece p, 
       lds_barrier();  // the merge reads are done (each waited in place) before the region is rewritten
     }
     if (!nxt) return;
-    cursor_next(cu, v, seq_lens, qsl);
+    cursor_next<TR::kCostRow>(cu, v, seq_lens, qsl);
     p = piece_of(cu.U, c0, c1, grain);
     pre = true;
   }
@@ -1918,7 +1927,7 @@ __device__ __forceinline__ void run_grain(const AttnArgs& A, int grain, const Sl
   const cptr<int32_t> seq_lens = ro(v.seq_lens);
   const cptr<int32_t> qsl = ro(v.qsl);
   UnitCursor cu;
-  cursor_from_slot(cu, v, st);
+  cursor_from_slot<TR::kCostRow>(cu, v, st);
   do {
     const pa_plan_unit& U = cu.U;
     if (U.cost0 >= c1) break;
@@ -1948,7 +1957,7 @@ __device__ __forceinline__ void run_grain(const AttnArgs& A, int grain, const Sl
           arrive_and_merge<TR>(A, cu.U, S, C, flag, reinterpret_cast<float*>(sm.buf));
       }
     }
-  } while (cursor_next(cu, v, seq_lens, qsl));
+  } while (cursor_next<TR::kCostRow>(cu, v, seq_lens, qsl));
 }
 
 // Staged path: workgroup b runs grain b, b + grid, ... of the plan in the workspace.
@@ -2038,7 +2047,7 @@ struct PreLds {
 
 // Cost of the kPer sequences of this thread in the block of kThreads * kPer at `base`
 // (c), and the part of their sum that is row-split work (returned).
-template <int kPer>
+template <int kPer, int kRw>
 __device__ __forceinline__ int64_t block_seq_costs(const PlanView& v, cptr<int32_t> sl, cptr<int32_t> qsl, int base,
                                                    int64_t (&c)[kPer], int (&n)[kPer], int (&q0)[kPer],
                                                    int (&qn)[kPer]) {
@@ -2052,7 +2061,7 @@ __device__ __forceinline__ int64_t block_seq_costs(const PlanView& v, cptr<int32
       n[e] = sl[s];
       q0[e] = qsl[s];
       qn[e] = qsl[s + 1] - q0[e];
-      const SeqUnits q = seq_units(n[e], q0[e], qn[e], v.group, v.full_rows != 0);
+      const SeqUnits q = seq_units<kRw>(n[e], q0[e], qn[e], v.group, v.full_rows != 0);
       c[e] = int64_t(v.num_kv_heads) * q.per_head;
       if (!q.split) row += c[e];
     }
@@ -2088,13 +2097,13 @@ __device__ __forceinline__ int64_t grain_of_block(int b, int grid, int64_t S) {
 // start in pl.st.  Each thread takes kPer sequences per pass of kThreads * kPer (one when the
 // batch fits one pass, so that no thread computes several sequences' costs in a row).  Returns
 // the grain index; S or more means the workgroup has none.
-template <int kPer, bool kSolo>
+template <int kPer, bool kSolo, int kRw>
 __device__ __forceinline__ int64_t plan_grain(const PlanView& v, PreLds& pl, int64_t& S, int64_t& C) {
   const cptr<int32_t> sl = ro(v.seq_lens), qsl = ro(v.qsl);
   constexpr int kBlock = kThreads * kPer;
   int64_t c[kPer];
   int n[kPer], q0[kPer], qn[kPer];
-  const int64_t row0 = block_seq_costs<kPer>(v, sl, qsl, 0, c, n, q0, qn);  // kept for the search below
+  const int64_t row0 = block_seq_costs<kPer, kRw>(v, sl, qsl, 0, c, n, q0, qn);  // kept for the search below
   C = 0;
   int64_t Cr = 0;
   // one block of sequences: the totals and this block's prefix come from one exchange
@@ -2109,7 +2118,7 @@ __device__ __forceinline__ int64_t plan_grain(const PlanView& v, PreLds& pl, int
   for (int base = 0; !one && base < v.num_seqs; base += kBlock) {
     int64_t c2[kPer];
     int n2[kPer], q02[kPer], qn2[kPer];
-    const int64_t row = base > 0 ? block_seq_costs<kPer>(v, sl, qsl, base, c2, n2, q02, qn2) : row0;
+    const int64_t row = base > 0 ? block_seq_costs<kPer, kRw>(v, sl, qsl, base, c2, n2, q02, qn2) : row0;
     int64_t x = 0;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) x += base > 0 ? c2[e] : c[e];
@@ -2123,13 +2132,13 @@ __device__ __forceinline__ int64_t plan_grain(const PlanView& v, PreLds& pl, int
     S = 0;
     return 0;
   }
-  S = grain_count(C - Cr, Cr, grid);
+  S = grain_count(C - Cr, Cr, grid, kRw);
   const int64_t k = grain_of_block(int(blockIdx.x), grid, S);
   if (k >= S) return k;
   const int64_t c0 = slice_begin(k, S, C), c1 = slice_begin(k + 1, S, C);
   int64_t carry = 0;
   for (int base = 0; base < v.num_seqs; base += kBlock) {
-    if (base > 0) block_seq_costs<kPer>(v, sl, qsl, base, c, n, q0, qn);
+    if (base > 0) block_seq_costs<kPer, kRw>(v, sl, qsl, base, c, n, q0, qn);
     int64_t x = 0;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) x += c[e];
@@ -2154,7 +2163,7 @@ __device__ __forceinline__ int64_t plan_grain(const PlanView& v, PreLds& pl, int
   __syncthreads();
   if (threadIdx.x < 64) {  // wave 0 places the cursor
     UnitCursor cu;
-    cursor_place_wave(cu, v, pl.hold_s, pl.hold_base, pl.hold_n, pl.hold_q0, pl.hold_qn, c0, int(threadIdx.x));
+    cursor_place_wave<kRw>(cu, v, pl.hold_s, pl.hold_base, pl.hold_n, pl.hold_q0, pl.hold_qn, c0, int(threadIdx.x));
     if (threadIdx.x == 0) pl.st = slot_from_cursor(cu, c0, c1);
   }
   __syncthreads();
@@ -2169,8 +2178,8 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fused_kernel(AttnArgs A
   __shared__ PreLds pl;
   int64_t S, C;
   constexpr bool kSolo = !TR::kScaled;  // FP8 pages stream faster with both workgroups of a CU
-  const int64_t k = A.plan.num_seqs <= kThreads ? plan_grain<1, kSolo>(A.plan, pl, S, C)
-                                                : plan_grain<4, kSolo>(A.plan, pl, S, C);
+  const int64_t k = A.plan.num_seqs <= kThreads ? plan_grain<1, kSolo, TR::kCostRow>(A.plan, pl, S, C)
+                                                : plan_grain<4, kSolo, TR::kCostRow>(A.plan, pl, S, C);
   if (k >= S) return;
   const SlotStart st = pl.st;
   run_grain<TR, true, kTree>(A, int(k), st, S, C, sm, &pl.flag);
