@@ -305,7 +305,7 @@ def main() -> int:
     if args.record_traffic:
         from paged_kv_cache_gqa_amd import workloads as W
         name = W.CONFIG_NAMES[args.config] + ("" if args.part == "all" else f"-{args.part}-part") + \
-            ("-tree" if args.op == "tree" else "")
+            {"tree": "-tree", "fp8": "-fp8kv"}.get(args.op, "")
         kernel = "attention_kernel" if args.staged else "attention_fused_kernel"
         print(json.dumps(record_traffic(name, *args.record_traffic, kernel=kernel)))
         return 0
