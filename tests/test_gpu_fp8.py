@@ -59,6 +59,30 @@ def test_fp8_random(case):
     check(w, out, lse)
 
 
+MIXED = [
+    # seed, prefill windows, decode sequences, Hq, Hkv, D
+    (121, 3, 60, 8, 1, 128),
+    (122, 2, 90, 32, 8, 128),
+    (123, 4, 40, 16, 2, 64),
+]
+
+
+@pytest.mark.parametrize("case", MIXED, ids=[f"s{c[0]}-P{c[1]}-D{c[2]}-G{c[3] // c[4]}-D{c[5]}" for c in MIXED])
+def test_fp8_mixed_prefill_decode(case):
+    """Prefill windows (row-split units) and decode sequences (key-split units) in one batch: the
+    planner's FP8 weights put the grain boundaries inside units of both kinds."""
+    seed, n_pre, n_dec, Hq, Hkv, D = case
+    rng = np.random.default_rng(seed)
+    prior = rng.integers(0, 700, n_pre, endpoint=True)
+    q_pre = rng.integers(65, 400, n_pre, endpoint=True)
+    n_d = rng.integers(200, 2500, n_dec, endpoint=True)
+    n = np.concatenate([prior + q_pre, n_d])
+    ql = np.concatenate([q_pre, np.ones(n_dec, dtype=np.int64)])
+    w = W.to_fp8(W.build(f"mixed-{seed}", seed, n, ql, Hq, Hkv, D, "bf16", rng=rng))
+    out, lse = run_fp8(w)
+    check(w, out, lse)
+
+
 @pytest.mark.parametrize("c", [2, 3, 4])
 def test_fp8_full_config(c):
     w = W.to_fp8(W.make_config(c))
