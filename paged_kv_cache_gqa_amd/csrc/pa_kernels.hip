@@ -432,11 +432,14 @@ struct F32 {
   __device__ static void store_out(char* dst, f32x4_t o) { *reinterpret_cast<f32x4_t*>(dst) = o; }
 };
 
-// OCP FP8 E4M3 -> bf16, four values (exact: every E4M3 value is a bf16 value).
+// OCP FP8 E4M3 -> bf16, four values (exact: every E4M3 value is a bf16 value), two per
+// v_cvt_scalef32_pk_bf16_fp8 with scale 1.  A probe over all 256 codes on MI355X gave the same bits
+// as v_cvt_pk_f32_fp8 followed by v_cvt_pk_bf16_f32 (NaN codes: NaN both ways), in half the
+// instructions.
 __device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t x) {
-  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(int(x), false);  // bytes 0, 1
-  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(int(x), true);   // bytes 2, 3
-  return uint2{pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1])};
+  const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);  // bytes 0, 1
+  const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true);   // bytes 2, 3
+  return uint2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
 }
 __device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(u32x2_t x) {
   const uint2 lo = fp8x4_to_bf16x4(x[0]), hi = fp8x4_to_bf16x4(x[1]);
