@@ -180,7 +180,7 @@ pa_status pa_attention_shared_prefix(const pa_desc* desc, const void* q, const v
  * scale its softmax weights before those are rounded to bf16.  Same single
  * launch, workspace (sized by pa_workspace_size for the bf16 descriptor) and
  * errors as pa_attention.  The grains are cut as in pa_plan's description
- * except that a chunk of a row-split unit weighs 10 instead of 4 (its K and V
+ * except that a chunk of a row-split unit weighs 8 instead of 4 (its K and V
  * are widened to bf16 on the way to the MFMAs, while a decode chunk moves half
  * the bytes), so that pa_plan does not describe this call's grains.
  */

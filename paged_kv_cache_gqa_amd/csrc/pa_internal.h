@@ -37,10 +37,11 @@ constexpr int kCostKeySplit = 4;
 constexpr int kCostRowSplit = PA_COST_ROW;
 // FP8 pages change the ratio: a key-split chunk moves half the bytes, while a row-split chunk also
 // widens its K and V fragments to bf16 before the MFMAs.  Fitted on MI355X (the mixed prefill +
-// decode batch with FP8 pages, µs per launch): row-split weight 4: 90.9, 8: 74.6, 10: 70.9,
-// 12: 72.4, 14: 75.3, 16: 79.8.
+// decode batch with FP8 pages, µs per launch, three runs each on one machine): row-split weight
+// 6: 68.8, 7: 65.7, 8: 65.0, 9: 65.3, 10: 66.5, 11: 67.7 (with the two-instruction widening of
+// codes to bf16 the optimum was 10; 4, bf16's weight, took 90.9).
 #ifndef PA_COST_ROW_FP8
-#define PA_COST_ROW_FP8 10
+#define PA_COST_ROW_FP8 8
 #endif
 constexpr int kCostRowSplitFp8 = PA_COST_ROW_FP8;
 // Fixed cost charged at the start of every unit (row and page-table loads, the
