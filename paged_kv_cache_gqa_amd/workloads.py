@@ -273,6 +273,24 @@ def make_random(seed: int, num_seqs: int, max_len: int, num_q_heads: int, num_kv
                  num_pages=used + slack_pages, rng=rng, **kw)
 
 
+def make_interleaved_mixed(seed: int, dtype: str) -> Workload:
+    """Prefill windows (2..300 tokens over a prior context of 0..900 keys) and decode / verify
+    sequences (1..6 tokens over 1..3000 keys) in a shuffled batch order, with a random kv-head count
+    (1, 2, 8), GQA group (1, 4, 8) and head dim (64, 128)."""
+    rng = np.random.default_rng(seed)
+    hkv = int(rng.choice([1, 2, 8]))
+    g = int(rng.choice([1, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    n_pre, n_dec = int(rng.integers(1, 5)), int(rng.integers(5, 120))
+    prior = rng.integers(0, 900, n_pre, endpoint=True)
+    q_pre = rng.integers(2, 300, n_pre, endpoint=True)
+    n_d = rng.integers(1, 3000, n_dec, endpoint=True)
+    q_d = np.minimum(n_d, rng.integers(1, 6, n_dec, endpoint=True))
+    n, ql = np.concatenate([prior + q_pre, n_d]), np.concatenate([q_pre, q_d])
+    perm = rng.permutation(len(n))
+    return build(f"interleaved-{seed}", seed, n[perm], ql[perm], g * hkv, hkv, d, dtype, rng=rng)
+
+
 def subset(w: Workload, seqs) -> Workload:
     """The same pools with only the listed sequences (block-table rows and queries)."""
     seqs = np.asarray(seqs, dtype=np.int64)

@@ -83,6 +83,14 @@ def test_fp8_mixed_prefill_decode(case):
     check(w, out, lse)
 
 
+@pytest.mark.parametrize("seed", [302, 308, 321])
+def test_fp8_interleaved_mixed_batch(seed):
+    """Prefill and decode / verify sequences in shuffled batch order, with FP8 pages."""
+    w = W.to_fp8(W.make_interleaved_mixed(seed, "bf16"))
+    out, lse = run_fp8(w)
+    check(w, out, lse)
+
+
 @pytest.mark.parametrize("c", [2, 3, 4])
 def test_fp8_full_config(c):
     w = W.to_fp8(W.make_config(c))

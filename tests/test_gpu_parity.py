@@ -48,6 +48,13 @@ def check(w, out, lse, ref=None, rows=None):
             assert eo.mean() <= mean and el.mean() <= mean, msg
 
 
+@pytest.mark.parametrize("seed", [301, 305, 310, 317])
+def test_interleaved_mixed_batch(seed):
+    w = W.make_interleaved_mixed(seed, "bf16")
+    out, lse = run_gpu(w)
+    check(w, out, lse)
+
+
 # ---------------------------------------------------------------------------
 # small shapes: several tiles, ragged tails, windows, both dtypes and head dims
 # ---------------------------------------------------------------------------
