@@ -9,8 +9,11 @@ several copies and step i reads copy i % n_copies, so that every step's K/V
 were last touched more than 1 GiB of traffic earlier (the 256 MB MALL cannot
 serve them); no flush kernel runs inside the timed region.
 
-Default workload: Llama-3-8B-shaped decode (64 sequences, context uniform in
-[512, 4096], 32 query / 8 KV heads, head dim 128, bf16, 16-slot pages).
+Default workload: the largest configuration, long-context reasoning decode
+(256 sequences, one query token each, context lognormal with median 8192 clipped
+to [1024, 32768], 64 query / 8 KV heads, head dim 128, bf16, 16-slot pages, 1%
+of keys scaled by 4); its 13 GB of K/V pools fit one GPU's HBM.  --config 1-4
+select the other workloads.
 `value` is algorithmic bytes (every valid K/V row once per KV head, Q, out,
 LSE, block-table entries) divided by the wall time per step over K steps issued
 back to back.  The roofline's kernel duration is the span of two HIP events on
@@ -131,8 +134,21 @@ def cpu_baseline(w, alg_bytes: int, min_seconds: float = 10.0, min_runs: int = 3
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
     return {"value": round(alg_bytes / t / 1e9, 4), "unit": "GB/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"the whole batch (all sequences, all heads) run {len(times)} times "
                       f"({sum(times):.1f} s in all), median {t:.3f} s per batch; fp64 two-pass softmax"}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (empty if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
 
 
 def bench_append(args, w) -> int:
@@ -159,7 +175,7 @@ def bench_append(args, w) -> int:
     alg_bytes = 2 * 2 * T * Hkv * D * k_new.element_size() + 4 * pages
     stream = torch.cuda.current_stream()
     desc = B.PaDesc(num_seqs=w.num_seqs, num_q_tokens=T, num_q_heads=Hkv, num_kv_heads=Hkv, head_dim=D,
-                    page_size=16, num_pages=w.num_pages, max_pages_per_seq=w.max_pages_per_seq,
+                    page_size=16, num_pages=w.num_pages, max_pages_per_seq=w.max_pages_per_seq, max_seq_len=0,
                     dtype=B._DTYPES[dt], scale=1.0)
     vp = ctypes.c_void_p
     cargs = (ctypes.byref(desc), vp(k_new.data_ptr()), vp(v_new.data_ptr()), vp(t["block_table"].data_ptr()),
@@ -275,7 +291,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5],
+                    help="workload (default 5: long-context decode, the largest that runs on one GPU)")
     ap.add_argument("--part", default="all", choices=["all", "prefill", "decode"],
                     help="configuration 3 only: time its prefill chunks or its decode rows alone")
     ap.add_argument("--op", default="attention", choices=["attention", "append", "tree", "fp8", "prefix"],

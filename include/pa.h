@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 #define PA_PAGE_SIZE 16
 
 typedef enum pa_status {
@@ -88,6 +88,11 @@ typedef struct pa_desc {
   int32_t page_size;         /* must be PA_PAGE_SIZE (16) */
   int32_t num_pages;         /* NP >= 1: pages in each pool */
   int32_t max_pages_per_seq; /* block_table row stride, >= ceil(max n_s / 16) */
+  int32_t max_seq_len;       /* host upper bound on every seq_lens[s], 0 <= max_seq_len <=
+                                max_pages_per_seq * 16; 0 = not stated (the bound is then
+                                max_pages_per_seq * 16).  Neither the workspace nor the plan
+                                depends on it: the single launch derives its work list on the
+                                device from seq_lens.  pa_validate reports a longer sequence. */
   int32_t dtype;             /* pa_dtype of q, k_pool, v_pool and out */
   float scale;               /* multiplies q.k before the softmax */
 } pa_desc;
@@ -95,8 +100,10 @@ typedef struct pa_desc {
 /* PA_ABI_VERSION of the loaded library. */
 int pa_abi_version(void);
 
-/* Static, human-readable name of a status code (never NULL). */
+/* Static, human-readable name of a status code (never NULL).  pa_status_str is the same
+ * function under a second name. */
 const char* pa_status_string(pa_status status);
+const char* pa_status_str(pa_status status);
 
 /* Host-only check of a descriptor (no HIP call): PA_OK, PA_ERR_BAD_SHAPE or PA_ERR_UNSUPPORTED. */
 pa_status pa_check_desc(const pa_desc* desc);
@@ -114,6 +121,10 @@ pa_status pa_check_desc(const pa_desc* desc);
  * does pa_plan.  A workspace sized for a larger descriptor serves smaller ones.
  */
 pa_status pa_workspace_size(const pa_desc* desc, size_t* bytes);
+
+/* The same size as a return value: pa_workspace_size's *bytes, or 0 when pa_workspace_size
+ * would return an error (NULL or bad descriptor, no HIP device). */
+size_t pa_workspace_bytes(const pa_desc* desc);
 
 /*
  * Zero the workspace's arrival counters (enqueues one small fill kernel on
@@ -311,8 +322,8 @@ pa_status pa_append_kv(const pa_desc* desc, const void* k_new, const void* v_new
 /*
  * Check the batch contents on the device: query_start_loc starts at 0, is
  * non-decreasing and ends at T_q; 0 <= q_len <= seq_len; ceil(seq_len/16) <=
- * max_pages_per_seq; every block-table entry a sequence reads lies in
- * [0, num_pages).  Uses the first 256 bytes of `workspace` and synchronizes
+ * max_pages_per_seq; seq_len <= max_seq_len when that is stated; every
+ * block-table entry a sequence reads lies in [0, num_pages).  Uses the first 256 bytes of `workspace` and synchronizes
  * `stream`.  Returns PA_OK or PA_ERR_INVALID_CONTENT.
  */
 pa_status pa_validate(const pa_desc* desc, const int32_t* block_table, const int32_t* seq_lens,

@@ -5,11 +5,18 @@ torch supplies device memory and the current stream; all arithmetic runs in
 the gfx950 kernels of ``libpa_mi355x.so``.  There is no fallback: if the
 library is missing or a call fails, a ``PagedAttentionError`` is raised.
 
+Streams: every call takes ``stream=`` (a ``torch.cuda.Stream``; default: torch's
+current stream).  Whatever the binding allocates for a call (out, lse, a
+workspace and its counter initialisation, contiguous copies of inputs) is
+allocated and initialised with that stream current, so torch's caching
+allocator orders its reuse after the call's kernels on that stream.
+
 torch is imported before the library is opened so that the library binds to
 the HIP runtime torch already loaded (one runtime per process).
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -18,6 +25,7 @@ import torch
 from .build import LIB_PATH
 
 PAGE_SIZE = 16
+ABI_VERSION = 2
 PA_F32, PA_BF16 = 0, 1
 _DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
 
@@ -33,7 +41,7 @@ class PaDesc(ctypes.Structure):
                 ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("num_pages", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("max_seq_len", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
 
 
 class PlanUnit(ctypes.Structure):
@@ -67,6 +75,10 @@ def lib():
         L.pa_abi_version.restype = ctypes.c_int
         L.pa_status_string.restype = ctypes.c_char_p
         L.pa_status_string.argtypes = [ctypes.c_int]
+        L.pa_status_str.restype = ctypes.c_char_p
+        L.pa_status_str.argtypes = [ctypes.c_int]
+        L.pa_workspace_bytes.restype = sz
+        L.pa_workspace_bytes.argtypes = [dp]
         L.pa_check_desc.argtypes = [dp]
         L.pa_workspace_size.argtypes = [dp, ctypes.POINTER(sz)]
         L.pa_workspace_init.argtypes = [dp, vp, sz, vp]
@@ -88,7 +100,7 @@ def lib():
                      "pa_merge_planned", "pa_plan_read", "pa_gather_kv", "pa_merge", "pa_validate", "pa_append_kv", "pa_attention_tree",
                      "pa_attention_fp8kv", "pa_shared_prefix_workspace_size", "pa_attention_shared_prefix"):
             getattr(L, name).restype = ctypes.c_int
-        if L.pa_abi_version() != 1:
+        if L.pa_abi_version() != ABI_VERSION:
             raise PagedAttentionError("load", -1, "ABI version mismatch")
         _lib = L
     return _lib
@@ -96,6 +108,10 @@ def lib():
 
 def status_string(status: int) -> str:
     return lib().pa_status_string(int(status)).decode()
+
+
+def status_str(status: int) -> str:
+    return lib().pa_status_str(int(status)).decode()
 
 
 def abi_version() -> int:
@@ -117,8 +133,15 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def make_desc(q, k_pool, block_table, seq_lens, scale: float) -> PaDesc:
-    """Descriptor from tensor shapes (host values only; nothing is read from the device)."""
+def _on(stream):
+    """Context in which the call's temporaries are allocated: `stream` made current (torch's
+    allocator then ties them to it), or nothing when the call runs on the current stream."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
+def make_desc(q, k_pool, block_table, seq_lens, scale: float, max_seq_len: int = 0) -> PaDesc:
+    """Descriptor from tensor shapes (host values only; nothing is read from the device).
+    max_seq_len: a known bound on seq_lens, or 0 for none (the block-table width bounds them)."""
     T, Hq, D = q.shape
     NP, Hkv, ps, D2 = k_pool.shape
     if ps != PAGE_SIZE or D2 != D:
@@ -127,7 +150,7 @@ def make_desc(q, k_pool, block_table, seq_lens, scale: float) -> PaDesc:
         raise TypeError(f"unsupported dtype {q.dtype}")
     return PaDesc(num_seqs=seq_lens.shape[0], num_q_tokens=T, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
                   page_size=PAGE_SIZE, num_pages=NP, max_pages_per_seq=block_table.shape[1],
-                  dtype=_DTYPES[q.dtype], scale=float(scale))
+                  max_seq_len=int(max_seq_len), dtype=_DTYPES[q.dtype], scale=float(scale))
 
 
 def check_desc(desc: PaDesc) -> int:
@@ -140,17 +163,23 @@ def workspace_size(desc: PaDesc) -> int:
     return int(n.value)
 
 
+def workspace_bytes(desc: PaDesc) -> int:
+    """pa_workspace_bytes: the workspace size, or 0 for a descriptor pa_workspace_size rejects."""
+    return int(lib().pa_workspace_bytes(ctypes.byref(desc)))
+
+
 def workspace_init(desc: PaDesc, workspace, stream=None) -> None:
     """Zero the workspace's arrival counters (pa_workspace_init)."""
     _check("pa_workspace_init", lib().pa_workspace_init(ctypes.byref(desc), _ptr(workspace), workspace.numel(),
                                                         _stream(stream)))
 
 
-def alloc_workspace(desc: PaDesc, device=None) -> torch.Tensor:
+def alloc_workspace(desc: PaDesc, device=None, stream=None) -> torch.Tensor:
     """A 256-byte-aligned uint8 device buffer of workspace_size(desc) bytes (torch's allocator aligns),
-    initialised with pa_workspace_init."""
-    ws = torch.empty(max(workspace_size(desc), 256), dtype=torch.uint8, device=device or "cuda")
-    workspace_init(desc, ws)
+    allocated on `stream` and initialised there with pa_workspace_init."""
+    with _on(stream):
+        ws = torch.empty(max(workspace_size(desc), 256), dtype=torch.uint8, device=device or "cuda")
+        workspace_init(desc, ws, stream)
     return ws
 
 
@@ -173,17 +202,25 @@ def _check_inputs(q, k_pool, v_pool, block_table, seq_lens, query_start_loc):
         raise ValueError("seq_lens [B], query_start_loc [B+1] and block_table [B][*] disagree")
 
 
+def _outputs(desc: PaDesc, q, out, lse, workspace, stream):
+    """out, lse and workspace of an attention call: the caller's, or allocated (and the workspace's
+    counters zeroed) with the call's stream current."""
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(desc, q.device, stream)
+    return out, lse, workspace
+
+
 def attention(q, k_pool, v_pool, block_table, seq_lens, query_start_loc, scale: float, out=None, lse=None,
               workspace=None, stream=None):
     """Paged causal GQA attention (pa_attention).  Returns (out [T_q][Hq][D], lse [T_q][Hq] float32)."""
     _check_inputs(q, k_pool, v_pool, block_table, seq_lens, query_start_loc)
     desc = make_desc(q, k_pool, block_table, seq_lens, scale)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
-    if workspace is None:
-        workspace = alloc_workspace(desc, q.device)
+    out, lse, workspace = _outputs(desc, q, out, lse, workspace, stream)
     _check("pa_attention", lib().pa_attention(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                               _ptr(block_table), _ptr(seq_lens), _ptr(query_start_loc), _ptr(out),
                                               _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -195,18 +232,14 @@ def attention_tree(q, k_pool, v_pool, block_table, seq_lens, query_start_loc, tr
     """pa_attention_tree: verify windows as draft-token trees.  tree_mask: [T_q] int64 device tensor holding
     each row's uint64 mask bits.  Returns (out, lse)."""
     _check_inputs(q, k_pool, v_pool, block_table, seq_lens, query_start_loc)
-    if not tree_mask.is_cuda or tree_mask.dtype not in (torch.int64, torch.uint64) or tree_mask.shape != q.shape[:1]:
-        raise ValueError("tree_mask must be a [T_q] int64 / uint64 device tensor")
+    if (not tree_mask.is_cuda or tree_mask.dtype not in (torch.int64, torch.uint64) or tree_mask.shape != q.shape[:1]
+            or not tree_mask.is_contiguous()):
+        raise ValueError("tree_mask must be a contiguous [T_q] int64 / uint64 device tensor")
     desc = make_desc(q, k_pool, block_table, seq_lens, scale)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
-    if workspace is None:
-        workspace = alloc_workspace(desc, q.device)
+    out, lse, workspace = _outputs(desc, q, out, lse, workspace, stream)
     _check("pa_attention_tree",
            lib().pa_attention_tree(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
-                                   _ptr(seq_lens), _ptr(query_start_loc), _ptr(tree_mask.contiguous()), _ptr(out),
+                                   _ptr(seq_lens), _ptr(query_start_loc), _ptr(tree_mask), _ptr(out),
                                    _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out, lse
 
@@ -226,14 +259,9 @@ def attention_fp8kv(q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens, 
     T, Hq, D = q.shape
     NP, Hkv = k_pool.shape[:2]
     desc = PaDesc(num_seqs=seq_lens.shape[0], num_q_tokens=T, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
-                  page_size=PAGE_SIZE, num_pages=NP, max_pages_per_seq=block_table.shape[1], dtype=PA_BF16,
-                  scale=float(scale))
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
-    if workspace is None:
-        workspace = alloc_workspace(desc, q.device)
+                  page_size=PAGE_SIZE, num_pages=NP, max_pages_per_seq=block_table.shape[1], max_seq_len=0,
+                  dtype=PA_BF16, scale=float(scale))
+    out, lse, workspace = _outputs(desc, q, out, lse, workspace, stream)
     _check("pa_attention_fp8kv",
            lib().pa_attention_fp8kv(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
                                     _ptr(v_scale), _ptr(block_table), _ptr(seq_lens), _ptr(query_start_loc),
@@ -241,13 +269,14 @@ def attention_fp8kv(q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens, 
     return out, lse
 
 
-def shared_prefix_workspace(desc: PaDesc, num_groups: int, device=None) -> torch.Tensor:
-    """Workspace for pa_attention_shared_prefix (arrival counters initialised)."""
+def shared_prefix_workspace(desc: PaDesc, num_groups: int, device=None, stream=None) -> torch.Tensor:
+    """Workspace for pa_attention_shared_prefix (arrival counters initialised on `stream`)."""
     n = ctypes.c_size_t(0)
     _check("pa_shared_prefix_workspace_size",
            lib().pa_shared_prefix_workspace_size(ctypes.byref(desc), int(num_groups), ctypes.byref(n)))
-    ws = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=device or "cuda")
-    workspace_init(desc, ws)
+    with _on(stream):
+        ws = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=device or "cuda")
+        workspace_init(desc, ws, stream)
     return ws
 
 
@@ -263,12 +292,9 @@ def attention_shared_prefix(q, k_pool, v_pool, block_table, seq_lens, query_star
     if group_start.shape != (G + 1,):
         raise ValueError("group_start must hold num_groups + 1 entries")
     desc = make_desc(q, k_pool, block_table, seq_lens, scale)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
     if workspace is None:
-        workspace = shared_prefix_workspace(desc, G, q.device)
+        workspace = shared_prefix_workspace(desc, G, q.device, stream)
+    out, lse, workspace = _outputs(desc, q, out, lse, workspace, stream)
     _check("pa_attention_shared_prefix",
            lib().pa_attention_shared_prefix(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
                                             _ptr(seq_lens), _ptr(query_start_loc), int(G), _ptr(group_start),
@@ -311,7 +337,8 @@ def plan_read(desc: PaDesc, seq_lens, query_start_loc, workspace, max_units: int
 
 def gather_kv(desc: PaDesc, which: int, pool, block_table, seq_lens, seq: int, n_keys: int, stream=None):
     """Dense [Hkv][n_keys][D] copy of one sequence's K (which=0) or V (which=1) rows."""
-    dense = torch.empty((desc.num_kv_heads, n_keys, desc.head_dim), dtype=pool.dtype, device=pool.device)
+    with _on(stream):
+        dense = torch.empty((desc.num_kv_heads, n_keys, desc.head_dim), dtype=pool.dtype, device=pool.device)
     _check("pa_gather_kv", lib().pa_gather_kv(ctypes.byref(desc), int(which), _ptr(pool), _ptr(block_table),
                                               _ptr(seq_lens), int(seq), int(n_keys), _ptr(dense), _stream(stream)))
     return dense
@@ -329,7 +356,7 @@ def append_kv(k_new, v_new, k_pool, v_pool, block_table, seq_lens, query_start_l
         raise ValueError("k_new / v_new must be [T_q][Hkv][D] in the pools' dtype")
     desc = PaDesc(num_seqs=seq_lens.shape[0], num_q_tokens=T, num_q_heads=Hkv, num_kv_heads=Hkv, head_dim=D,
                   page_size=PAGE_SIZE, num_pages=k_pool.shape[0], max_pages_per_seq=block_table.shape[1],
-                  dtype=_DTYPES[k_pool.dtype], scale=1.0)
+                  max_seq_len=0, dtype=_DTYPES[k_pool.dtype], scale=1.0)
     _check("pa_append_kv", lib().pa_append_kv(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(block_table),
                                               _ptr(seq_lens), _ptr(query_start_loc), _ptr(k_pool), _ptr(v_pool),
                                               _stream(stream)))
@@ -338,9 +365,12 @@ def append_kv(k_new, v_new, k_pool, v_pool, block_table, seq_lens, query_start_l
 def merge(o_parts, lse_parts, out_dtype=torch.float32, stream=None):
     """Log-sum-exp merge (pa_merge) of o_parts [P][rows][D] f32 and lse_parts [P][rows] f32."""
     P, rows, D = o_parts.shape
-    out = torch.empty((rows, D), dtype=out_dtype, device=o_parts.device)
-    lse = torch.empty((rows,), dtype=torch.float32, device=o_parts.device)
-    _check("pa_merge", lib().pa_merge(P, rows, D, _ptr(o_parts.contiguous()), _ptr(lse_parts.contiguous()),
+    with _on(stream):
+        o_parts = o_parts.contiguous()
+        lse_parts = lse_parts.contiguous()
+        out = torch.empty((rows, D), dtype=out_dtype, device=o_parts.device)
+        lse = torch.empty((rows,), dtype=torch.float32, device=o_parts.device)
+    _check("pa_merge", lib().pa_merge(P, rows, D, _ptr(o_parts), _ptr(lse_parts),
                                       _DTYPES[out_dtype], _ptr(out), _ptr(lse), _stream(stream)))
     return out, lse
 

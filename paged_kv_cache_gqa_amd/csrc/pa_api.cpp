@@ -129,8 +129,12 @@ pa::AttnArgs attn_args(const pa_desc& d, const void* q, const void* k, const voi
   a.arrive = ws.arrive;
   a.num_q_heads = d.num_q_heads;
   a.max_pages = d.max_pages_per_seq;
-  a.scale_log2 = std::fabs(d.scale) * 1.44269504088896340736f;
+  // Scores are taken in the base-2 domain with the positive factor |scale| * log2(e); a negative
+  // scale flips Q's sign bits instead.  scale == 0 makes every score 0: Q is cleared (q_keep = 0)
+  // and the factor set to 1, so that masked keys (-inf) never meet a zero factor (-inf * 0 = NaN).
+  a.scale_log2 = d.scale == 0.f ? 1.f : std::fabs(d.scale) * 1.44269504088896340736f;
   a.q_sign = d.scale < 0.f ? (d.dtype == PA_BF16 ? 0x80008000u : 0x80000000u) : 0u;
+  a.q_keep = d.scale == 0.f ? 0u : 0xFFFFFFFFu;
   return a;
 }
 
@@ -139,6 +143,8 @@ pa::AttnArgs attn_args(const pa_desc& d, const void* q, const void* k, const voi
 extern "C" {
 
 int pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char* pa_status_str(pa_status s) { return pa_status_string(s); }
 
 const char* pa_status_string(pa_status s) {
   switch (s) {
@@ -158,6 +164,8 @@ pa_status pa_check_desc(const pa_desc* d) {
   if (d->num_seqs < 0 || d->num_q_tokens < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1) return PA_ERR_BAD_SHAPE;
   if (d->num_q_heads % d->num_kv_heads != 0) return PA_ERR_BAD_SHAPE;
   if (d->num_pages < 1 || d->max_pages_per_seq < 1) return PA_ERR_BAD_SHAPE;
+  if (d->max_seq_len < 0 || int64_t(d->max_seq_len) > int64_t(d->max_pages_per_seq) * PA_PAGE_SIZE)
+    return PA_ERR_BAD_SHAPE;
   if (d->head_dim != 64 && d->head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (d->page_size != PA_PAGE_SIZE) return PA_ERR_UNSUPPORTED;
   if (d->dtype != PA_F32 && d->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
@@ -177,6 +185,11 @@ pa_status pa_workspace_size(const pa_desc* desc, size_t* bytes) {
   if (gs != PA_OK) return gs;
   *bytes = pa::ws_layout(*desc, grid, max_grid).total;
   return PA_OK;
+}
+
+size_t pa_workspace_bytes(const pa_desc* desc) {
+  size_t n = 0;
+  return pa_workspace_size(desc, &n) == PA_OK ? n : 0;
 }
 
 pa_status pa_plan(const pa_desc* desc, const int32_t* seq_lens, const int32_t* qsl, void* workspace,
@@ -477,7 +490,7 @@ pa_status pa_validate(const pa_desc* desc, const int32_t* block_table, const int
   if (workspace_bytes < 256) return PA_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int32_t* flag = static_cast<int32_t*>(workspace);
-  if (hipMemsetAsync(flag, 0, sizeof(int32_t), s) != hipSuccess) return PA_ERR_HIP;
+  if (pa::launch_fill_zero(flag, sizeof(int32_t), stream) != 0) return PA_ERR_HIP;
   if (pa::launch_validate(*desc, block_table, seq_lens, qsl, flag, stream) != 0) return PA_ERR_HIP;
   int32_t host = 0;
   if (hipMemcpyAsync(&host, flag, sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess) return PA_ERR_HIP;

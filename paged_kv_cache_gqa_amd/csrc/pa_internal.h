@@ -17,10 +17,7 @@ constexpr int kSplitRows = 32;       // a unit with <= 32 rows splits its chunks
 // Row tiles (16 rows) of each wave in a row-split unit.  One (64-row units) measured 14% faster
 // on prefill windows than two: twice the units means half the pieces per split unit, so half
 // the partial results written and merged, which outweighs the K/V fragments read per MFMA.
-#ifndef PA_ROW_TILES
-#define PA_ROW_TILES 1
-#endif
-constexpr int kRowTiles = PA_ROW_TILES;
+constexpr int kRowTiles = 1;
 constexpr int kBlockRows = 64 * kRowTiles;  // a larger unit is cut into blocks of 4 waves x 16 kRowTiles rows
 constexpr int kPlanThreads = 1024;
 
@@ -31,19 +28,13 @@ constexpr int kPlanThreads = 1024;
 // one wave streams 8 KiB of K and 8 KiB of V from HBM for a few rows).  With
 // 128-row units (two row tiles per wave) the row-split weight was 5.
 constexpr int kCostKeySplit = 4;
-#ifndef PA_COST_ROW
-#define PA_COST_ROW (kRowTiles == 1 ? 4 : 5)
-#endif
-constexpr int kCostRowSplit = PA_COST_ROW;
+constexpr int kCostRowSplit = 4;
 // FP8 pages change the ratio: a key-split chunk moves half the bytes, while a row-split chunk also
 // widens its K and V fragments to bf16 before the MFMAs.  Fitted on MI355X (the mixed prefill +
 // decode batch with FP8 pages, µs per launch, three runs each on one machine): row-split weight
 // 6: 68.8, 7: 65.7, 8: 65.0, 9: 65.3, 10: 66.5, 11: 67.7 (with the two-instruction widening of
 // codes to bf16 the optimum was 10; 4, bf16's weight, took 90.9).
-#ifndef PA_COST_ROW_FP8
-#define PA_COST_ROW_FP8 8
-#endif
-constexpr int kCostRowSplitFp8 = PA_COST_ROW_FP8;
+constexpr int kCostRowSplitFp8 = 8;
 // Fixed cost charged at the start of every unit (row and page-table loads, the
 // pipeline fill, the cross-wave merge and the output), so that grains that start
 // many units get fewer chunks.  Fitted on MI355X (bench.py, configurations 2-5):
@@ -57,11 +48,6 @@ inline __host__ __device__ int unit_start_cost(bool key_split, int rows) {
   return key_split ? (rows <= 16 ? kCostStartKs1 : kCostStartKs2) : kCostStartRow;
 }
 
-// bf16 decode: K of a chunk by global->LDS DMA (1) or straight to registers (0)
-#ifndef PA_K_VIA_LDS
-#define PA_K_VIA_LDS 1
-#endif
-
 // The cost axis is cut into S equal grains, one per workgroup (measured on
 // MI355X: more, smaller grains per workgroup only added merge work), with
 //   S = min(grid, Ck / kCostKeySplit + Cr / (kRowGrainChunks * rw))
@@ -72,10 +58,7 @@ inline __host__ __device__ int unit_start_cost(bool key_split, int rows) {
 // 128-row unit leaves 64 KiB of partial state to merge).  Grain boundaries --
 // and so every split of a unit's keys and its partial-result slots -- depend
 // only on the batch shape and the grid.
-#ifndef PA_ROW_GRAIN_CHUNKS
-#define PA_ROW_GRAIN_CHUNKS 8
-#endif
-constexpr int kRowGrainChunks = PA_ROW_GRAIN_CHUNKS;
+constexpr int kRowGrainChunks = 8;
 inline __host__ __device__ int64_t grain_count(int64_t ck, int64_t cr, int grid, int rw = kCostRowSplit) {
   int64_t s = ck / kCostKeySplit + cr / (int64_t(kRowGrainChunks) * rw);
   if (s > grid) s = grid;
@@ -129,6 +112,7 @@ struct AttnArgs {
   int32_t max_pages;
   float scale_log2;  // |scale| * log2(e): scores live in the base-2 domain
   uint32_t q_sign;   // xor applied to Q's bits: the sign bits when scale < 0, else 0
+  uint32_t q_keep;   // and applied to Q's bits first: 0 when scale == 0 (every score 0), else all ones
 };
 
 struct PlanArgs {

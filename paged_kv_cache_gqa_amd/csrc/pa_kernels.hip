@@ -784,11 +784,12 @@ __device__ __forceinline__ int tree_setup(const AttnArgs& A, const RowInfo (&ri)
 }
 
 // Q fragment of one row; for a negative scale the signs are flipped (exact), so that the
-// factor applied to q.k is always |scale| * log2(e) >= 0.
+// factor applied to q.k is always |scale| * log2(e) > 0; for scale 0 the fragment is cleared
+// (every score is then exactly 0) and the factor is 1.
 template <class TR>
 __device__ __forceinline__ u32x4_t load_q_frag(const AttnArgs& A, const RowInfo& ri, int f, int quad) {
   const char* base = static_cast<const char*>(A.q) + (int64_t(ri.tok) * A.num_q_heads + ri.head) * TR::D * TR::kEb;
-  return ri.valid ? (ld16(base + TR::q_off(f, quad)) ^ A.q_sign) : u32x4_t{0u, 0u, 0u, 0u};
+  return ri.valid ? ((ld16(base + TR::q_off(f, quad)) & A.q_keep) ^ A.q_sign) : u32x4_t{0u, 0u, 0u, 0u};
 }
 
 // Final (normalised) output of one row tile's 4 d values at tile t (part < 0), or
@@ -948,7 +949,7 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, const Seq
   // (an L2 hit), so the number of loads in flight is the same on every path and the waits --
   // the compiler's for V, the explicit one for the K DMA -- are exact.
   using RG = Ring<TR>;
-  constexpr bool kKviaLds = TR::kBf16 && PA_K_VIA_LDS;
+  constexpr bool kKviaLds = TR::kBf16;  // fp32 pages: K fragments straight to registers
   constexpr int kQRegion = kWaves * 2 * TR::kQF * 64;  // u32x4 slots of the Q slices (2 row tiles)
   static_assert(!kKviaLds || (kQRegion * 16 + kWaves * 2 * RG::kBlk <= Smem<TR>::kBytes), "LDS budget");
   char* kslot = reinterpret_cast<char*>(sm.buf + kQRegion) + w * 2 * RG::kBlk;
@@ -1701,10 +1702,6 @@ __device__ __forceinline__ Piece piece_of(const pa_plan_unit& U, int64_t c0, int
   return p;
 }
 
-#ifndef PA_KS_STREAM
-#define PA_KS_STREAM 1
-#endif
-
 // Key-split units of RT row tiles (bf16 pages, K by DMA) run back to back: the cursor's unit and
 // the units after it in the grain while they are of that kind.  In a wave's last step of a unit,
 // its one load in flight is already its first chunk of the next unit (page ids loaded at the unit
@@ -1717,7 +1714,7 @@ template <class TR, int RT>
 __device__ void run_keysplit_stream(const AttnArgs& A, UnitCursor& cu, Piece p, int64_t c0, int64_t c1, int grain,
                                     Smem<TR>& sm) {
   using RG = Ring<TR>;
-  static_assert(TR::kBf16 && PA_K_VIA_LDS, "bf16 pages with K by DMA");
+  static_assert(TR::kBf16, "bf16 pages with K by DMA");
   constexpr bool kPreQ = RT == 1;  // two row tiles of Q held across a unit would spill
   const PlanView& v = A.plan;
   const cptr<int32_t> seq_lens = ro(v.seq_lens);
@@ -1938,7 +1935,7 @@ __device__ __forceinline__ void run_grain(const AttnArgs& A, int grain, const Sl
     const int i0 = pc.i0, i1 = pc.i1, part = pc.part;
     if (i0 < i1) {
       bool streamed = false;
-      if constexpr (PA_KS_STREAM && TR::kBf16 && !TR::kScaled && PA_K_VIA_LDS && !kTree) {
+      if constexpr (TR::kBf16 && !TR::kScaled && !kTree) {
         // a stream never holds the piece the grain starts inside (its arrival would wait for the
         // next unit's loads); the one it ends inside can only be the stream's last unit
         // (units of two row tiles streamed ~1% slower: their Q cannot be held across a unit)
@@ -2435,14 +2432,14 @@ __global__ void gather_kernel(int which, int Hkv, int D, int max_pages, const E*
 // ---------------------------------------------------------------------------
 // Content validation: sets *flag to 1 on the first inconsistency found.
 // ---------------------------------------------------------------------------
-__global__ void validate_kernel(int B, int T, int NP, int max_pages, const int32_t* block_table,
+__global__ void validate_kernel(int B, int T, int NP, int max_pages, int max_len, const int32_t* block_table,
                                 const int32_t* seq_lens, const int32_t* qsl, int32_t* flag) {
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
   if (s == 0 && (qsl[0] != 0 || qsl[B] != T)) atomicOr(flag, 1);
   if (s >= B) return;
   const int n = seq_lens[s];
   const int qn = qsl[s + 1] - qsl[s];
-  if (qn < 0 || n < 0 || qn > n) {
+  if (qn < 0 || n < 0 || qn > n || n > max_len) {
     atomicOr(flag, 1);
     return;
   }
@@ -2673,8 +2670,10 @@ int launch_prefix_prep(const PrefixPrep& a, void* stream) {
 int launch_validate(const pa_desc& d, const int32_t* block_table, const int32_t* seq_lens, const int32_t* qsl,
                     int32_t* flag, void* stream) {
   const int grid = d.num_seqs > 0 ? (d.num_seqs + 255) / 256 : 1;
+  // a sequence may not exceed the stated max_seq_len, or (none stated) its block-table row
+  const int max_len = d.max_seq_len > 0 ? d.max_seq_len : d.max_pages_per_seq * kPage;
   hipLaunchKernelGGL(validate_kernel, dim3(grid), dim3(256), 0, as_stream(stream), d.num_seqs, d.num_q_tokens,
-                     d.num_pages, d.max_pages_per_seq, block_table, seq_lens, qsl, flag);
+                     d.num_pages, d.max_pages_per_seq, max_len, block_table, seq_lens, qsl, flag);
   return int(hipGetLastError());
 }
 

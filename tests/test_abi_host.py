@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("pa_attention", "pa_attention_tree", "pa_attention_fp8kv", "pa_attention_shared_prefix", "pa_workspace_size", "pa_workspace_init", "pa_append_kv", "pa_plan", "pa_attention_planned", "pa_merge_planned",
               "pa_merge", "pa_gather_kv", "pa_validate", "pa_check_desc", "pa_status_string", "pa_abi_version",
-              "pa_plan_read"):
+              "pa_plan_read", "pa_workspace_bytes", "pa_status_str"):
         assert n in names
 
 
@@ -39,21 +39,22 @@ def test_library_exports_every_declared_symbol(pa):
 
 
 def test_abi_version_and_status_strings(pa):
-    assert pa.abi_version() == 1
+    assert pa.abi_version() == 2
     for st in range(7):
         assert pa.status_string(st).startswith("PA_")
+        assert pa.status_str(st) == pa.status_string(st)
     assert "unknown" in pa.status_string(99)
 
 
 def test_struct_sizes_match_header(pa):
-    assert ctypes.sizeof(pa.PaDesc) == 40
+    assert ctypes.sizeof(pa.PaDesc) == 44
     assert ctypes.sizeof(pa.PlanUnit) == 48
     assert ctypes.sizeof(pa.PlanHeader) == 32
 
 
 def good_desc(pa, **kw):
     d = dict(num_seqs=4, num_q_tokens=4, num_q_heads=8, num_kv_heads=2, head_dim=64, page_size=16, num_pages=64,
-             max_pages_per_seq=16, dtype=0, scale=0.125)
+             max_pages_per_seq=16, max_seq_len=0, dtype=0, scale=0.125)
     d.update(kw)
     return pa.PaDesc(**d)
 
@@ -62,7 +63,8 @@ def good_desc(pa, **kw):
     ("num_seqs", -1, 2), ("num_q_tokens", -3, 2), ("num_q_heads", 0, 2), ("num_kv_heads", 0, 2),
     ("num_kv_heads", 3, 2), ("num_pages", 0, 2), ("max_pages_per_seq", 0, 2), ("head_dim", 96, 3),
     ("head_dim", 256, 3), ("page_size", 32, 3), ("dtype", 2, 3), ("scale", float("nan"), 2),
-    ("scale", float("inf"), 2), ("max_pages_per_seq", 1 << 27, 2),
+    ("scale", float("inf"), 2), ("max_pages_per_seq", 1 << 27, 2), ("max_seq_len", -1, 2),
+    ("max_seq_len", 16 * 16 + 1, 2),
 ])
 def test_check_desc_rejects(pa, field, value, status):
     assert pa.check_desc(good_desc(pa)) == 0
@@ -81,6 +83,10 @@ def test_null_pointers_rejected_without_touching_the_device(pa):
     d = good_desc(pa)
     # a NULL descriptor is caught before any HIP call
     assert L.pa_check_desc(None) == 1
+    assert L.pa_workspace_bytes(None) == 0  # errors read as size 0
+    assert L.pa_workspace_bytes(ctypes.byref(good_desc(pa, head_dim=96))) == 0
+    assert pa.check_desc(good_desc(pa, max_seq_len=16 * 16)) == 0
+    assert pa.check_desc(good_desc(pa, scale=0.0)) == 0
     assert L.pa_attention(None, None, None, None, None, None, None, None, None, None, 0, None) == 1
     assert L.pa_merge(0, 4, 64, None, None, 0, None, None, None) == 2  # n_parts < 1
     assert L.pa_merge(1, 4, 96, None, None, 0, None, None, None) == 3  # head_dim

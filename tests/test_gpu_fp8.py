@@ -91,7 +91,7 @@ def test_fp8_interleaved_mixed_batch(seed):
     check(w, out, lse)
 
 
-@pytest.mark.parametrize("c", [2, 3, 4])
+@pytest.mark.parametrize("c", [2, 3, 4, 5])
 def test_fp8_full_config(c):
     w = W.to_fp8(W.make_config(c))
     out, lse = run_fp8(w)

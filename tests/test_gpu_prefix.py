@@ -61,21 +61,17 @@ def test_shared_prefix_random(case):
 
 
 def test_shared_prefix_system_prompt_configuration():
-    """8 groups of 16 decode sequences over a shared 4096-token prefix; compared with the oracle on
-    two sequences of each group and with pa_attention on the whole batch."""
+    """8 groups of 16 decode sequences over a shared 4096-token prefix: every sequence against the
+    oracle (max and mean bounds), and against plain pa_attention on the same batch."""
     w = W.make_shared_prefix_config()
     out, lse = run_prefix(w)
+    check(w, out, lse)
     t = pa.to_device(w)
     po, pl = pa.attention(t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"], t["query_start_loc"],
                           w.scale)
     torch.cuda.synchronize()
     assert (out.float() - po.float()).abs().max().item() <= 2e-2
     assert (lse - pl).abs().max().item() <= 2e-2
-    seqs = np.array([g * 16 + k for g in range(8) for k in (0, 15)])
-    sub = W.subset(w, seqs)
-    rows = np.concatenate([np.arange(w.query_start_loc[s], w.query_start_loc[s + 1]) for s in seqs])
-    ref = oracle.attention_workload(sub)
-    check(sub, out[torch.from_numpy(rows).cuda()], lse[torch.from_numpy(rows).cuda()], ref)
 
 
 def test_shared_prefix_rejects_bad_group_counts():

@@ -77,9 +77,9 @@ def test_random_trees(case):
 
 
 def test_verify_configuration_with_trees():
-    """The speculative-verify configuration (5-token windows over 2k-16k keys), sequences 0-7, with random
-    draft trees over the 4 draft tokens."""
-    w = W.subset(W.make_config(4), np.arange(8))
+    """The whole speculative-verify configuration (32 sequences, 5-token windows over 2k-16k keys) with
+    random draft trees over the 4 draft tokens."""
+    w = W.make_config(4)
     masks, _ = W.random_trees(w.q_lens(), 4004)
     out, lse = run_tree(w, masks)
     check(w, masks, out, lse)
