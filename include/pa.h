@@ -153,6 +153,25 @@ pa_status pa_attention(const pa_desc* desc, const void* q, const void* k_pool, c
                        size_t workspace_bytes, void* stream);
 
 /*
+ * pa_attention without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same computation, kernel, grid and result (bitwise) as
+ * pa_attention; the caller passes inputs and outputs only.  The arrival
+ * counters and partial results live in a static device array of the library
+ * (32.3 MiB on each GPU it runs on, held until the process ends), sized for an
+ * attention grid of at most 512 workgroups (MI355X: 256 compute units x 2) and
+ * D <= 128; a device whose grid is larger gets PA_ERR_WORKSPACE_TOO_SMALL.  The
+ * batch size is not limited.  The first call on a device looks the array up and
+ * enqueues one fill kernel on `stream` that zeroes its counters; every call
+ * leaves them zero.  Nothing is allocated or freed.  All calls on one GPU share
+ * its array: calls that overlap on one GPU (on different streams, or from
+ * several threads) race and give undefined results -- order them on one stream.
+ */
+pa_status pa_attention_noalloc(const pa_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               const int32_t* query_start_loc, void* out, float* lse, void* stream);
+
+/*
  * pa_attention for batches whose sequences share prompt prefixes (the
  * prefix-reuse attention of the XY-Serve verdict page, load_bearing_attack
  * and pith_inferences: shared prefix pages; the result is identical to

@@ -93,12 +93,14 @@ def lib():
         L.pa_validate.argtypes = [dp, vp, vp, vp, vp, sz, vp]
         L.pa_append_kv.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.pa_attention_tree.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.pa_attention_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.pa_attention_fp8kv.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.pa_shared_prefix_workspace_size.argtypes = [dp, i32, ctypes.POINTER(sz)]
         L.pa_attention_shared_prefix.argtypes = [dp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
         for name in ("pa_check_desc", "pa_workspace_size", "pa_workspace_init", "pa_attention", "pa_plan", "pa_attention_planned",
                      "pa_merge_planned", "pa_plan_read", "pa_gather_kv", "pa_merge", "pa_validate", "pa_append_kv", "pa_attention_tree",
-                     "pa_attention_fp8kv", "pa_shared_prefix_workspace_size", "pa_attention_shared_prefix"):
+                     "pa_attention_fp8kv", "pa_shared_prefix_workspace_size", "pa_attention_shared_prefix",
+                     "pa_attention_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         if L.pa_abi_version() != ABI_VERSION:
             raise PagedAttentionError("load", -1, "ABI version mismatch")
@@ -224,6 +226,22 @@ def attention(q, k_pool, v_pool, block_table, seq_lens, query_start_loc, scale: 
     _check("pa_attention", lib().pa_attention(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                               _ptr(block_table), _ptr(seq_lens), _ptr(query_start_loc), _ptr(out),
                                               _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def attention_noalloc(q, k_pool, v_pool, block_table, seq_lens, query_start_loc, scale: float, out, lse,
+                      stream=None):
+    """pa_attention_noalloc: pa_attention with the library's static scratch instead of a workspace.
+    out [T_q][Hq][D] (q's dtype) and lse [T_q][Hq] float32 are the caller's; nothing is allocated."""
+    _check_inputs(q, k_pool, v_pool, block_table, seq_lens, query_start_loc)
+    if out.shape != q.shape or out.dtype != q.dtype or lse.shape != q.shape[:2] or lse.dtype != torch.float32:
+        raise ValueError("out must match q and lse be float32 [T_q][Hq]")
+    if not out.is_contiguous() or not lse.is_contiguous():
+        raise ValueError("out and lse must be contiguous")
+    desc = make_desc(q, k_pool, block_table, seq_lens, scale)
+    _check("pa_attention_noalloc",
+           lib().pa_attention_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                      _ptr(seq_lens), _ptr(query_start_loc), _ptr(out), _ptr(lse), _stream(stream)))
     return out, lse
 
 

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libpa_mi355x.so")
-SOURCES = [os.path.join(CSRC, "pa_kernels.hip"), os.path.join(CSRC, "pa_api.cpp")]
+SOURCES = [os.path.join(CSRC, "pa_kernels.hip"), os.path.join(CSRC, "pa_api.cpp"), os.path.join(CSRC, "pa_noalloc.hip")]
 HEADERS = [os.path.join(CSRC, "pa_internal.h"), os.path.join(INCLUDE, "pa.h")]
 ARCH = "gfx950"
 

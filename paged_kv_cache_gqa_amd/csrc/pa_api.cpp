@@ -111,22 +111,44 @@ pa::PlanView plan_view(const pa_desc& d, const int32_t* seq_lens, const int32_t*
 
 pa::AttnArgs attn_args(const pa_desc& d, const void* q, const void* k, const void* v, const int32_t* bt,
                        const int32_t* sl, const int32_t* qsl, void* out, float* lse, const Ws& ws) {
-  pa::AttnArgs a;
+  pa::AttnArgs a = pa::single_launch_args(d, q, k, v, bt, sl, qsl, out, lse, ws.part_o, ws.part_lse, ws.arrive);
   a.plan = plan_view(d, sl, qsl, ws);
+  return a;
+}
+
+}  // namespace
+
+namespace pa {
+
+pa_status attention_grid(const pa_desc& d, int* grid) { return device_grid(d, grid); }
+
+AttnArgs single_launch_args(const pa_desc& d, const void* q, const void* k, const void* v, const int32_t* bt,
+                            const int32_t* sl, const int32_t* qsl, void* out, float* lse, float* part_o,
+                            float* part_lse, int32_t* arrive) {
+  AttnArgs a;
+  a.plan.seq_lens = sl;
+  a.plan.qsl = qsl;
+  a.plan.hdr = nullptr;  // the single launch plans in-kernel: no stored plan
+  a.plan.seq_cost = nullptr;
+  a.plan.slots = nullptr;
+  a.plan.num_seqs = d.num_seqs;
+  a.plan.num_kv_heads = d.num_kv_heads;
+  a.plan.group = d.num_q_heads / d.num_kv_heads;
+  a.plan.full_rows = 0;
   a.q = q;
   a.k_pool = k;
   a.v_pool = v;
   a.block_table = bt;
   a.out = out;
   a.lse = lse;
-  a.part_o = ws.part_o;
-  a.part_lse = ws.part_lse;
+  a.part_o = part_o;
+  a.part_lse = part_lse;
   a.tree_mask = nullptr;
   a.k_scale = nullptr;
   a.v_scale = nullptr;
   a.key_base = nullptr;
   a.out_f32 = nullptr;
-  a.arrive = ws.arrive;
+  a.arrive = arrive;
   a.num_q_heads = d.num_q_heads;
   a.max_pages = d.max_pages_per_seq;
   // Scores are taken in the base-2 domain with the positive factor |scale| * log2(e); a negative
@@ -138,7 +160,7 @@ pa::AttnArgs attn_args(const pa_desc& d, const void* q, const void* k, const voi
   return a;
 }
 
-}  // namespace
+}  // namespace pa
 
 extern "C" {
 

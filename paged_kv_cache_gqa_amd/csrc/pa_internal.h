@@ -178,7 +178,7 @@ struct WsLayout {
   int64_t partial_rows, max_units;
 };
 
-inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Rows of one partial position: the largest unit.
 constexpr int kPartRows = kBlockRows;
@@ -233,4 +233,10 @@ int launch_validate(const pa_desc& d, const int32_t* block_table, const int32_t*
                     const int32_t* qsl, int32_t* flag, void* stream);
 // Workgroups per CU the attention kernel can hold (occupancy query), or < 0 on error.
 int attention_blocks_per_cu(int dtype, int head_dim);
+// Host side (pa_api.cpp): the single launch's grid for d on the current device, and its arguments
+// with the partial results and arrival counters at the given device addresses.
+pa_status attention_grid(const pa_desc& d, int* grid);
+AttnArgs single_launch_args(const pa_desc& d, const void* q, const void* k, const void* v, const int32_t* bt,
+                            const int32_t* sl, const int32_t* qsl, void* out, float* lse, float* part_o,
+                            float* part_lse, int32_t* arrive);
 }  // namespace pa
