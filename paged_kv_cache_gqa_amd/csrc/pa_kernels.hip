@@ -232,6 +232,46 @@ __device__ __forceinline__ void lds_read_v_imm<64>(uint32_t base, u32x4_t* vf) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) vf[t] = u32x4_t{x[2 * t][0], x[2 * t][1], x[2 * t + 1][0], x[2 * t + 1][1]};
 }
+
+// K fragments of chunk slot `ks` and V fragments of slot `vs` of the row-split ring (bf16 pages) in
+// one LDS round trip: K page 0 rows at the four swizzled column addresses ka[kk] (page 1 at
+// +kBlk), V^T rows from one per-lane base with immediate offsets (pages at 2 and 3 kBlk, tile t at
+// +512 t).
+#define PA_K16(P, A, O) "ds_read_b128 %" #P ", %" #A " offset:" #O "\n"
+template <int D>
+__device__ __forceinline__ void lds_read_kv_imm(const uint32_t (&ka)[D / 32], uint32_t vbase, u32x4_t* kf, u32x4_t* vf);
+template <>
+__device__ __forceinline__ void lds_read_kv_imm<128>(const uint32_t (&ka)[4], uint32_t vbase, u32x4_t* kf, u32x4_t* vf) {
+  u32x2_t x[16];
+  asm volatile(PA_K16(0, 24, 0) PA_K16(1, 25, 0) PA_K16(2, 26, 0) PA_K16(3, 27, 0)
+               PA_K16(4, 24, 4096) PA_K16(5, 25, 4096) PA_K16(6, 26, 4096) PA_K16(7, 27, 4096)
+               PA_V8(8, 28, 8192) PA_V8(9, 28, 12288) PA_V8(10, 28, 8704) PA_V8(11, 28, 12800)
+               PA_V8(12, 28, 9216) PA_V8(13, 28, 13312) PA_V8(14, 28, 9728) PA_V8(15, 28, 13824)
+               PA_V8(16, 28, 10240) PA_V8(17, 28, 14336) PA_V8(18, 28, 10752) PA_V8(19, 28, 14848)
+               PA_V8(20, 28, 11264) PA_V8(21, 28, 15360) PA_V8(22, 28, 11776) PA_V8(23, 28, 15872)
+               "s_waitcnt lgkmcnt(0)"
+               : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3]), "=&v"(kf[4]), "=&v"(kf[5]), "=&v"(kf[6]),
+                 "=&v"(kf[7]), "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+                 "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]), "=&v"(x[12]),
+                 "=&v"(x[13]), "=&v"(x[14]), "=&v"(x[15])
+               : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(vbase));
+#pragma unroll
+  for (int t = 0; t < 8; ++t) vf[t] = u32x4_t{x[2 * t][0], x[2 * t][1], x[2 * t + 1][0], x[2 * t + 1][1]};
+}
+template <>
+__device__ __forceinline__ void lds_read_kv_imm<64>(const uint32_t (&ka)[2], uint32_t vbase, u32x4_t* kf, u32x4_t* vf) {
+  u32x2_t x[8];
+  asm volatile(PA_K16(0, 12, 0) PA_K16(1, 13, 0) PA_K16(2, 12, 2048) PA_K16(3, 13, 2048)
+               PA_V8(4, 14, 4096) PA_V8(5, 14, 6144) PA_V8(6, 14, 4608) PA_V8(7, 14, 6656)
+               PA_V8(8, 14, 5120) PA_V8(9, 14, 7168) PA_V8(10, 14, 5632) PA_V8(11, 14, 7680)
+               "s_waitcnt lgkmcnt(0)"
+               : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3]), "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]),
+                 "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7])
+               : "v"(ka[0]), "v"(ka[1]), "v"(vbase));
+#pragma unroll
+  for (int t = 0; t < 4; ++t) vf[t] = u32x4_t{x[2 * t][0], x[2 * t][1], x[2 * t + 1][0], x[2 * t + 1][1]};
+}
+#undef PA_K16
 #undef PA_V8
 
 template <int D_>
@@ -338,6 +378,22 @@ struct Bf16 {
       vf[t0 + 1] = u32x4_t{x2[0], x2[1], x3[0], x3[1]};
     }
   }
+  // K of ring slot `ks` and V of slot `vs` in one LDS round trip where the geometry allows it
+  template <class RG>
+  __device__ static void lds_read_kv(const char* ks, const char* vs, int lane, u32x4_t (&kf)[kKF],
+                                     u32x4_t (&vf)[kVF]) {
+    if constexpr (RG::kPitchV == 32 && RG::kBlk == 32 * D) {
+      const int m = lane & 15, quad = lane >> 4;
+      uint32_t ka[D / 32];
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) ka[kk] = lds_addr(ks + m * RG::kPitchK + RG::swz_k(m, 4 * kk + quad) * 16);
+      const uint32_t vbase = lds_addr(vs + m * RG::kPitchV + RG::swz_v(m, quad >> 1) * 16 + 8 * (quad & 1));
+      lds_read_kv_imm<D>(ka, vbase, kf, vf);
+    } else {
+      lds_read_k<RG>(ks, lane, kf);
+      lds_read_v<RG>(vs, lane, vf);
+    }
+  }
   __device__ static void store_out(char* dst, f32x4_t o) {  // 4 consecutive d
     uint2 v;
     v.x = pack_bf16x2(o[0], o[1]);
@@ -428,6 +484,12 @@ struct F32 {
       a[g] = lds_addr(slot + (2 + h) * RG::kBlk + d * RG::kPitchV + RG::swz_v(d, quad) * 16);
     }
     lds_read_b128<kVF>(a, vf);
+  }
+  template <class RG>
+  __device__ static void lds_read_kv(const char* ks, const char* vs, int lane, u32x4_t (&kf)[kKF],
+                                     u32x4_t (&vf)[kVF]) {
+    lds_read_k<RG>(ks, lane, kf);
+    lds_read_v<RG>(vs, lane, vf);
   }
   __device__ static void store_out(char* dst, f32x4_t o) { *reinterpret_cast<f32x4_t*>(dst) = o; }
 };
@@ -523,6 +585,12 @@ struct Fp8Kv {
       vf[t0 + 1] = v_convert(VRaw{x2, x3});
     }
   }
+  template <class RG>
+  __device__ static void lds_read_kv(const char* ks, const char* vs, int lane, u32x4_t (&kf)[kKF],
+                                     u32x4_t (&vf)[kVF]) {
+    lds_read_k<RG>(ks, lane, kf);
+    lds_read_v<RG>(vs, lane, vf);
+  }
   __device__ static void store_out(char* dst, f32x4_t o) { Bf16<D>::store_out(dst, o); }
 };
 
@@ -564,9 +632,10 @@ struct PageIds {
 // The block-table loads of chunk c (every lane loads the same two entries) ...
 __device__ __forceinline__ PageIds page_ids_load(cptr<int32_t> bt_row, int c, int n_seq) {
   // both loads unconditional (no wait at a branch join); the second index is clamped to the
-  // sequence's last page, so it never reads past the pages the sequence owns
-  const bool two = c * kChunkKeys + kPage < n_seq;
-  const int ib = two ? 2 * c + 1 : 2 * c;
+  // sequence's last page, so it never reads past the pages the sequence owns: it is 2c + 1 when
+  // the chunk's second page starts before n_seq (the sign bit of c*32 + 16 - n_seq), else 2c --
+  // integer arithmetic that stays in scalar registers
+  const int ib = 2 * c + int(uint32_t(c * kChunkKeys + kPage - n_seq) >> 31);
   return PageIds{bt_row[2 * c], bt_row[ib]};
 }
 // ... and their values as wave-uniform page ids (waits for the loads).
@@ -646,84 +715,144 @@ struct TreeMask {
   int win0;
 };
 
-// Scores of one chunk for every row tile, masked, folded into the online softmax.
-// Returns the P operands; rescales O by exp2(m_old - m_new).
-// `getq(rt, qf)` fills the Q fragments of row tile rt (from registers or LDS).  kTree: keys of
-// the window are also masked by the rows' tree masks.
-template <class TR, int RT, bool kTree, class GetQ>
-__device__ __forceinline__ void softmax_chunk(State<TR, RT>& st, GetQ getq, const u32x4_t (&kf)[TR::kKF], int key0,
-                                              const int (&p_row)[RT], const TreeMask<RT>& tm, const ChunkScale& cs,
-                                              bool mask, float sl2, int lane, typename TR::PFrag (&pf)[RT]) {
+// Softmax of NC chunks in two phases.
+//
+// Phase 1 (softmax_prep): the raw scores s[j] (QK^T results of chunk j; half h holds the keys of
+// page h) of every row tile, with the K scale applied and masked keys set to -inf, into x; and the
+// running maxima moved where a score exceeds them by more than 2^kLazy.  The common path tests each
+// lane's own scores only: a row's maximum exceeds the threshold iff one of the four lanes holding
+// the row sees a score above it, so the cross-lane maximum (two lane swaps) is taken only on the
+// rare path that moves a maximum.  The results are the same as with the row maximum taken first.
+// kTree: keys of the window are also masked by the rows' tree masks.
+template <class TR, int RT, int NC, bool kTree>
+__device__ __forceinline__ void softmax_prep(State<TR, RT>& st, const f32x4_t (&s)[NC][RT][2], const int (&key0)[NC],
+                                             const int (&p_row)[RT], const TreeMask<RT>& tm,
+                                             const ChunkScale (&cs)[NC], const bool (&mask)[NC], float sl2, int lane,
+                                             float (&x)[NC][RT][8]) {
   const int quad = lane >> 4;
+  bool over = false;
+  float lm[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {  // raw scores q.k; the positive factor scale*log2(e) is applied inside exp2
+        x[c][rt][e] = s[c][rt][0][e];
+        x[c][rt][4 + e] = s[c][rt][1][e];
+      }
+      if constexpr (TR::kScaled) {  // the K scale of each page multiplies its keys' scores
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[c][rt][e] *= cs[c].k0;
+          x[c][rt][4 + e] *= cs[c].k1;
+        }
+      }
+      if (mask[c]) {
+        const int lim = p_row[rt] - key0[c];  // element j visible iff its key <= lim
+        // tree rows: a window key k (>= 0) is visible only where bit k of the row's mask is set.
+        // Written branch-free (bitwise & | on the conditions, the bit index clamped to 0..63): a
+        // short-circuit form compiled to divergent branches that lost the score of visible keys.
+        const uint32_t m_lo = uint32_t(tm.m[rt]), m_hi = uint32_t(tm.m[rt] >> 32);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          bool vis = p_key(j, quad) <= lim;
+          if constexpr (kTree) {
+            const int k = key0[c] + p_key(j, quad) - tm.win0;  // window token index of the key
+            const uint32_t kc = uint32_t(min(max(k, 0), 63));
+            const uint32_t bit = ((kc < 32 ? m_lo : m_hi) >> (kc & 31)) & 1u;
+            vis = vis & ((k < 0) | (bit != 0u));
+          }
+          x[c][rt][j] = vis ? x[c][rt][j] : -INFINITY;
+        }
+      }
+      const float cm = max3(max3(x[c][rt][0], x[c][rt][1], x[c][rt][2]), max3(x[c][rt][3], x[c][rt][4], x[c][rt][5]),
+                            max2(x[c][rt][6], x[c][rt][7]));
+      lm[rt] = c == 0 ? cm : max2(lm[rt], cm);
+    }
+    over |= lm[rt] * sl2 > st.m[rt] + kLazy;  // -inf * sl2 = -inf never passes (sl2 > 0)
+  }
+  if (__any(over)) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float mx = quad_max(lm[rt]);
+      const float mx2 = mx == -INFINITY ? -INFINITY : mx * sl2;  // row maximum in the base-2 domain
+      if (__any(mx2 > st.m[rt] + kLazy)) {
+        const float m_new = max2(st.m[rt], mx2);
+        const float alpha = fast_exp2(st.m[rt] - (m_new == -INFINITY ? 0.f : m_new));
+        st.l[rt] *= alpha;
+#pragma unroll
+        for (int t = 0; t < TR::kTiles; ++t) st.o[rt][t] *= alpha;
+        st.m[rt] = m_new;
+      }
+    }
+  }
+}
+
+// Phase 2 (softmax_exp): P = 2^(x * sl2 - m) against the running maxima, its sum into l, and the
+// P operands of the PV MFMAs (FP8 pages: P times the V scale of its page; l takes the unscaled P).
+template <class TR, int RT, int NC>
+__device__ __forceinline__ void softmax_exp(State<TR, RT>& st, const float (&x)[NC][RT][8],
+                                            const ChunkScale (&cs)[NC], float sl2,
+                                            typename TR::PFrag (&pf)[NC][RT]) {
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const float neg_m = st.m[rt] == -INFINITY ? 0.f : -st.m[rt];
+    float sum = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        p[j] = fast_exp2(__builtin_fmaf(x[c][rt][j], sl2, neg_m));
+        sum += p[j];
+      }
+      if constexpr (TR::kScaled) {  // the V scale of each page multiplies its P values (the sum l does not)
+        float pv[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          pv[j] = p[j] * cs[c].v0;
+          pv[4 + j] = p[4 + j] * cs[c].v1;
+        }
+        pf[c][rt] = TR::make_p(pv);
+      } else {
+        pf[c][rt] = TR::make_p(p);
+      }
+    }
+    st.l[rt] += sum;
+  }
+}
+
+// QK^T of one chunk for every row tile: s[rt][h] = scores of page h's keys for row tile rt.
+// `getq(rt, qf)` fills the Q fragments of row tile rt (from registers or LDS).
+template <class TR, int RT, class GetQ>
+__device__ __forceinline__ void qk_chunk(GetQ getq, const u32x4_t (&kf)[TR::kKF], f32x4_t (&s)[RT][2]) {
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     u32x4_t qf[TR::kQF];
     getq(rt, qf);
-    const f32x4_t s0 = TR::qk(kf, 0, qf);
-    const f32x4_t s1 = TR::qk(kf, 1, qf);
-    float x[8];  // raw scores q.k; the positive factor scale*log2(e) is applied inside exp2
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[e] = s0[e];
-      x[4 + e] = s1[e];
-    }
-    if constexpr (TR::kScaled) {  // the K scale of each page multiplies its keys' scores
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[e] *= cs.k0;
-        x[4 + e] *= cs.k1;
-      }
-    }
-    if (mask) {
-      const int lim = p_row[rt] - key0;  // element j visible iff its key <= lim
-      // tree rows: a window key k (>= 0) is visible only where bit k of the row's mask is set.
-      // Written branch-free (bitwise & | on the conditions, the bit index clamped to 0..63): a
-      // short-circuit form compiled to divergent branches that lost the score of visible keys.
-      const uint32_t m_lo = uint32_t(tm.m[rt]), m_hi = uint32_t(tm.m[rt] >> 32);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        bool vis = p_key(j, quad) <= lim;
-        if constexpr (kTree) {
-          const int k = key0 + p_key(j, quad) - tm.win0;  // window token index of the key
-          const uint32_t kc = uint32_t(min(max(k, 0), 63));
-          const uint32_t bit = ((kc < 32 ? m_lo : m_hi) >> (kc & 31)) & 1u;
-          vis = vis & ((k < 0) | (bit != 0u));
-        }
-        x[j] = vis ? x[j] : -INFINITY;
-      }
-    }
-    float mx = max3(max3(x[0], x[1], x[2]), max3(x[3], x[4], x[5]), max2(x[6], x[7]));
-    mx = quad_max(mx);
-    const float mx2 = mx == -INFINITY ? -INFINITY : mx * sl2;  // row maximum in the base-2 domain
-    if (__any(mx2 > st.m[rt] + kLazy)) {
-      const float m_new = max2(st.m[rt], mx2);
-      const float alpha = fast_exp2(st.m[rt] - (m_new == -INFINITY ? 0.f : m_new));
-      st.l[rt] *= alpha;
-#pragma unroll
-      for (int t = 0; t < TR::kTiles; ++t) st.o[rt][t] *= alpha;
-      st.m[rt] = m_new;
-    }
-    const float neg_m = st.m[rt] == -INFINITY ? 0.f : -st.m[rt];
-    float p[8];
-    float sum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      p[j] = fast_exp2(__builtin_fmaf(x[j], sl2, neg_m));
-      sum += p[j];
-    }
-    st.l[rt] += sum;
-    if constexpr (TR::kScaled) {  // the V scale of each page multiplies its P values (the sum l does not)
-      float pv[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pv[j] = p[j] * cs.v0;
-        pv[4 + j] = p[4 + j] * cs.v1;
-      }
-      pf[rt] = TR::make_p(pv);
-    } else {
-      pf[rt] = TR::make_p(p);
-    }
+    s[rt][0] = TR::qk(kf, 0, qf);
+    s[rt][1] = TR::qk(kf, 1, qf);
   }
+}
+
+// Scores of one chunk for every row tile, masked, folded into the online softmax: the P operands,
+// with O rescaled by 2^(m_old - m_new) where a running maximum moved.
+template <class TR, int RT, bool kTree, class GetQ>
+__device__ __forceinline__ void softmax_chunk(State<TR, RT>& st, GetQ getq, const u32x4_t (&kf)[TR::kKF], int key0,
+                                              const int (&p_row)[RT], const TreeMask<RT>& tm, const ChunkScale& cs,
+                                              bool mask, float sl2, int lane, typename TR::PFrag (&pf)[RT]) {
+  f32x4_t s[1][RT][2];
+  qk_chunk<TR, RT>(getq, kf, s[0]);
+  float x[1][RT][8];
+  const int k0[1] = {key0};
+  const ChunkScale c1[1] = {cs};
+  const bool m1[1] = {mask};
+  softmax_prep<TR, RT, 1, kTree>(st, s, k0, p_row, tm, c1, m1, sl2, lane, x);
+  typename TR::PFrag p1[1][RT];
+  softmax_exp<TR, RT, 1>(st, x, c1, sl2, p1);
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) pf[rt] = p1[0][rt];
 }
 
 template <class TR, int RT>
@@ -1074,38 +1203,13 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, const Seq
   __syncthreads();
 }
 
-// One chunk of a row-split unit: start the DMA of chunk `next` (if >= 0) into slot `fill`, then
-// compute on the chunk held in slot `cur` (a different slot, landed before the last barrier).
-// `after_reads` runs once this chunk's LDS reads are done (it starts the next page-id loads).
-template <class TR, int RT, bool kTree, class Issue, class After, class GetQ>
-__device__ __forceinline__ void ring_step(char* fill, const char* cur, Issue issue, bool do_issue, After after_reads,
-                                          bool active, State<TR, RT>& st, GetQ getq, int key0,
-                                          const int (&p_row)[RT], const TreeMask<RT>& tm, const ChunkScale& cs,
-                                          int mask_from, int n_seq, float sl2, int lane) {
-  using RG = Ring<TR>;
-  if (do_issue) issue(fill);
-  if (active) {
-    const int quad = lane >> 4;
-    u32x4_t kf[TR::kKF];
-    TR::template lds_read_k<RG>(cur, lane, kf);
-    typename TR::PFrag pf[RT];
-    softmax_chunk<TR, RT, kTree>(st, getq, kf, key0, p_row, tm, cs, key0 + kChunkKeys - 1 >= mask_from, sl2, lane,
-                                 pf);
-    u32x4_t vf[TR::kVF];
-    TR::template lds_read_v<RG>(cur, lane, vf);
-    asm volatile("" ::: "memory");
-    after_reads();
-    if (key0 + kChunkKeys > n_seq) TR::sanitize_v(vf, quad, n_seq - key0);
-    pv_chunk<TR, RT>(st, vf, pf);
-  } else {
-    after_reads();
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Row-split unit (prefill, <= 64 rows): wave w owns rows [16w, 16w+16).  The
-// workgroup streams chunks through an LDS ring with global->LDS DMA, kNB - 1
-// chunks ahead of the one being computed; every wave issues 1/4 of each chunk.
+// workgroup streams chunks through an LDS ring with global->LDS DMA; every wave
+// issues 1/4 of each chunk.  A step covers NP chunks (64 keys; 32 for fp32 pages
+// at D = 128, whose chunks fill half the ring each) under one barrier and one
+// softmax pass, and the ring holds two steps: the next step's chunks land while
+// this one is computed.
 // ---------------------------------------------------------------------------
 template <class TR, bool kTree>
 __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, const SeqUnits& sq, int i0, int i1, int part,
@@ -1113,12 +1217,18 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, const Seq
   using RG = Ring<TR>;
   constexpr int RT = kRowTiles;
   constexpr int kWaveRows = 16 * RT;  // rows of each wave
+  constexpr int NP = RG::kNB / 2;     // chunks per step
+  static_assert(RG::kNB == 4 || RG::kNB == 2, "ring of two steps");
   int lane = threadIdx.x & 63;
   asm volatile("" : "+v"(lane));  // lane-derived values are recomputed per unit, not held across the unit loop
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int quad = lane >> 4;
-  const int s = U.seq;
-  const int n_seq = sq.n, q0 = sq.q0, qn = sq.qn;
+  // wave-uniform values in scalar registers (the chunk loop's index and address arithmetic stays scalar)
+  const int s = __builtin_amdgcn_readfirstlane(U.seq);
+  const int n_seq = __builtin_amdgcn_readfirstlane(sq.n), q0 = sq.q0, qn = __builtin_amdgcn_readfirstlane(sq.qn);
+  i0 = __builtin_amdgcn_readfirstlane(i0);
+  i1 = __builtin_amdgcn_readfirstlane(i1);
+  const int kvh = __builtin_amdgcn_readfirstlane(U.kv_head);
   const cptr<int32_t> bt_row = ro(A.block_table) + int64_t(s) * A.max_pages +
                                (A.key_base ? ro(A.key_base)[s] / kPage : 0);
   const bool active = kWaveRows * w < U.n_rows;
@@ -1134,8 +1244,8 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, const Seq
   TreeMask<RT> tm;
   const int mask_from = tree_setup<RT, kTree>(A, ri, n_seq, qn, min_p, tm);
 
-  // Unit start: the page ids of the first kNB chunks are loaded before Q, so that the DMAs of the
-  // first kNB - 1 chunks wait for one round trip only and Q arrives behind them.
+  // Unit start: the page ids of the first two steps are loaded before Q, so that the first step's
+  // DMAs wait for one round trip only and Q arrives behind them.
   PageIds ids0[RG::kNB];
 #pragma unroll
   for (int j = 0; j < RG::kNB; ++j) ids0[j] = page_ids_load(bt_row, min(i0 + j, i1 - 1), n_seq);
@@ -1151,60 +1261,102 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, const Seq
   State<TR, RT> st;
   state_init(st);
 
-  // Wave w copies block w of each chunk; lane `lane` of DMA instruction i fills LDS bytes
-  // [i*1024 + 16*lane, +16) of the block image, i.e. row r, swizzled column cc.
+  // Wave w copies the (page, kv head) block of K page 0, K page 1, V page 0 or V page 1 (w = 0..3):
+  // its pool and head offset are fixed for the unit, the page changes per chunk.  Lane `lane` of DMA
+  // instruction i fills LDS bytes [i*1024 + 16*lane, +16) of the block image (row r, swizzled column).
   char* ring = reinterpret_cast<char*>(sm.buf);
-  // FP8 pages: every wave loads a chunk's scales just before its DMAs; they travel with the chunk
-  // through a shift register (scl[0] belongs to the chunk being computed).
-  constexpr int kPerChunk = RG::kInstr + (TR::kScaled ? 1 : 0);  // this wave's loads per chunk
-  float scl[RG::kNB];
+  const char* wave_pool = static_cast<const char*>(w < 2 ? A.k_pool : A.v_pool) + int64_t(kvh) * RG::kBlk;
+  const int64_t page_stride = int64_t(A.plan.num_kv_heads) * RG::kBlk;
+  uint32_t src[RG::kInstr];  // this lane's source offset within the block, per DMA instruction
+#pragma unroll
+  for (int i = 0; i < RG::kInstr; ++i) {
+    const int o = i * 1024 + 16 * lane;
+    if (w < 2) {
+      const int r = o / RG::kPitchK, cc = (o % RG::kPitchK) / 16;
+      src[i] = uint32_t(r * RG::kPitchK + RG::swz_k(r, cc) * 16);
+    } else {
+      const int r = o / RG::kPitchV, cc = (o % RG::kPitchV) / 16;
+      src[i] = uint32_t(r * RG::kPitchV + RG::swz_v(r, cc) * 16);
+    }
+  }
+  // FP8 pages: every wave loads a chunk's scales just before its DMAs (lane l: scale (l & 3) of it)
   auto issue = [&](PageIds ids, char* slot) -> float {
-    const float sc = load_scale_lane<TR>(A, U.kv_head, ids, lane);
-    const ChunkPages cp = pages_of<TR>(A, U.kv_head, ids);
-    const __amdgpu_buffer_rsrc_t rs = block_rsrc(w == 0 ? cp.k0 : w == 1 ? cp.k1 : w == 2 ? cp.v0 : cp.v1, RG::kBlk);
+    const float sc = load_scale_lane<TR>(A, kvh, ids, lane);
+    const int pg = (w & 1) ? ids.b : ids.a;
+    const __amdgpu_buffer_rsrc_t rs = block_rsrc(wave_pool + int64_t(pg) * page_stride, RG::kBlk);
     char* dst = slot + w * RG::kBlk;
 #pragma unroll
-    for (int i = 0; i < RG::kInstr; ++i) {
-      const int o = i * 1024 + 16 * lane;
-      uint32_t src;
-      if (w < 2) {
-        const int r = o / RG::kPitchK, cc = (o % RG::kPitchK) / 16;
-        src = uint32_t(r * RG::kPitchK + RG::swz_k(r, cc) * 16);
-      } else {
-        const int r = o / RG::kPitchV, cc = (o % RG::kPitchV) / 16;
-        src = uint32_t(r * RG::kPitchV + RG::swz_v(r, cc) * 16);
-      }
-      dma16(rs, src, dst + i * 1024);
-    }
+    for (int i = 0; i < RG::kInstr; ++i) dma16(rs, src[i], dst + i * 1024);
     return sc;
   };
+  auto slot_of_chunk = [&](int c) { return ring + ((c - i0) & (RG::kNB - 1)) * RG::kChunk; };
 
+  // prologue: the first step's chunks; the page ids of the second step are already loaded
+  float scl[NP];
 #pragma unroll
-  for (int j = 0; j < RG::kNB - 1; ++j)
-    scl[j] = i0 + j < i1 ? issue(uniform_ids(ids0[j]), ring + j * RG::kChunk) : 0.f;
-  // page ids of the chunk issued in the next iteration, loaded one iteration ahead
-  PageIds nx = uniform_ids(ids0[RG::kNB - 1]);
-  for (int c = i0; c < i1; ++c) {
-    const int j = c - i0;
-    const int ahead = min(RG::kNB - 2, i1 - 1 - c);  // chunks this wave issued after chunk c
-    static_assert(RG::kNB <= 4, "waits below cover up to 2 chunks ahead");
-    if (ahead >= 2) wait_vmcnt<2 * kPerChunk>();
-    else if (ahead == 1) wait_vmcnt<kPerChunk>();
-    else wait_vmcnt<0>();
-    lds_barrier();  // chunk c is in LDS for every wave; chunk c-1's slot is free
-    const int next = c + RG::kNB - 1;
-    float scl_new = 0.f;
-    ring_step<TR, RT, kTree>(
-        ring + ((j + RG::kNB - 1) % RG::kNB) * RG::kChunk, ring + (j % RG::kNB) * RG::kChunk,
-        [&](char* slot) { scl_new = issue(nx, slot); }, next < i1,
-        [&] { nx = page_ids(bt_row, min(next + 1, i1 - 1), n_seq); }, active, st, getq, c * kChunkKeys, p_row,
-        tm, read_scales<TR>(scl[0]), mask_from, n_seq, A.scale_log2, lane);
+  for (int j = 0; j < NP; ++j) scl[j] = i0 + j < i1 ? issue(uniform_ids(ids0[j]), slot_of_chunk(i0 + j)) : 0.f;
+  PageIds nx[NP];
 #pragma unroll
-    for (int k = 0; k + 1 < RG::kNB - 1; ++k) scl[k] = scl[k + 1];
-    scl[RG::kNB - 2] = scl_new;
+  for (int j = 0; j < NP; ++j) nx[j] = uniform_ids(ids0[NP + j]);
+
+  for (int c = i0; c < i1; c += NP) {
+    wait_vmcnt<0>();  // this wave's share of the step's chunks has landed (nothing was issued after them)
+    lds_barrier();    // ... every wave's share; every wave is done with the previous step's slots
+    float scl_new[NP];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int cn = c + NP + j;
+      scl_new[j] = cn < i1 ? issue(nx[j], slot_of_chunk(cn)) : 0.f;
+    }
+    if (active) {
+      // chunk j of the step: c + j, or (past the unit's end) a copy of chunk c whose keys are all
+      // masked, so that it adds exactly nothing
+      int key0[NP];
+      bool msk[NP];
+      ChunkScale cs[NP];
+      f32x4_t sc[NP][RT][2];
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        const bool real = c + j < i1;
+        const int cj = real ? c + j : c;
+        u32x4_t kf[TR::kKF];
+        TR::template lds_read_k<RG>(slot_of_chunk(cj), lane, kf);
+        qk_chunk<TR, RT>(getq, kf, sc[j]);
+        key0[j] = real ? cj * kChunkKeys : (1 << 29);
+        msk[j] = !real || cj * kChunkKeys + kChunkKeys - 1 >= mask_from;
+        cs[j] = read_scales<TR>(scl[j]);
+      }
+      float x[NP][RT][8];
+      softmax_prep<TR, RT, NP, kTree>(st, sc, key0, p_row, tm, cs, msk, A.scale_log2, lane, x);
+      typename TR::PFrag pf[NP][RT];
+      softmax_exp<TR, RT, NP>(st, x, cs, A.scale_log2, pf);
+      // V after the scores, so that K and V fragments of the step are not live together
+      u32x4_t vf[NP][TR::kVF];
+#pragma unroll
+      for (int j = 0; j < NP; ++j) TR::template lds_read_v<RG>(slot_of_chunk(c + j < i1 ? c + j : c), lane, vf[j]);
+      asm volatile("" ::: "memory");
+      // page ids of the step after next, after the step's last LDS read
+#pragma unroll
+      for (int j = 0; j < NP; ++j) nx[j] = page_ids_load(bt_row, min(c + 2 * NP + j, i1 - 1), n_seq);
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        const int cj = c + j < i1 ? c + j : c;
+        if (cj * kChunkKeys + kChunkKeys > n_seq) TR::sanitize_v(vf[j], quad, n_seq - cj * kChunkKeys);
+      }
+#pragma unroll
+      for (int j = 0; j < NP; ++j) pv_chunk<TR, RT>(st, vf[j], pf[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NP; ++j) nx[j] = page_ids_load(bt_row, min(c + 2 * NP + j, i1 - 1), n_seq);
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      nx[j] = uniform_ids(nx[j]);
+      scl[j] = scl_new[j];
+    }
   }
   wait_all_loads();  // nothing of this unit left in flight
-  lds_barrier();                        // every wave is done with the ring before it is reused
+  lds_barrier();     // every wave is done with the ring before it is reused
 
   if (active) {
 #pragma unroll
