@@ -44,6 +44,8 @@ METRIC = "decode KV-read HBM GB/s (% of peak) + prefill/verify TFLOP/s, 1 MI355X
 KERNEL_SOURCES = ["paged_kv_cache_gqa_amd/csrc/pa_kernels.hip", "paged_kv_cache_gqa_amd/csrc/pa_internal.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_kernel_hbm_traffic.json")
 
+TILE_DESCRIPTION = dict(batch=2, q_heads=32, kv_heads=8, head_dim=128, context="2048 prior + 2048 new",
+                        queries_per_seq="2048")
 DESCRIPTIONS = {
     1: dict(batch=4, q_heads=8, kv_heads=2, head_dim=64, context="{17,64,100,256}", queries_per_seq="1"),
     2: dict(batch=64, q_heads=32, kv_heads=8, head_dim=128, context="uniform[512,4096]", queries_per_seq="1"),
@@ -295,13 +297,15 @@ def main() -> int:
                     help="workload (default 5: long-context decode, the largest that runs on one GPU)")
     ap.add_argument("--part", default="all", choices=["all", "prefill", "decode"],
                     help="configuration 3 only: time its prefill chunks or its decode rows alone")
-    ap.add_argument("--op", default="attention", choices=["attention", "append", "tree", "fp8", "prefix"],
+    ap.add_argument("--op", default="attention", choices=["attention", "append", "tree", "fp8", "prefix", "tile"],
                     help="attention (default): the attention call; append: the paged KV append of the batch's new "
                          "tokens (pa_append_kv); tree: attention with each window a random draft-token tree "
                          "(pa_attention_tree); fp8: attention over the batch's K/V quantized to FP8 E4M3 pages with "
                          "per-(page, kv head) scales (pa_attention_fp8kv); prefix: shared-prefix attention "
                          "(pa_attention_shared_prefix) on the system-prompt decode batch (8 groups x 16 sequences, "
-                         "4096-token shared prefix), --config ignored")
+                         "4096-token shared prefix), --config ignored; tile: pa_attention on a long chunked prefill "
+                         "(2 x 2048-token windows on 2048 tokens of context, 32/8 heads, head dim 128), the prefill "
+                         "tile's steady state, reported as MFMA TFLOP/s, --config ignored")
     ap.add_argument("--staged", action="store_true",
                     help="time pa_plan + pa_attention_planned + pa_merge_planned instead of the single launch")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
@@ -321,7 +325,8 @@ def main() -> int:
 
     if args.record_traffic:
         from paged_kv_cache_gqa_amd import workloads as W
-        name = W.CONFIG_NAMES[args.config] + ("" if args.part == "all" else f"-{args.part}-part") + \
+        name = W.LONG_PREFILL_NAME if args.op == "tile" else \
+            W.CONFIG_NAMES[args.config] + ("" if args.part == "all" else f"-{args.part}-part") + \
             {"tree": "-tree", "fp8": "-fp8kv"}.get(args.op, "")
         kernel = "attention_kernel" if args.staged else "attention_fused_kernel"
         print(json.dumps(record_traffic(name, *args.record_traffic, kernel=kernel)))
@@ -337,8 +342,9 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.op == "prefix":
         return bench_prefix(args)
-    w = W.make_config(args.config)
-    if args.part != "all":
+    tile = args.op == "tile"
+    w = W.make_long_prefill() if tile else W.make_config(args.config)
+    if args.part != "all" and not tile:
         ql = w.q_lens()
         keep = np.nonzero(ql > 1 if args.part == "prefill" else ql == 1)[0]
         w = W.subset(w, keep)
@@ -450,11 +456,12 @@ def main() -> int:
     kernel = "attention_kernel" if args.staged else "attention_fused_kernel"
     if (tree or fp8) and args.staged:
         raise SystemExit("--op tree / fp8 run the single launch only")
-    config = {"workload": f"{w.name} (configuration {args.config})", **DESCRIPTIONS[args.config],
+    desc_cfg = TILE_DESCRIPTION if tile else DESCRIPTIONS[args.config]
+    config = {"workload": w.name if tile else f"{w.name} (configuration {args.config})", **desc_cfg,
               "part": args.part, "path": "staged (3 launches)" if args.staged else "single launch",
               "windows": "random draft-token trees (per-row ancestor masks)" if tree else "causal",
               "kv_pages": "FP8 E4M3, per-(page, kv head) fp32 scales" if fp8 else w.dtype,
-              "page_size": 16, "seed": 1000 + args.config, "kv_pool_copies": n_copies,
+              "page_size": 16, "seed": 1007 if tile else 1000 + args.config, "kv_pool_copies": n_copies,
               "algorithmic_bytes": alg_bytes, "algorithmic_flops": alg_flops}
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -473,6 +480,13 @@ def main() -> int:
                      "per_launch": "algorithmic bytes of the whole batch (one launch covers the batch)",
                      "events_pass_ms_per_step": round(ms_per_step_events, 5)},
     }
+    if tile:  # an MFMA-bound workload: TFLOP/s against the dense bf16 peak
+        k_tf = alg_flops / (attn_mean * 1e-3) / 1e12
+        line.update({"metric": "prefill tile MFMA TFLOP/s (bf16, % of dense peak), 1 MI355X",
+                     "value": round(tflops, 2), "unit": "TFLOP/s"})
+        line["roofline"].update({"bound": "mfma", "achieved": round(k_tf, 2), "peak": BF16_PEAK_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": round(k_tf / BF16_PEAK_TFLOPS, 4),
+                                 "per_launch": "algorithmic flops of the whole batch (one launch covers the batch)"})
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, alg_bytes)
     print(json.dumps(line), flush=True)

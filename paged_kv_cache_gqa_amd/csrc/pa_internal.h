@@ -35,6 +35,9 @@ constexpr int kCostRowSplit = 4;
 // 6: 68.8, 7: 65.7, 8: 65.0, 9: 65.3, 10: 66.5, 11: 67.7 (with the two-instruction widening of
 // codes to bf16 the optimum was 10; 4, bf16's weight, took 90.9).
 constexpr int kCostRowSplitFp8 = 8;
+static_assert((kCostKeySplit & (kCostKeySplit - 1)) == 0 && (kCostRowSplit & (kCostRowSplit - 1)) == 0 &&
+                  (kCostRowSplitFp8 & (kCostRowSplitFp8 - 1)) == 0,
+              "chunk weights are powers of two (the kernels divide by them with shifts)");
 // Fixed cost charged at the start of every unit (row and page-table loads, the
 // pipeline fill, the cross-wave merge and the output), so that grains that start
 // many units get fewer chunks.  Fitted on MI355X (bench.py, configurations 2-5):

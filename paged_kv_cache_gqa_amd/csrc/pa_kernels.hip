@@ -1842,11 +1842,14 @@ struct Piece {
   int i0, i1, part;
 };
 __device__ __forceinline__ Piece piece_of(const pa_plan_unit& U, int64_t c0, int64_t c1, int grain) {
+  // chunk weights are powers of two: ceil divisions by them are shifts (a 64-bit division is a long
+  // emulated sequence, measured at ~0.7 us per unit start on MI355X)
   const int64_t w = U.cost_weight;
+  const int sh = __builtin_ctz(uint32_t(U.cost_weight));
   const int64_t cs = chunk_start(U, 0);
   Piece p;
-  p.i0 = int(c0 > cs ? (c0 - cs + w - 1) / w : 0);
-  const int64_t e = c1 > cs ? (c1 - cs + w - 1) / w : 0;
+  p.i0 = int(c0 > cs ? (c0 - cs + w - 1) >> sh : 0);
+  const int64_t e = c1 > cs ? (c1 - cs + w - 1) >> sh : 0;
   p.i1 = int(e < U.n_chunks ? e : U.n_chunks);
   // a grain holds at most two pieces of split units: the one it starts inside (position 0)
   // and the one it ends inside (position 1)

@@ -446,3 +446,15 @@ def make_shared_prefix_config(seed: int = 1006) -> Workload:
     256..1024 tokens, one query token each; Llama-3-8B attention shape (32 / 8 heads, head dim 128)."""
     return make_shared_prefix(seed, [16] * 8, [4096] * 8, 1024, 1, 32, 8, 128, "bf16", suffix_min=256,
                               name=SHARED_PREFIX_NAME)
+
+
+LONG_PREFILL_NAME = "long-prefill-bf16"
+
+
+def make_long_prefill(seed: int = 1007) -> Workload:
+    """Long chunked prefill for the prefill tile's steady state: 2 sequences, each a 2048-token
+    window on 2048 tokens of prior context (4096 keys), Llama-3-8B attention shape (32 query / 8 KV
+    heads, head dim 128), bf16, values N(0, 1), pages in a seeded permutation of a pool with 10%
+    slack."""
+    return build(LONG_PREFILL_NAME, seed, [4096, 4096], [2048, 2048], 32, 8, 128, "bf16")
+

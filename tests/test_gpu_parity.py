@@ -107,6 +107,14 @@ def test_config5_full_batch():
     check(w, out, lse)
 
 
+def test_long_prefill_tile_workload():
+    """The long chunked prefill that bench.py --op tile times (2 x 2048-token windows on 2048 keys of
+    context, 32/8 heads): every row against the oracle."""
+    w = W.make_long_prefill()
+    out, lse = run_gpu(w)
+    check(w, out, lse)
+
+
 # ---------------------------------------------------------------------------
 # edge cases
 # ---------------------------------------------------------------------------
