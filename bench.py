@@ -288,6 +288,50 @@ def bench_prefix(args) -> int:
     return 0
 
 
+def bench_read(args) -> int:
+    """The device's plain streaming-read rate (pa_read_stream over an 8 GiB buffer): the practical
+    ceiling that the memory-bound attention paths are measured against, beside the 8 TB/s peak."""
+    import torch
+
+    import paged_kv_cache_gqa_amd as pa
+
+    nbytes = 8 << 30
+    g = torch.Generator(device="cuda").manual_seed(1008)
+    buf = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda", generator=g)
+    stream = torch.cuda.current_stream()
+    rates = {}
+    for grid in (256, 512, 1024, 2048, 4096):
+        sink = torch.empty((grid,), dtype=torch.int32, device="cuda")
+        for _ in range(max(1, args.warmup // 4)):
+            pa.read_stream(buf, grid, sink)
+        torch.cuda.synchronize()
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            pa.read_stream(buf, grid, sink)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / args.steps
+        rates[grid] = (nbytes / (ms * 1e-3) / 1e9, ms)
+    best = max(rates, key=lambda k: rates[k][0])
+    gbs, ms = rates[best]
+    line = {
+        "metric": "plain streaming read GB/s (% of HBM peak), 1 MI355X",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u32", "data": "synthetic (seeded random words)",
+        "config": {"workload": "one pass over an 8 GiB device buffer, 16-byte loads, one contiguous slice per "
+                               "workgroup of 256 threads", "bytes": nbytes, "grid": best},
+        "by_grid_gbs": {str(k): round(v[0], 1) for k, v in rates.items()},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 5), "traffic": None, "kernel": "pa::read_stream_kernel",
+                     "kernel_ms_mean": round(ms, 5),
+                     "kernel_ms_source": "two events bracketing the timed launches, divided by the steps"},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -297,7 +341,7 @@ def main() -> int:
                     help="workload (default 5: long-context decode, the largest that runs on one GPU)")
     ap.add_argument("--part", default="all", choices=["all", "prefill", "decode"],
                     help="configuration 3 only: time its prefill chunks or its decode rows alone")
-    ap.add_argument("--op", default="attention", choices=["attention", "append", "tree", "fp8", "prefix", "tile"],
+    ap.add_argument("--op", default="attention", choices=["attention", "append", "tree", "fp8", "prefix", "tile", "read"],
                     help="attention (default): the attention call; append: the paged KV append of the batch's new "
                          "tokens (pa_append_kv); tree: attention with each window a random draft-token tree "
                          "(pa_attention_tree); fp8: attention over the batch's K/V quantized to FP8 E4M3 pages with "
@@ -305,7 +349,9 @@ def main() -> int:
                          "(pa_attention_shared_prefix) on the system-prompt decode batch (8 groups x 16 sequences, "
                          "4096-token shared prefix), --config ignored; tile: pa_attention on a long chunked prefill "
                          "(2 x 2048-token windows on 2048 tokens of context, 32/8 heads, head dim 128), the prefill "
-                         "tile's steady state, reported as MFMA TFLOP/s, --config ignored")
+                         "tile's steady state, reported as MFMA TFLOP/s, --config ignored; read: the device's plain "
+                         "streaming-read rate (pa_read_stream over 8 GiB), the practical ceiling for the decode "
+                         "paths, --config ignored")
     ap.add_argument("--staged", action="store_true",
                     help="time pa_plan + pa_attention_planned + pa_merge_planned instead of the single launch")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
@@ -342,6 +388,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.op == "prefix":
         return bench_prefix(args)
+    if args.op == "read":
+        return bench_read(args)
     tile = args.op == "tile"
     w = W.make_long_prefill() if tile else W.make_config(args.config)
     if args.part != "all" and not tile:

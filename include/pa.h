@@ -349,6 +349,18 @@ pa_status pa_validate(const pa_desc* desc, const int32_t* block_table, const int
                       const int32_t* query_start_loc, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/*
+ * Diagnostics: the device's streaming-read rate, the practical ceiling for the
+ * memory-bound (decode) paths.  Reads `bytes` of device memory at `buf` with
+ * 16-byte loads, workgroup g taking the contiguous slice [g * bytes / grid,
+ * (g + 1) * bytes / grid), and writes the XOR of the slice's 32-bit words to
+ * sink[g] (device memory, `grid` words), so that the reads cannot be skipped
+ * and the caller can check them.  `bytes` must be a positive multiple of
+ * 16 * grid and 1 <= grid <= 65535, else PA_ERR_BAD_SHAPE.  Asynchronous on
+ * `stream`.
+ */
+pa_status pa_read_stream(const void* buf, size_t bytes, int32_t grid, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,6 +12,7 @@ _BINDING_NAMES = {
     "check_desc", "workspace_size", "alloc_workspace", "make_desc", "status_string", "abi_version", "lib",
     "PagedAttentionError", "PaDesc", "to_device", "append_kv", "workspace_init", "attention_tree",
     "attention_fp8kv", "attention_shared_prefix", "shared_prefix_workspace", "status_str", "workspace_bytes", "attention_noalloc",
+    "read_stream",
 }
 
 

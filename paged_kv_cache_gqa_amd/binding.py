@@ -97,10 +97,11 @@ def lib():
         L.pa_attention_fp8kv.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.pa_shared_prefix_workspace_size.argtypes = [dp, i32, ctypes.POINTER(sz)]
         L.pa_attention_shared_prefix.argtypes = [dp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.pa_read_stream.argtypes = [vp, sz, i32, vp, vp]
         for name in ("pa_check_desc", "pa_workspace_size", "pa_workspace_init", "pa_attention", "pa_plan", "pa_attention_planned",
                      "pa_merge_planned", "pa_plan_read", "pa_gather_kv", "pa_merge", "pa_validate", "pa_append_kv", "pa_attention_tree",
                      "pa_attention_fp8kv", "pa_shared_prefix_workspace_size", "pa_attention_shared_prefix",
-                     "pa_attention_noalloc"):
+                     "pa_attention_noalloc", "pa_read_stream"):
             getattr(L, name).restype = ctypes.c_int
         if L.pa_abi_version() != ABI_VERSION:
             raise PagedAttentionError("load", -1, "ABI version mismatch")
@@ -400,6 +401,19 @@ def validate(desc: PaDesc, block_table, seq_lens, query_start_loc, workspace, st
     if st not in (0, 6):
         _check("pa_validate", st)
     return int(st)
+
+
+def read_stream(buf, grid: int, sink=None, stream=None):
+    """pa_read_stream over the bytes of the contiguous device tensor `buf`; returns the [grid] uint32
+    sink of per-workgroup XOR words (as int32)."""
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    with _on(stream):
+        if sink is None:
+            sink = torch.empty((grid,), dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    _check("pa_read_stream", lib().pa_read_stream(_ptr(buf), nbytes, grid, _ptr(sink), _stream(stream)))
+    return sink
 
 
 def to_device(w, device="cuda"):

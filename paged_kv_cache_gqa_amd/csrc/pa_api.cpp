@@ -520,4 +520,10 @@ pa_status pa_validate(const pa_desc* desc, const int32_t* block_table, const int
   return host ? PA_ERR_INVALID_CONTENT : PA_OK;
 }
 
+pa_status pa_read_stream(const void* buf, size_t bytes, int32_t grid, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return PA_ERR_NULL_POINTER;
+  if (grid < 1 || grid > 65535 || bytes == 0 || bytes % (size_t(16) * size_t(grid)) != 0) return PA_ERR_BAD_SHAPE;
+  return pa::launch_read_stream(buf, bytes, grid, sink, stream) == 0 ? PA_OK : PA_ERR_HIP;
+}
+
 }  // extern "C"

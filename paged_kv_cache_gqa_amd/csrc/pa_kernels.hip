@@ -632,10 +632,10 @@ struct PageIds {
 // The block-table loads of chunk c (every lane loads the same two entries) ...
 __device__ __forceinline__ PageIds page_ids_load(cptr<int32_t> bt_row, int c, int n_seq) {
   // both loads unconditional (no wait at a branch join); the second index is clamped to the
-  // sequence's last page, so it never reads past the pages the sequence owns: it is 2c + 1 when
-  // the chunk's second page starts before n_seq (the sign bit of c*32 + 16 - n_seq), else 2c --
-  // integer arithmetic that stays in scalar registers
-  const int ib = 2 * c + int(uint32_t(c * kChunkKeys + kPage - n_seq) >> 31);
+  // sequence's last page, so it never reads past the pages the sequence owns: for a chunk that
+  // holds keys (c * 32 < n_seq) it is 2c + 1 when that page starts before n_seq, else 2c (a
+  // minimum, which stays in scalar registers)
+  const int ib = min(2 * c + 1, (n_seq - 1) / kPage);
   return PageIds{bt_row[2 * c], bt_row[ib]};
 }
 // ... and their values as wave-uniform page ids (waits for the loads).
@@ -1156,7 +1156,7 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, const Seq
     u32x4_t vf[TR::kVF];
 #pragma unroll
     for (int f = 0; f < TR::kVF; ++f) vf[f] = TR::v_convert(vr[f]);
-    TR::sanitize_v(vf, quad, n_seq - key0);
+    if (key0 + kChunkKeys > n_seq) TR::sanitize_v(vf, quad, n_seq - key0);  // the sequence's last chunk
     pv_chunk<TR, RT>(st, vf, pf);
     load_v<TR>(cp, vl, vr);
   }
@@ -2015,7 +2015,7 @@ __device__ void run_keysplit_stream(const AttnArgs& A, UnitCursor& cu, Piece p, 
       u32x4_t vf[TR::kVF];
 #pragma unroll
       for (int f = 0; f < TR::kVF; ++f) vf[f] = TR::v_convert(vr[f]);
-      TR::sanitize_v(vf, quad, n_seq - key0);
+      if (key0 + kChunkKeys > n_seq) TR::sanitize_v(vf, quad, n_seq - key0);  // the sequence's last chunk
       pv_chunk<TR, RT>(st, vf, pf);
       load_v<TR>(ncp, vl, vr);
     }
@@ -2694,6 +2694,35 @@ int launch_fill_zero(void* p, size_t bytes, void* stream) {
   if (grid > 1024) grid = 1024;
   hipLaunchKernelGGL(fill_zero_kernel, dim3(unsigned(grid)), dim3(256), 0, as_stream(stream),
                      static_cast<uint32_t*>(p), words);
+  return int(hipGetLastError());
+}
+
+// Streaming read of one contiguous slice per workgroup (16-byte loads, four in flight per thread
+// per pass), folded to one XOR word per workgroup.
+__global__ __launch_bounds__(256) void read_stream_kernel(const u32x4_t* __restrict__ buf, int64_t per,
+                                                          uint32_t* sink) {
+  const u32x4_t* b = buf + per * blockIdx.x;
+  u32x4_t acc = {0u, 0u, 0u, 0u};
+  for (int64_t i = threadIdx.x; i < per; i += 4 * 256) {
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    const u32x4_t x0 = b[i];
+    const u32x4_t x1 = i + 256 < per ? b[i + 256] : z;
+    const u32x4_t x2 = i + 512 < per ? b[i + 512] : z;
+    const u32x4_t x3 = i + 768 < per ? b[i + 768] : z;
+    acc ^= x0 ^ x1 ^ x2 ^ x3;
+  }
+  uint32_t r = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) r ^= uint32_t(__shfl_xor(int(r), o));
+  __shared__ uint32_t wx[4];
+  if ((threadIdx.x & 63) == 0) wx[threadIdx.x >> 6] = r;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = wx[0] ^ wx[1] ^ wx[2] ^ wx[3];
+}
+
+int launch_read_stream(const void* buf, size_t bytes, int grid, uint32_t* sink, void* stream) {
+  hipLaunchKernelGGL(read_stream_kernel, dim3(unsigned(grid)), dim3(256), 0, as_stream(stream),
+                     static_cast<const u32x4_t*>(buf), int64_t(bytes / 16 / size_t(grid)), sink);
   return int(hipGetLastError());
 }
 

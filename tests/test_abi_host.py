@@ -100,3 +100,10 @@ def test_null_pointers_rejected_without_touching_the_device(pa):
                           None, None, 0, None) == 3
     assert L.pa_gather_kv(ctypes.byref(d), 2, None, None, None, 0, 4, None, None) == 2
     assert L.pa_gather_kv(ctypes.byref(d), 0, None, None, None, 7, 4, None, None) == 2  # seq out of range
+    # streaming-read diagnostic: sizes are checked before any HIP call
+    buf, sink = ctypes.c_void_p(16), ctypes.c_void_p(16)
+    assert L.pa_read_stream(None, 1024, 4, sink, None) == 1
+    assert L.pa_read_stream(buf, 1024, 0, sink, None) == 2
+    assert L.pa_read_stream(buf, 1024, 65536, sink, None) == 2
+    assert L.pa_read_stream(buf, 1000, 4, sink, None) == 2  # not a multiple of 16 * grid
+    assert L.pa_read_stream(buf, 0, 1, sink, None) == 2
