@@ -368,6 +368,7 @@ pa_status pa_attention_shared_prefix(const pa_desc* desc, const void* q, const v
   pp.pre_o = pw.part_o;
   pp.pre_lse = pw.part_lse;
   pp.rows = rows;
+  pp.num_seqs = desc->num_seqs;
   pp.num_groups = num_groups;
   pp.max_pages = desc->max_pages_per_seq;
   pp.head_dim = desc->head_dim;

@@ -168,6 +168,7 @@ struct PrefixPrep {
   float* pre_o;           // [rows][D]
   float* pre_lse;         // [rows]
   int64_t rows;           // T_q * Hq
+  int32_t num_seqs;       // B = group_start[num_groups]
   int32_t num_groups;
   int32_t max_pages;
   int32_t head_dim;

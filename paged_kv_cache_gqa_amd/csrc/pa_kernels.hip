@@ -2820,21 +2820,33 @@ int launch_append_kv(const AppendArgs& a, int dtype, int num_seqs, int num_q_tok
 // first member's pages) and all the group's query tokens, every row seeing every key.  Every
 // sequence of the suffix pass keeps its queries and sees its keys from prefix_len onwards.
 // ---------------------------------------------------------------------------
+// Every output element has its own thread (grid-strided): the groups' prefix windows, their
+// block-table rows (one entry per thread), each sequence's suffix length and key base (its group
+// found by a binary search of group_start), and the prefix pass's zeroed results.
 __global__ void prefix_prep_kernel(PrefixPrep a) {
   const int64_t tid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t nthreads = int64_t(gridDim.x) * blockDim.x;
+  const cptr<int32_t> gs = ro(a.group_start), pl = ro(a.prefix_len);
   for (int64_t g = tid; g < a.num_groups; g += nthreads) {
-    const int s0 = a.group_start[g], s1 = a.group_start[g + 1];
-    const int P = a.prefix_len[g];
-    a.pre_seq_lens[g] = P;
-    a.pre_qsl[g] = a.qsl[s0];
-    if (g == a.num_groups - 1) a.pre_qsl[a.num_groups] = a.qsl[s1];
-    for (int j = 0; j < a.max_pages; ++j)
-      a.pre_bt[g * a.max_pages + j] = j < P / kPage ? a.block_table[int64_t(s0) * a.max_pages + j] : -1;
-    for (int s = s0; s < s1; ++s) {
-      a.suf_seq_lens[s] = a.seq_lens[s] - P;
-      a.key_base[s] = P;
+    a.pre_seq_lens[g] = pl[g];
+    a.pre_qsl[g] = a.qsl[gs[g]];
+    if (g == a.num_groups - 1) a.pre_qsl[a.num_groups] = a.qsl[gs[a.num_groups]];
+  }
+  const int64_t bt_entries = int64_t(a.num_groups) * a.max_pages;
+  for (int64_t i = tid; i < bt_entries; i += nthreads) {
+    const int g = int(i / a.max_pages), j = int(i - int64_t(g) * a.max_pages);
+    a.pre_bt[i] = j < pl[g] / kPage ? a.block_table[int64_t(gs[g]) * a.max_pages + j] : -1;
+  }
+  for (int64_t s = tid; s < a.num_seqs; s += nthreads) {
+    int lo = 0, hi = a.num_groups - 1;  // the last g with group_start[g] <= s
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (gs[mid] <= s) lo = mid;
+      else hi = mid - 1;
     }
+    const int P = pl[lo];
+    a.suf_seq_lens[s] = a.seq_lens[s] - P;
+    a.key_base[s] = P;
   }
   // rows of a group without a shared prefix are never written by the prefix pass: they count as
   // having seen no key there
@@ -2843,7 +2855,9 @@ __global__ void prefix_prep_kernel(PrefixPrep a) {
 }
 
 int launch_prefix_prep(const PrefixPrep& a, void* stream) {
-  const int64_t work = a.rows * a.head_dim > a.num_groups ? a.rows * a.head_dim : a.num_groups;
+  int64_t work = a.rows * a.head_dim;
+  if (work < int64_t(a.num_groups) * a.max_pages) work = int64_t(a.num_groups) * a.max_pages;
+  if (work < a.num_seqs) work = a.num_seqs;
   int64_t grid = (work + 255) / 256;
   if (grid > 2048) grid = 2048;
   if (grid < 1) grid = 1;
