@@ -1343,8 +1343,14 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, const Seq
         const int cj = c + j < i1 ? c + j : c;
         if (cj * kChunkKeys + kChunkKeys > n_seq) TR::sanitize_v(vf[j], quad, n_seq - cj * kChunkKeys);
       }
+      // tile by tile, the step's chunks back to back into one accumulator (chunk by chunk, the
+      // compiler wrote the second chunk's results beside the accumulators and copied them back)
 #pragma unroll
-      for (int j = 0; j < NP; ++j) pv_chunk<TR, RT>(st, vf[j], pf[j]);
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int t = 0; t < TR::kTiles; ++t)
+#pragma unroll
+          for (int j = 0; j < NP; ++j) st.o[rt][t] = TR::pv(vf[j], t, pf[j][rt], st.o[rt][t]);
     } else {
 #pragma unroll
       for (int j = 0; j < NP; ++j) nx[j] = page_ids_load(bt_row, min(c + 2 * NP + j, i1 - 1), n_seq);
