@@ -146,6 +146,14 @@ pa_status pa_workspace_init(const pa_desc* desc, void* workspace, size_t workspa
  * arrival counters (see pa_workspace_size).  T_q == 0 enqueues nothing.
  * Results are bitwise reproducible for a given batch shape and device, and
  * bitwise equal to those of the staged path below.
+ *
+ * Ordering the in-launch merge relies on (gfx950): a piece's partial results
+ * are stored with device scope (written through the XCD's L2 to the
+ * device-coherent level) and have completed (s_waitcnt vmcnt(0)) before its
+ * workgroup increments the unit's arrival counter, a relaxed atomic at agent
+ * scope; the workgroup that reads the completing count then loads the pieces
+ * with device scope (missing the non-coherent L2).  No L2-wide write-back or
+ * invalidate is issued.  Two calls that share one workspace must not overlap.
  */
 pa_status pa_attention(const pa_desc* desc, const void* q, const void* k_pool, const void* v_pool,
                        const int32_t* block_table, const int32_t* seq_lens,
