@@ -140,6 +140,17 @@ def test_single_long_sequence_max_length():
     check(w, out, lse)
 
 
+def test_million_key_sequences_split_over_hundreds_of_grains():
+    """2^20 + 3 keys (65537 pages per sequence): a decode row group (one key-split unit of 32769
+    chunks) and a 64-row prefill block over almost the same length (one row-split unit).  The grid's
+    512 grains cut each unit into ~256 pieces, merged inside the launch (the row-split merge past
+    its 8-piece fast path)."""
+    n = (1 << 20) + 3
+    w = W.build("million", 6, [n, n - 5], [1, 8], 8, 1, 128, "bf16")
+    out, lse = run_gpu(w)
+    check(w, out, lse)
+
+
 # ---------------------------------------------------------------------------
 # invariants of the GPU result
 # ---------------------------------------------------------------------------
