@@ -111,7 +111,7 @@ pa_status pa_check_desc(const pa_desc* desc);
 /*
  * Bytes of device workspace pa_attention needs for `desc` on the current HIP
  * device (per workgroup of the persistent launch: an arrival counter and room
- * for two partial results of up to 64 rows; the staged plan).  The size
+ * for two partial results of up to 128 rows; the staged plan).  The size
  * depends only on the descriptor and on the device's compute-unit count.
  * Writes *bytes; returns PA_ERR_NULL_POINTER, a descriptor error or PA_ERR_HIP.
  *
@@ -144,8 +144,12 @@ pa_status pa_workspace_init(const pa_desc* desc, void* workspace, size_t workspa
  * were split across grains merges the pieces by log-sum-exp.  `workspace` must
  * hold at least pa_workspace_size bytes, be 256-byte aligned and have zero
  * arrival counters (see pa_workspace_size).  T_q == 0 enqueues nothing.
- * Results are bitwise reproducible for a given batch shape and device, and
- * bitwise equal to those of the staged path below.
+ * Row blocks have 64 rows, or 128 for bf16 batches at head_dim 128 with
+ * T_q * Hq >= 64 * (the launch's workgroups) -- a lot of prefill work, where
+ * longer blocks double the MFMA work per K/V byte staged in LDS.  Results are
+ * bitwise reproducible for a given batch shape and device, and bitwise equal
+ * to those of the staged path below whenever the single launch uses 64-row
+ * blocks (the staged path always does).
  *
  * Ordering the in-launch merge relies on (gfx950): a piece's partial results
  * are stored with device scope (written through the XCD's L2 to the
@@ -166,7 +170,7 @@ pa_status pa_attention(const pa_desc* desc, const void* q, const void* k_pool, c
  * forbid allocation.  Same computation, kernel, grid and result (bitwise) as
  * pa_attention; the caller passes inputs and outputs only.  The arrival
  * counters and partial results live in a static device array of the library
- * (32.3 MiB on each GPU it runs on, held until the process ends), sized for an
+ * (64.3 MiB on each GPU it runs on, held until the process ends), sized for an
  * attention grid of at most 512 workgroups (MI355X: 256 compute units x 2) and
  * D <= 128; a device whose grid is larger gets PA_ERR_WORKSPACE_TOO_SMALL.  The
  * batch size is not limited.  The first call on a device looks the array up and

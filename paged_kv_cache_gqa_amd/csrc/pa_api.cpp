@@ -122,6 +122,16 @@ namespace pa {
 
 pa_status attention_grid(const pa_desc& d, int* grid) { return device_grid(d, grid); }
 
+// 128-row row blocks for bf16 batches at head dim 128 with at least one 64-row block of query rows
+// per workgroup of the grid (T_q x Hq >= 64 x grid): with that much prefill work, twice the MFMA
+// work per K/V byte read from LDS outweighs the extra pieces of the longer units (measured on
+// MI355X: long prefill tile 344 -> 279 us, 4 x 1024-token windows 62 -> 58 us; configuration 3's
+// prefill, 272 blocks of 64 rows on a 512-workgroup grid, 31.8 -> 38.8 us with 128-row blocks).
+bool tall_blocks(const pa_desc& d, int grid) {
+  return d.dtype == PA_BF16 && d.head_dim == 128 &&
+         int64_t(d.num_q_tokens) * d.num_q_heads >= int64_t(kBlockRows) * grid;
+}
+
 AttnArgs single_launch_args(const pa_desc& d, const void* q, const void* k, const void* v, const int32_t* bt,
                             const int32_t* sl, const int32_t* qsl, void* out, float* lse, float* part_o,
                             float* part_lse, int32_t* arrive) {
@@ -285,7 +295,9 @@ pa_status single_launch(const pa_desc* desc, const void* q, const void* k_pool, 
   if (ps != PA_OK) return ps;
   pa::AttnArgs a = attn_args(*desc, q, k_pool, v_pool, block_table, seq_lens, qsl, out, lse, ws);
   a.tree_mask = tree_mask;
-  return pa::launch_attention_fused(a, desc->dtype, desc->head_dim, grid, stream) == 0 ? PA_OK : PA_ERR_HIP;
+  return pa::launch_attention_fused(a, desc->dtype, desc->head_dim, grid, stream, pa::tall_blocks(*desc, grid)) == 0
+             ? PA_OK
+             : PA_ERR_HIP;
 }
 }  // namespace
 
@@ -379,12 +391,14 @@ pa_status pa_attention_shared_prefix(const pa_desc* desc, const void* q, const v
   pa::AttnArgs a = attn_args(dp, q, k_pool, v_pool, pw.pre_bt, pw.pre_seq_lens, pw.pre_qsl, out, pw.part_lse, ws);
   a.plan.full_rows = 1;
   a.out_f32 = pw.part_o;
-  if (pa::launch_attention_fused(a, desc->dtype, desc->head_dim, grid, stream) != 0) return PA_ERR_HIP;
+  if (pa::launch_attention_fused(a, desc->dtype, desc->head_dim, grid, stream, pa::tall_blocks(dp, grid)) != 0)
+    return PA_ERR_HIP;
   // suffix pass: every sequence from the end of its prefix on, causal as usual
   pa::AttnArgs b = attn_args(*desc, q, k_pool, v_pool, block_table, pw.suf_seq_lens, qsl, out, pw.part_lse + rows, ws);
   b.key_base = pw.key_base;
   b.out_f32 = pw.part_o + rows * desc->head_dim;
-  if (pa::launch_attention_fused(b, desc->dtype, desc->head_dim, grid, stream) != 0) return PA_ERR_HIP;
+  if (pa::launch_attention_fused(b, desc->dtype, desc->head_dim, grid, stream, pa::tall_blocks(*desc, grid)) != 0)
+    return PA_ERR_HIP;
   // log-sum-exp merge of the two passes into out / lse
   return pa::launch_merge(2, rows, desc->head_dim, pw.part_o, pw.part_lse, desc->dtype, out, lse, stream) == 0
              ? PA_OK

@@ -14,11 +14,19 @@ constexpr int kChunkKeys = 32;       // keys per chunk = two pages = one 16x16x3
 constexpr int kWaves = 4;            // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSplitRows = 32;       // a unit with <= 32 rows splits its chunks across the 4 waves
-// Row tiles (16 rows) of each wave in a row-split unit.  One (64-row units) measured 14% faster
-// on prefill windows than two: twice the units means half the pieces per split unit, so half
-// the partial results written and merged, which outweighs the K/V fragments read per MFMA.
-constexpr int kRowTiles = 1;
-constexpr int kBlockRows = 64 * kRowTiles;  // a larger unit is cut into blocks of 4 waves x 16 kRowTiles rows
+// Row-split units are blocks of 4 waves x 16 kRowTiles rows.  The staged path and most batches use
+// one row tile per wave (64-row blocks): twice the units of two row tiles means half the pieces
+// per split unit, so half the partial results written and merged (config-3-sized prefill: 31.8
+// against 38.8 us with 128-row blocks).  Batches with a lot of prefill work run a kernel with two
+// row tiles per wave (128-row blocks: twice the MFMA work per K/V byte read from LDS and per
+// chunk's DMA, page-table and loop instructions; the long prefill tile 344 -> 279 us).
+constexpr int kBlockRows = 64;      // rows of a staged-path row block
+constexpr int kMaxBlockRows = 128;  // rows of the largest row block of any kernel
+// The row-split geometry of a kernel, one template integer for the planner: the cost weight of a
+// row-split chunk (low byte) and the row tiles per wave (a block has 64 x tiles rows).
+constexpr int row_geom(int weight, int tiles) { return weight | (tiles << 8); }
+constexpr int rg_weight(int rg) { return rg & 255; }
+constexpr int rg_rows(int rg) { return 64 * (rg >> 8); }
 constexpr int kPlanThreads = 1024;
 
 // Cost weights per 32-key chunk on the planner's balancing axis, fitted to
@@ -29,6 +37,7 @@ constexpr int kPlanThreads = 1024;
 // 128-row units (two row tiles per wave) the row-split weight was 5.
 constexpr int kCostKeySplit = 4;
 constexpr int kCostRowSplit = 4;
+constexpr int kRgDefault = row_geom(kCostRowSplit, 1);  // the staged planner's geometry
 // FP8 pages change the ratio: a key-split chunk moves half the bytes, while a row-split chunk also
 // widens its K and V fragments to bf16 before the MFMAs.  Fitted on MI355X (the mixed prefill +
 // decode batch with FP8 pages, µs per launch, three runs each on one machine): row-split weight
@@ -185,7 +194,7 @@ struct WsLayout {
 constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Rows of one partial position: the largest unit.
-constexpr int kPartRows = kBlockRows;
+constexpr int kPartRows = kMaxBlockRows;
 
 // grid: workgroups of the attention launch for d; max_grid: the largest such grid of any dtype /
 // head dim on the device (the arrival counters sit at a fixed offset with a fixed size, so one
@@ -195,7 +204,7 @@ inline WsLayout ws_layout(const pa_desc& d, int grid, int max_grid) {
   const int64_t B = d.num_seqs > 0 ? d.num_seqs : 0;
   const int64_t T = d.num_q_tokens > 0 ? d.num_q_tokens : 0;
   const int64_t G = d.num_kv_heads > 0 ? d.num_q_heads / d.num_kv_heads : 1;
-  // units per sequence = Hkv * (1 if q_len*G <= 32 else ceil(q_len*G/128))
+  // staged-plan units per sequence = Hkv * (1 if q_len*G <= 32 else ceil(q_len*G/64))
   L.max_units = int64_t(d.num_kv_heads) * (B + (T * G + kBlockRows - 1) / kBlockRows);
   const int64_t grains = grid;
   L.partial_rows = grains * 2 * kPartRows;
@@ -218,7 +227,8 @@ namespace pa {
 int launch_plan(const PlanArgs& a, void* stream);
 int launch_attention(const AttnArgs& a, int dtype, int head_dim, int grid, void* stream);
 // single launch: in-kernel planning of each grain and merge of split units by their last piece
-int launch_attention_fused(const AttnArgs& a, int dtype, int head_dim, int grid, void* stream);
+// tall: bf16 at head dim 128 without tree masks runs the kernel with 128-row row blocks
+int launch_attention_fused(const AttnArgs& a, int dtype, int head_dim, int grid, void* stream, bool tall = false);
 // single launch over FP8 E4M3 pages (bf16 q / out; a.k_scale, a.v_scale set)
 int launch_attention_fp8kv(const AttnArgs& a, int head_dim, int grid, void* stream);
 int launch_fill_zero(void* p, size_t bytes, void* stream);
@@ -241,6 +251,8 @@ int attention_blocks_per_cu(int dtype, int head_dim);
 // Host side (pa_api.cpp): the single launch's grid for d on the current device, and its arguments
 // with the partial results and arrival counters at the given device addresses.
 pa_status attention_grid(const pa_desc& d, int* grid);
+// whether the single launch runs 128-row row blocks for d on a grid of `grid` workgroups
+bool tall_blocks(const pa_desc& d, int grid);
 AttnArgs single_launch_args(const pa_desc& d, const void* q, const void* k, const void* v, const int32_t* bt,
                             const int32_t* sl, const int32_t* qsl, void* out, float* lse, float* part_o,
                             float* part_lse, int32_t* arrive);

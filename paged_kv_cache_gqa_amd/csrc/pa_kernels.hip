@@ -32,11 +32,14 @@
 //  * Decode/verify units (<= 32 rows) let the 4 waves take alternate chunks and
 //    merge in LDS.  Each wave keeps one chunk in flight: V straight to
 //    registers, K (bf16) by global->LDS DMA into the wave's own slot.  Prefill
-//    units (<= 64 rows) give each wave 16 rows; the 4 waves DMA the 4 page
-//    blocks of a chunk into a ring of LDS slots shared by all of them (XOR-
-//    swizzled rows, so the MFMA fragment reads are conflict-free).
+//    units (<= 64 rows; <= 128 in the kernel for prefill-heavy bf16 batches)
+//    give each wave 16 (32) rows; the 4 waves DMA the 4 page blocks of a chunk
+//    into a ring of LDS slots shared by all of them (XOR-swizzled rows, so the
+//    MFMA fragment reads are conflict-free).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "pa_internal.h"
 
@@ -287,7 +290,8 @@ struct Bf16 {
   static constexpr int kVLoads = 2 * kVF;  // global load instructions per chunk of V (two pages per tile)
   static constexpr int kEbKV = kEb;        // bytes per K/V pool element
   static constexpr bool kScaled = false;   // per-(page, head) K/V scales
-  static constexpr int kCostRow = kCostRowSplit;  // planner weight of a row-split chunk
+  static constexpr int kRowTiles = 1;  // 16-row tiles of each wave in a row-split unit
+  static constexpr int kRowGeom = row_geom(kCostRowSplit, kRowTiles);  // the planner's row-split geometry
   using VRaw = u32x4_t;                    // a V fragment as loaded
 
   __device__ static int q_off(int f, int quad) { return (32 * f + 8 * quad) * kEb; }
@@ -402,6 +406,14 @@ struct Bf16 {
   }
 };
 
+// bf16 pages with 128-row row-split units (two 16-row tiles per wave), for batches with a lot of
+// prefill work; a 128-row chunk step weighs twice a 64-row one on the cost axis.
+template <int D_>
+struct Bf16Tall : Bf16<D_> {
+  static constexpr int kRowTiles = 2;
+  static constexpr int kRowGeom = row_geom(2 * kCostRowSplit, kRowTiles);
+};
+
 template <int D_>
 struct F32 {
   static constexpr int D = D_;
@@ -415,7 +427,8 @@ struct F32 {
   static constexpr int kVLoads = kVF;
   static constexpr int kEbKV = kEb;
   static constexpr bool kScaled = false;
-  static constexpr int kCostRow = kCostRowSplit;
+  static constexpr int kRowTiles = 1;
+  static constexpr int kRowGeom = row_geom(kCostRowSplit, kRowTiles);
   using VRaw = u32x4_t;
 
   __device__ static int q_off(int f, int quad) { return (16 * f + 4 * quad) * kEb; }
@@ -525,7 +538,8 @@ struct Fp8Kv {
   static constexpr bool kBf16 = true;
   static constexpr int kVLoads = 2 * kVF;
   static constexpr bool kScaled = true;
-  static constexpr int kCostRow = kCostRowSplitFp8;
+  static constexpr int kRowTiles = 1;
+  static constexpr int kRowGeom = row_geom(kCostRowSplitFp8, kRowTiles);
   using VRaw = u32x2_t;  // 4 codes of page 0 (keys 4q..4q+3), 4 codes of page 1
 
   __device__ static int q_off(int f, int quad) { return (32 * f + 8 * quad) * kEb; }
@@ -1204,20 +1218,21 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, const Seq
 }
 
 // ---------------------------------------------------------------------------
-// Row-split unit (prefill, <= 64 rows): wave w owns rows [16w, 16w+16).  The
-// workgroup streams chunks through an LDS ring with global->LDS DMA; every wave
-// issues 1/4 of each chunk.  A step covers NP chunks (64 keys; 32 for fp32 pages
-// at D = 128, whose chunks fill half the ring each) under one barrier and one
-// softmax pass, and the ring holds two steps: the next step's chunks land while
-// this one is computed.
+// Row-split unit (prefill, <= 64 x kRowTiles rows): wave w owns rows [16 RT w, 16 RT (w + 1)).
+// The workgroup streams chunks through an LDS ring with global->LDS DMA; every wave issues 1/4 of
+// each chunk.  A step covers NP chunks (64 keys with one row tile per wave; 32 for fp32 pages at
+// D = 128, whose chunks fill half the ring each, and with two row tiles, whose registers hold one
+// chunk) under one barrier and one softmax pass, and the ring holds at least two steps: the next
+// step's chunks land while this one is computed.
 // ---------------------------------------------------------------------------
 template <class TR, bool kTree>
 __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, const SeqUnits& sq, int i0, int i1, int part,
                              Smem<TR>& sm) {
   using RG = Ring<TR>;
-  constexpr int RT = kRowTiles;
+  constexpr int RT = TR::kRowTiles;
   constexpr int kWaveRows = 16 * RT;  // rows of each wave
-  constexpr int NP = RG::kNB / 2;     // chunks per step
+  // chunks per step: two with one row tile per wave; one with two (their registers hold one chunk)
+  constexpr int NP = RT == 1 ? RG::kNB / 2 : 1;
   static_assert(RG::kNB == 4 || RG::kNB == 2, "ring of two steps");
   int lane = threadIdx.x & 63;
   asm volatile("" : "+v"(lane));  // lane-derived values are recomputed per unit, not held across the unit loop
@@ -1384,18 +1399,20 @@ __device__ __forceinline__ int64_t slice_begin(int64_t k, int64_t S, int64_t C) 
 
 // ---------------------------------------------------------------------------
 // The plan.  Sequence s contributes Hkv groups of nb units (nb = 1 when its
-// q_len * G rows fit one key-split unit, else ceil(rows / kBlockRows) row blocks);
+// q_len * G rows fit one key-split unit, else ceil(rows / R) row blocks of R rows, R set by the
+// kernel's row geometry);
 // units are ordered (sequence, kv head, row block) on one cost axis.  Only the
 // per-sequence cost prefix is stored; units are rebuilt from it on the fly.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// keys visible to the last row of row block rb of a sequence (n keys, qn tokens, G heads; with
-// full rows every row sees all n keys)
+// keys visible to the last row of row block rb (R rows per block) of a sequence (n keys, qn
+// tokens, G heads; with full rows every row sees all n keys)
+template <int R>
 __device__ __forceinline__ int block_keys(int n, int qn, int G, int rb, bool full) {
   if (full) return n;
   const int rows = qn * G;
-  const int last = (min(kBlockRows * (rb + 1), rows) - 1) / G;
+  const int last = (min(R * (rb + 1), rows) - 1) / G;
   return n - qn + last + 1;
 }
 
@@ -1425,20 +1442,21 @@ __device__ __forceinline__ int64_t floor_sum(uint32_t n, uint32_t m, uint32_t a,
 }
 
 // Chunks of row blocks 0 .. r-1 of a sequence, r < nb (none of them the last block).  With
-// R = kBlockRows rows per block, block rb's last row is token floor((R rb + R - 1) / G), so it sees
+// R rows per block, block rb's last row is token floor((R rb + R - 1) / G), so it sees
 // keys(rb) = c + floor((R rb + R - 1) / G) keys, c = n - qn + 1, and ceil(keys / 32) =
 // floor((R rb + G (c + 31) + R - 1) / (32 G)) (a floor of a floor is one floor of the product).
 // That numerator's constant B splits into 32 G h + b with h = floor((c + 31 + floor((R - 1) / G))
 // / 32) and 0 <= b < 32 G, which leaves a floor sum over rb with small coefficients.
+template <int R>
 __device__ __forceinline__ int64_t block_chunks_before(int n, int qn, int G, bool full, int r) {
   if (full) return int64_t(r) * ceil_div(n, kChunkKeys);
   const int x = n - qn + kChunkKeys;  // c + 31
-  const int h = (x + (kBlockRows - 1) / G) / kChunkKeys;
-  const int b = G * (x - kChunkKeys * h) + kBlockRows - 1;
-  return int64_t(r) * h + floor_sum(uint32_t(r), uint32_t(kChunkKeys * G), kBlockRows, uint32_t(b));
+  const int h = (x + (R - 1) / G) / kChunkKeys;
+  const int b = G * (x - kChunkKeys * h) + R - 1;
+  return int64_t(r) * h + floor_sum(uint32_t(r), uint32_t(kChunkKeys * G), R, uint32_t(b));
 }
 
-template <int kRw = kCostRowSplit>
+template <int kRg = kRgDefault>
 __device__ SeqUnits seq_units(int n, int q0, int qn, int G, bool full) {
   SeqUnits q;
   q.n = n;
@@ -1454,10 +1472,10 @@ __device__ SeqUnits seq_units(int n, int q0, int qn, int G, bool full) {
     q.nb = 1;
     q.per_head = unit_start_cost(true, q.rows) + int64_t(ceil_div(n, kChunkKeys)) * kCostKeySplit;
   } else {
-    q.nb = ceil_div(q.rows, kBlockRows);
+    q.nb = ceil_div(q.rows, rg_rows(kRg));
     // the last block's last row is the window's last token: it sees all n keys
-    const int64_t ch = block_chunks_before(n, qn, G, full, q.nb - 1) + ceil_div(n, kChunkKeys);
-    q.per_head = int64_t(q.nb) * kCostStartRow + ch * kRw;
+    const int64_t ch = block_chunks_before<rg_rows(kRg)>(n, qn, G, full, q.nb - 1) + ceil_div(n, kChunkKeys);
+    q.per_head = int64_t(q.nb) * kCostStartRow + ch * rg_weight(kRg);
   }
   return q;
 }
@@ -1472,22 +1490,23 @@ __device__ __forceinline__ int64_t chunk_start(const pa_plan_unit& U, int i) {
 }
 
 // Cost from the start of a kv head's row blocks to the start of block rb (rb < nb).
-template <int kRw>
+template <int kRg>
 __device__ __forceinline__ int64_t block_start(const SeqUnits& q, int G, int rb) {
-  return int64_t(rb) * kCostStartRow + block_chunks_before(q.n, q.qn, G, q.full, rb) * kRw;
+  return int64_t(rb) * kCostStartRow + block_chunks_before<rg_rows(kRg)>(q.n, q.qn, G, q.full, rb) * rg_weight(kRg);
 }
 
-template <int kRw>
+template <int kRg>
 __device__ pa_plan_unit make_unit(int s, const SeqUnits& q, int G, int g, int rb, int64_t cost0) {
   pa_plan_unit U;
   U.seq = s;
   U.kv_head = g;
-  U.row0 = q.split ? 0 : rb * kBlockRows;
-  U.n_rows = q.split ? q.rows : min(kBlockRows, q.rows - rb * kBlockRows);
-  U.n_keys = q.split ? q.n : block_keys(q.n, q.qn, G, rb, q.full);
+  constexpr int R = rg_rows(kRg);
+  U.row0 = q.split ? 0 : rb * R;
+  U.n_rows = q.split ? q.rows : min(R, q.rows - rb * R);
+  U.n_keys = q.split ? q.n : block_keys<R>(q.n, q.qn, G, rb, q.full);
   U.n_chunks = ceil_div(U.n_keys, kChunkKeys);
   U.kind = q.split ? 0 : 1;
-  U.cost_weight = q.split ? kCostKeySplit : kRw;
+  U.cost_weight = q.split ? kCostKeySplit : rg_weight(kRg);
   U.cost0 = cost0;
   U.first_slot = 0;
   U.n_pieces = 0;
@@ -1502,20 +1521,20 @@ struct UnitCursor {
   pa_plan_unit U;
 };
 
-template <int kRw, class P>
+template <int kRg, class P>
 __device__ void cursor_load_seq(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl) {
   const int q0 = qsl[cu.s];
-  cu.q = seq_units<kRw>(seq_lens[cu.s], q0, qsl[cu.s + 1] - q0, v.group, v.full_rows != 0);
+  cu.q = seq_units<kRg>(seq_lens[cu.s], q0, qsl[cu.s + 1] - q0, v.group, v.full_rows != 0);
 }
 
 // Position the cursor on the unit of sequence s (n keys, queries q0 .. q0 + qn - 1, starting at
 // cost seq_base) whose cost range holds c.
-template <int kRw>
+template <int kRg>
 __device__ void cursor_place(UnitCursor& cu, const PlanView& v, int s, int64_t seq_base, int n, int q0, int qn,
                              int64_t c) {
   cu.s = s;
   cu.seq_base = seq_base;
-  cu.q = seq_units<kRw>(n, q0, qn, v.group, v.full_rows != 0);
+  cu.q = seq_units<kRg>(n, q0, qn, v.group, v.full_rows != 0);
   const int64_t off = c - cu.seq_base;
   cu.g = int(off / cu.q.per_head);
   int64_t acc = cu.seq_base + int64_t(cu.g) * cu.q.per_head;
@@ -1525,12 +1544,12 @@ __device__ void cursor_place(UnitCursor& cu, const PlanView& v, int s, int64_t s
     int lo = 0, hi = cu.q.nb - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (acc + block_start<kRw>(cu.q, v.group, mid) <= c) lo = mid; else hi = mid - 1;
+      if (acc + block_start<kRg>(cu.q, v.group, mid) <= c) lo = mid; else hi = mid - 1;
     }
     cu.rb = lo;
-    acc += block_start<kRw>(cu.q, v.group, lo);
+    acc += block_start<kRg>(cu.q, v.group, lo);
   }
-  cu.U = make_unit<kRw>(cu.s, cu.q, v.group, cu.g, cu.rb, acc);
+  cu.U = make_unit<kRg>(cu.s, cu.q, v.group, cu.g, cu.rb, acc);
 }
 
 // cursor_place done by all 64 lanes of a wave together (every lane gets the same cursor): the
@@ -1538,20 +1557,21 @@ __device__ void cursor_place(UnitCursor& cu, const PlanView& v, int s, int64_t s
 // at or below c.  Up to 64 blocks: lane r takes block r's chunk count and a wave scan of the
 // counts gives every start; more blocks: lanes evaluate floor-sum starts of 64 candidates per
 // round (two rounds for up to 4096) -- instead of a serial binary search of floor sums.
-template <int kRw>
+template <int kRg>
 __device__ void cursor_place_wave(UnitCursor& cu, const PlanView& v, int s, int64_t seq_base, int n, int q0, int qn,
                                   int64_t c, int lane) {
   cu.s = s;
   cu.seq_base = seq_base;
-  cu.q = seq_units<kRw>(n, q0, qn, v.group, v.full_rows != 0);
+  cu.q = seq_units<kRg>(n, q0, qn, v.group, v.full_rows != 0);
   const int64_t off = c - cu.seq_base;
   cu.g = int(off / cu.q.per_head);
   int64_t acc = cu.seq_base + int64_t(cu.g) * cu.q.per_head;
   cu.rb = 0;
   if (!cu.q.split && cu.q.nb <= 64) {
     // one block per lane: its chunk count, and a wave scan of the counts gives every block's start
-    const int64_t ch = lane < cu.q.nb ? ceil_div(block_keys(n, qn, v.group, lane, cu.q.full), kChunkKeys) : 0;
-    const int64_t start = int64_t(lane) * kCostStartRow + (wave_incl_scan64(ch) - ch) * kRw;
+    const int64_t ch =
+        lane < cu.q.nb ? ceil_div(block_keys<rg_rows(kRg)>(n, qn, v.group, lane, cu.q.full), kChunkKeys) : 0;
+    const int64_t start = int64_t(lane) * kCostStartRow + (wave_incl_scan64(ch) - ch) * rg_weight(kRg);
     const uint64_t below = __ballot(lane < cu.q.nb && acc + start <= c);  // a prefix of the lanes
     const int rb = 63 - __builtin_clzll(below);
     cu.rb = rb;
@@ -1563,7 +1583,7 @@ __device__ void cursor_place_wave(UnitCursor& cu, const PlanView& v, int s, int6
     while (lo < hi) {
       const int step = (hi - lo + 64) / 64;  // candidates lo, lo + step, ... cover [lo, hi]
       const int r = min(lo + lane * step, hi);
-      const uint64_t below = __ballot(acc + block_start<kRw>(cu.q, v.group, r) <= c);  // a prefix of the lanes
+      const uint64_t below = __ballot(acc + block_start<kRg>(cu.q, v.group, r) <= c);  // a prefix of the lanes
       const int last = 63 - __builtin_clzll(below);
       const int r_last = min(lo + last * step, hi);
       hi = min(r_last + step - 1, hi);
@@ -1571,13 +1591,13 @@ __device__ void cursor_place_wave(UnitCursor& cu, const PlanView& v, int s, int6
       if (step == 1) break;
     }
     cu.rb = lo;
-    acc += block_start<kRw>(cu.q, v.group, lo);
+    acc += block_start<kRg>(cu.q, v.group, lo);
   }
-  cu.U = make_unit<kRw>(cu.s, cu.q, v.group, cu.g, cu.rb, acc);
+  cu.U = make_unit<kRg>(cu.s, cu.q, v.group, cu.g, cu.rb, acc);
 }
 
 // Position the cursor on the unit whose cost range holds c (0 <= c < total).
-template <int kRw = kCostRowSplit, class P, class Q>
+template <int kRg = kRgDefault, class P, class Q>
 __device__ void cursor_find(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl, Q seq_cost, int64_t c) {
   int lo = 0, hi = v.num_seqs - 1;  // last s with seq_cost[s] <= c
   while (lo < hi) {
@@ -1585,7 +1605,7 @@ __device__ void cursor_find(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl
     if (seq_cost[mid] <= c) lo = mid; else hi = mid - 1;
   }
   const int q0 = qsl[lo];
-  cursor_place<kRw>(cu, v, lo, seq_cost[lo], seq_lens[lo], q0, qsl[lo + 1] - q0, c);
+  cursor_place<kRg>(cu, v, lo, seq_cost[lo], seq_lens[lo], q0, qsl[lo + 1] - q0, c);
 }
 
 __device__ __forceinline__ SlotStart slot_from_cursor(const UnitCursor& cu, int64_t c0, int64_t c1) {
@@ -1605,14 +1625,14 @@ __device__ __forceinline__ SlotStart slot_from_cursor(const UnitCursor& cu, int6
 }
 
 // Position the cursor as the planner recorded for one slot.
-template <int kRw = kCostRowSplit>
+template <int kRg = kRgDefault>
 __device__ __forceinline__ void cursor_from_slot(UnitCursor& cu, const PlanView& v, const SlotStart& st) {
   cu.s = st.s;
   cu.g = st.g;
   cu.rb = st.rb;
   cu.seq_base = st.seq_base;
-  cu.q = seq_units<kRw>(st.n, st.q0, st.qn, v.group, v.full_rows != 0);
-  cu.U = make_unit<kRw>(st.s, cu.q, v.group, st.g, st.rb, st.unit_cost0);
+  cu.q = seq_units<kRg>(st.n, st.q0, st.qn, v.group, v.full_rows != 0);
+  cu.U = make_unit<kRg>(st.s, cu.q, v.group, st.g, st.rb, st.unit_cost0);
 }
 
 __device__ __forceinline__ SlotStart load_slot(cptr<SlotStart> p) {
@@ -1631,7 +1651,7 @@ __device__ __forceinline__ SlotStart load_slot(cptr<SlotStart> p) {
 }
 
 // Advance to the next unit; returns false past the last one.
-template <int kRw = kCostRowSplit, class P>
+template <int kRg = kRgDefault, class P>
 __device__ bool cursor_next(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl) {
   const int64_t next_cost = cu.U.cost0 + unit_cost(cu.U);
   if (++cu.rb >= cu.q.nb) {
@@ -1641,11 +1661,11 @@ __device__ bool cursor_next(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl
       do {
         cu.seq_base += int64_t(v.num_kv_heads) * cu.q.per_head;
         if (++cu.s >= v.num_seqs) return false;
-        cursor_load_seq<kRw>(cu, v, seq_lens, qsl);
+        cursor_load_seq<kRg>(cu, v, seq_lens, qsl);
       } while (cu.q.nb == 0);
     }
   }
-  cu.U = make_unit<kRw>(cu.s, cu.q, v.group, cu.g, cu.rb, next_cost);
+  cu.U = make_unit<kRg>(cu.s, cu.q, v.group, cu.g, cu.rb, next_cost);
   return true;
 }
 
@@ -1745,23 +1765,24 @@ __device__ void merge_unit(const float* part_o, const float* part_lse, void* out
   };
   constexpr int kLanesPerRow = TR::D / 4;
   constexpr int kRowsPerPass = kThreads / kLanesPerRow;
-  constexpr int kRows = kPartRows / kRowsPerPass;  // rows of each thread
+  constexpr int kMergeRows = 64;                   // rows folded per pass (a 128-row unit takes two)
+  constexpr int kRows = kMergeRows / kRowsPerPass;  // rows of each thread per pass
   constexpr int kP = 16 / kRows;                   // pieces per round trip
   const int d4 = threadIdx.x % kLanesPerRow, r0 = threadIdx.x / kLanesPerRow;
   f32x4_t oj[kP][kRows];
-  auto load_pieces = [&](int j0) {
+  auto load_pieces = [&](int j0, int rbase) {
 #pragma unroll
     for (int p = 0; p < kP; ++p)
 #pragma unroll
       for (int i = 0; i < kRows; ++i) {
-        const int r = r0 + i * kRowsPerPass;
+        const int r = rbase + r0 + i * kRowsPerPass;
         oj[p][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if (j0 + p < n_pieces && r < U.n_rows)
           oj[p][i] = load_coherent4(part_o, ((pbase(j0 + p) + r) * TR::D + 4 * d4) * 4);
       }
   };
   // the first pieces' o rows are loaded before the lse round trip, so the two latencies overlap
-  load_pieces(0);
+  load_pieces(0, 0);
   for (int r = threadIdx.x; r < U.n_rows; r += kThreads) {
     float lj[kMergeFastPieces];
 #pragma unroll
@@ -1785,26 +1806,28 @@ __device__ void merge_unit(const float* part_o, const float* part_lse, void* out
   }
   wait_lds();
   lds_barrier();  // wbuf written (a full __syncthreads would also wait for the o loads in flight)
-  f32x4_t acc[kRows];
+  for (int rbase = 0; rbase < U.n_rows; rbase += kMergeRows) {
+    f32x4_t acc[kRows];
 #pragma unroll
-  for (int i = 0; i < kRows; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int j0 = 0; j0 < n_pieces; j0 += kP) {
-    if (j0 > 0) load_pieces(j0);
+    for (int i = 0; i < kRows; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < n_pieces; j0 += kP) {
+      if (j0 > 0 || rbase > 0) load_pieces(j0, rbase);
 #pragma unroll
-    for (int p = 0; p < kP; ++p)
+      for (int p = 0; p < kP; ++p)
 #pragma unroll
-      for (int i = 0; i < kRows; ++i) {
-        const int r = r0 + i * kRowsPerPass;
-        if (j0 + p < n_pieces && r < U.n_rows) acc[i] += oj[p][i] * wbuf[(j0 + p) * kPartRows + r];
-      }
-  }
+        for (int i = 0; i < kRows; ++i) {
+          const int r = rbase + r0 + i * kRowsPerPass;
+          if (j0 + p < n_pieces && r < U.n_rows) acc[i] += oj[p][i] * wbuf[(j0 + p) * kPartRows + r];
+        }
+    }
 #pragma unroll
-  for (int i = 0; i < kRows; ++i) {
-    const int r = r0 + i * kRowsPerPass;
-    if (r >= U.n_rows) continue;
-    const int64_t orow = out_row(r);
-    if (out_f32) *reinterpret_cast<f32x4_t*>(out_f32 + orow * TR::D + 4 * d4) = acc[i];
-    else TR::store_out(static_cast<char*>(out) + (orow * TR::D + 4 * d4) * TR::kEb, acc[i]);
+    for (int i = 0; i < kRows; ++i) {
+      const int r = rbase + r0 + i * kRowsPerPass;
+      if (r >= U.n_rows) continue;
+      const int64_t orow = out_row(r);
+      if (out_f32) *reinterpret_cast<f32x4_t*>(out_f32 + orow * TR::D + 4 * d4) = acc[i];
+      else TR::store_out(static_cast<char*>(out) + (orow * TR::D + 4 * d4) * TR::kEb, acc[i]);
+    }
   }
   __syncthreads();  // wbuf is read by every thread before the caller reuses LDS
 }
@@ -1940,7 +1963,7 @@ __device__ void run_keysplit_stream(const AttnArgs& A, UnitCursor& cu, Piece p, 
     RowInfo rnext{0, 0, -1, false};
     {
       UnitCursor nc = cu;
-      nxt = cursor_next<TR::kCostRow>(nc, v, seq_lens, qsl) && nc.U.cost0 < c1 && same_kind(nc.U);
+      nxt = cursor_next<TR::kRowGeom>(nc, v, seq_lens, qsl) && nc.U.cost0 < c1 && same_kind(nc.U);
       if (nxt) {
         const Piece np = piece_of(nc.U, c0, c1, grain);
         nxt = np.i0 < np.i1;
@@ -2070,7 +2093,7 @@ __device__ void run_keysplit_stream(const AttnArgs& A, UnitCursor& cu, Piece p, 
       lds_barrier();  // the merge reads are done (each waited in place) before the region is rewritten
     }
     if (!nxt) return;
-    cursor_next<TR::kCostRow>(cu, v, seq_lens, qsl);
+    cursor_next<TR::kRowGeom>(cu, v, seq_lens, qsl);
     p = piece_of(cu.U, c0, c1, grain);
     pre = true;
   }
@@ -2088,7 +2111,7 @@ __device__ __forceinline__ void run_grain(const AttnArgs& A, int grain, const Sl
   const cptr<int32_t> seq_lens = ro(v.seq_lens);
   const cptr<int32_t> qsl = ro(v.qsl);
   UnitCursor cu;
-  cursor_from_slot<TR::kCostRow>(cu, v, st);
+  cursor_from_slot<TR::kRowGeom>(cu, v, st);
   do {
     const pa_plan_unit& U = cu.U;
     if (U.cost0 >= c1) break;
@@ -2118,7 +2141,7 @@ __device__ __forceinline__ void run_grain(const AttnArgs& A, int grain, const Sl
           arrive_and_merge<TR>(A, cu.U, S, C, flag, reinterpret_cast<float*>(sm.buf));
       }
     }
-  } while (cursor_next<TR::kCostRow>(cu, v, seq_lens, qsl));
+  } while (cursor_next<TR::kRowGeom>(cu, v, seq_lens, qsl));
 }
 
 // Staged path: workgroup b runs grain b, b + grid, ... of the plan in the workspace.
@@ -2208,7 +2231,7 @@ struct PreLds {
 
 // Cost of the kPer sequences of this thread in the block of kThreads * kPer at `base`
 // (c), and the part of their sum that is row-split work (returned).
-template <int kPer, int kRw>
+template <int kPer, int kRg>
 __device__ __forceinline__ int64_t block_seq_costs(const PlanView& v, cptr<int32_t> sl, cptr<int32_t> qsl, int base,
                                                    int64_t (&c)[kPer], int (&n)[kPer], int (&q0)[kPer],
                                                    int (&qn)[kPer]) {
@@ -2222,7 +2245,7 @@ __device__ __forceinline__ int64_t block_seq_costs(const PlanView& v, cptr<int32
       n[e] = sl[s];
       q0[e] = qsl[s];
       qn[e] = qsl[s + 1] - q0[e];
-      const SeqUnits q = seq_units<kRw>(n[e], q0[e], qn[e], v.group, v.full_rows != 0);
+      const SeqUnits q = seq_units<kRg>(n[e], q0[e], qn[e], v.group, v.full_rows != 0);
       c[e] = int64_t(v.num_kv_heads) * q.per_head;
       if (!q.split) row += c[e];
     }
@@ -2258,13 +2281,13 @@ __device__ __forceinline__ int64_t grain_of_block(int b, int grid, int64_t S) {
 // start in pl.st.  Each thread takes kPer sequences per pass of kThreads * kPer (one when the
 // batch fits one pass, so that no thread computes several sequences' costs in a row).  Returns
 // the grain index; S or more means the workgroup has none.
-template <int kPer, bool kSolo, int kRw>
+template <int kPer, bool kSolo, int kRg>
 __device__ __forceinline__ int64_t plan_grain(const PlanView& v, PreLds& pl, int64_t& S, int64_t& C) {
   const cptr<int32_t> sl = ro(v.seq_lens), qsl = ro(v.qsl);
   constexpr int kBlock = kThreads * kPer;
   int64_t c[kPer];
   int n[kPer], q0[kPer], qn[kPer];
-  const int64_t row0 = block_seq_costs<kPer, kRw>(v, sl, qsl, 0, c, n, q0, qn);  // kept for the search below
+  const int64_t row0 = block_seq_costs<kPer, kRg>(v, sl, qsl, 0, c, n, q0, qn);  // kept for the search below
   C = 0;
   int64_t Cr = 0;
   // one block of sequences: the totals and this block's prefix come from one exchange
@@ -2279,7 +2302,7 @@ __device__ __forceinline__ int64_t plan_grain(const PlanView& v, PreLds& pl, int
   for (int base = 0; !one && base < v.num_seqs; base += kBlock) {
     int64_t c2[kPer];
     int n2[kPer], q02[kPer], qn2[kPer];
-    const int64_t row = base > 0 ? block_seq_costs<kPer, kRw>(v, sl, qsl, base, c2, n2, q02, qn2) : row0;
+    const int64_t row = base > 0 ? block_seq_costs<kPer, kRg>(v, sl, qsl, base, c2, n2, q02, qn2) : row0;
     int64_t x = 0;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) x += base > 0 ? c2[e] : c[e];
@@ -2293,13 +2316,13 @@ __device__ __forceinline__ int64_t plan_grain(const PlanView& v, PreLds& pl, int
     S = 0;
     return 0;
   }
-  S = grain_count(C - Cr, Cr, grid, kRw);
+  S = grain_count(C - Cr, Cr, grid, rg_weight(kRg));
   const int64_t k = grain_of_block(int(blockIdx.x), grid, S);
   if (k >= S) return k;
   const int64_t c0 = slice_begin(k, S, C), c1 = slice_begin(k + 1, S, C);
   int64_t carry = 0;
   for (int base = 0; base < v.num_seqs; base += kBlock) {
-    if (base > 0) block_seq_costs<kPer, kRw>(v, sl, qsl, base, c, n, q0, qn);
+    if (base > 0) block_seq_costs<kPer, kRg>(v, sl, qsl, base, c, n, q0, qn);
     int64_t x = 0;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) x += c[e];
@@ -2324,7 +2347,7 @@ __device__ __forceinline__ int64_t plan_grain(const PlanView& v, PreLds& pl, int
   __syncthreads();
   if (threadIdx.x < 64) {  // wave 0 places the cursor
     UnitCursor cu;
-    cursor_place_wave<kRw>(cu, v, pl.hold_s, pl.hold_base, pl.hold_n, pl.hold_q0, pl.hold_qn, c0, int(threadIdx.x));
+    cursor_place_wave<kRg>(cu, v, pl.hold_s, pl.hold_base, pl.hold_n, pl.hold_q0, pl.hold_qn, c0, int(threadIdx.x));
     if (threadIdx.x == 0) pl.st = slot_from_cursor(cu, c0, c1);
   }
   __syncthreads();
@@ -2339,8 +2362,8 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fused_kernel(AttnArgs A
   __shared__ PreLds pl;
   int64_t S, C;
   constexpr bool kSolo = !TR::kScaled;  // FP8 pages stream faster with both workgroups of a CU
-  const int64_t k = A.plan.num_seqs <= kThreads ? plan_grain<1, kSolo, TR::kCostRow>(A.plan, pl, S, C)
-                                                : plan_grain<4, kSolo, TR::kCostRow>(A.plan, pl, S, C);
+  const int64_t k = A.plan.num_seqs <= kThreads ? plan_grain<1, kSolo, TR::kRowGeom>(A.plan, pl, S, C)
+                                                : plan_grain<4, kSolo, TR::kRowGeom>(A.plan, pl, S, C);
   if (k >= S) return;
   const SlotStart st = pl.st;
   run_grain<TR, true, kTree>(A, int(k), st, S, C, sm, &pl.flag);
@@ -2653,7 +2676,12 @@ static int launch_fused_t(const AttnArgs& a, int grid, void* stream) {
   return int(hipGetLastError());
 }
 
-int launch_attention_fused(const AttnArgs& a, int dtype, int D, int grid, void* stream) {
+int launch_attention_fused(const AttnArgs& a, int dtype, int D, int grid, void* stream, bool tall) {
+  if (dtype == PA_BF16 && D == 128 && tall && !a.tree_mask) {
+    hipLaunchKernelGGL((attention_fused_kernel<Bf16Tall<128>, false>), dim3(grid), dim3(kThreads), 0,
+                       as_stream(stream), a);
+    return int(hipGetLastError());
+  }
   if (dtype == PA_BF16) return D == 128 ? launch_fused_t<Bf16<128>>(a, grid, stream) : launch_fused_t<Bf16<64>>(a, grid, stream);
   return D == 128 ? launch_fused_t<F32<128>>(a, grid, stream) : launch_fused_t<F32<64>>(a, grid, stream);
 }
@@ -2673,7 +2701,7 @@ int launch_attention_fp8kv(const AttnArgs& a, int D, int grid, void* stream) {
 // paths give bitwise identical results.
 template <class TR>
 static int blocks_per_cu_t() {
-  int n = 0, m = 0, t = 0;
+  int n = 0, m = 0, t = 0, h = 1 << 20;
   void (*staged)(AttnArgs) = attention_kernel<TR>;
   void (*fused)(AttnArgs) = attention_fused_kernel<TR, false>;
   void (*tree)(AttnArgs) = attention_fused_kernel<TR, true>;
@@ -2684,7 +2712,14 @@ static int blocks_per_cu_t() {
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&t, reinterpret_cast<const void*>(tree), kThreads, 0) !=
           hipSuccess)
     return -1;
+  if constexpr (std::is_same<TR, Bf16<128>>::value) {  // the 128-row-block kernel shares the grid
+    void (*tall)(AttnArgs) = attention_fused_kernel<Bf16Tall<128>, false>;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&h, reinterpret_cast<const void*>(tall), kThreads, 0) !=
+        hipSuccess)
+      return -1;
+  }
   n = n < m ? n : m;
+  n = n < h ? n : h;
   return n < t ? n : t;
 }
 

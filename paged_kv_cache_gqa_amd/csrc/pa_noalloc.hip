@@ -16,7 +16,7 @@
 namespace {
 
 // Largest attention grid the scratch serves: 256 compute units x 2 workgroups (MI355X).  With
-// 64-row partial results of D <= 128 floats that is 32.3 MiB per device.
+// partial results of up to 128 rows of D <= 128 floats that is 64.3 MiB per device.
 constexpr int kScratchGrid = 512;
 constexpr int kScratchMaxD = 128;
 constexpr size_t kArriveBytes = pa::align256(sizeof(int32_t) * kScratchGrid);
@@ -70,5 +70,7 @@ extern "C" pa_status pa_attention_noalloc(const pa_desc* desc, const void* q, co
   float* part_o = reinterpret_cast<float*>(base + kArriveBytes + kPartLseBytes);
   const pa::AttnArgs a = pa::single_launch_args(*desc, q, k_pool, v_pool, block_table, seq_lens, query_start_loc,
                                                 out, lse, part_o, part_lse, arrive);
-  return pa::launch_attention_fused(a, desc->dtype, desc->head_dim, grid, stream) == 0 ? PA_OK : PA_ERR_HIP;
+  return pa::launch_attention_fused(a, desc->dtype, desc->head_dim, grid, stream, pa::tall_blocks(*desc, grid)) == 0
+             ? PA_OK
+             : PA_ERR_HIP;
 }

@@ -140,6 +140,26 @@ def test_single_long_sequence_max_length():
     check(w, out, lse)
 
 
+# Batches with T_q * Hq >= 64 x (workgroups) run 128-row row blocks (two row tiles per wave); these
+# keep T_q * Hq above 64 x 1024, past the threshold for any grid up to 1024 workgroups.
+TALL_CASES = [
+    # name, seed, seq_lens, q_lens, Hq, Hkv
+    ("g4", 84, [2500, 1700, 2048, 900], [2000, 1200, 2048, 900], 32, 8),
+    ("g7", 85, [3000, 2222, 1500], [2900, 1400, 1500], 28, 4),  # 128-row blocks end mid-token
+    ("g8-mixed", 86, [6000, 9000] + [700 + 37 * i for i in range(40)] + [1200 + 91 * i for i in range(10)],
+     [6000, 3000] + [1] * 40 + [5] * 10, 8, 1),  # with decode rows and verify windows
+]
+
+
+@pytest.mark.parametrize("case", TALL_CASES, ids=[c[0] for c in TALL_CASES])
+def test_tall_row_blocks(case):
+    name, seed, n, q, hq, hkv = case
+    assert sum(q) * hq >= 64 * 1024
+    w = W.build(f"tall-{name}", seed, n, q, hq, hkv, 128, "bf16")
+    out, lse = run_gpu(w)
+    check(w, out, lse)
+
+
 def test_million_key_sequences_split_over_hundreds_of_grains():
     """2^20 + 3 keys (65537 pages per sequence): a decode row group (one key-split unit of 32769
     chunks) and a 64-row prefill block over almost the same length (one row-split unit).  The grid's

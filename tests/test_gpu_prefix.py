@@ -48,6 +48,7 @@ CASES = [
     (122, [5, 3], [512, 256], 300, 1, 32, 8, 128, "bf16"),      # decode groups: key-split prefix units
     (123, [2, 3], [512, 1024], 400, 300, 8, 1, 128, "bf16"),    # prefill windows: 64-row units in both passes
     (124, [16], [2048], 500, 4, 32, 8, 128, "bf16"),            # one big group, verify-sized windows
+    (126, [6, 6], [1024, 512], 1500, 1500, 8, 1, 128, "bf16"),  # long windows: 128-row blocks in both passes
     (125, [1, 1, 1, 1], [0, 0, 0, 0], 300, 6, 12, 3, 64, "bf16"),  # no sharing at all
 ]
 

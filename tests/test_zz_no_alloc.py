@@ -45,13 +45,14 @@ def _noalloc_abi(t, w, out, lse):
     assert rc == 0, pa.status_str(rc)
 
 
-@pytest.mark.parametrize("first,second", [(3, 2), (4, 1)])
+@pytest.mark.parametrize("first,second", [(3, 2), (4, 1), ("tile", 3)])
 def test_noalloc_equals_attention_on_two_calls(first, second):
     """Two calls in a row on the shared scratch, the second with a smaller batch: each equals
     pa_attention (bitwise) and matches the oracle.  The mixed batch (configuration 3) and the
-    llama3-8b decode batch (configuration 2) both have key-split units merged through the scratch."""
+    llama3-8b decode batch (configuration 2) both have key-split units merged through the scratch;
+    the long prefill tile runs 128-row blocks, whose split pieces fill the scratch's largest slots."""
     for c in (first, second):
-        w = W.make_config(c)
+        w = W.make_long_prefill() if c == "tile" else W.make_config(c)
         t = pa.to_device(w)
         ref_o, ref_l = pa.attention(t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
                                     t["query_start_loc"], w.scale)
