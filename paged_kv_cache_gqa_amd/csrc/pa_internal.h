@@ -33,8 +33,8 @@ constexpr int kPlanThreads = 1024;
 // measured wall time on MI355X (mixed prefill + decode batch): a chunk of a
 // row-split unit (prefill: up to 64 rows of MFMA work on one chunk staged in
 // LDS) takes about as long as a chunk of a key-split unit (decode / verify:
-// one wave streams 8 KiB of K and 8 KiB of V from HBM for a few rows).  With
-// 128-row units (two row tiles per wave) the row-split weight was 5.
+// one wave streams 8 KiB of K and 8 KiB of V from HBM for a few rows).  A chunk of a 128-row
+// unit weighs twice as much (8: of 4, 8 and 16 the fastest on prefill-heavy mixed batches).
 constexpr int kCostKeySplit = 4;
 constexpr int kCostRowSplit = 4;
 constexpr int kRgDefault = row_geom(kCostRowSplit, 1);  // the staged planner's geometry
