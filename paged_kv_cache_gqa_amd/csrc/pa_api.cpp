@@ -424,7 +424,8 @@ pa_status pa_attention_fp8kv(const pa_desc* desc, const void* q, const uint8_t* 
   pa::AttnArgs a = attn_args(*desc, q, k_pool, v_pool, block_table, seq_lens, qsl, out, lse, ws);
   a.k_scale = k_scale;
   a.v_scale = v_scale;
-  return pa::launch_attention_fp8kv(a, desc->head_dim, grid, stream) == 0 ? PA_OK : PA_ERR_HIP;
+  return pa::launch_attention_fp8kv(a, desc->head_dim, grid, stream, pa::tall_blocks(*desc, grid)) == 0 ? PA_OK
+                                                                                                      : PA_ERR_HIP;
 }
 
 pa_status pa_attention_tree(const pa_desc* desc, const void* q, const void* k_pool, const void* v_pool,

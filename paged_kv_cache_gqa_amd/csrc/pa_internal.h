@@ -230,7 +230,7 @@ int launch_attention(const AttnArgs& a, int dtype, int head_dim, int grid, void*
 // tall: bf16 at head dim 128 without tree masks runs the kernel with 128-row row blocks
 int launch_attention_fused(const AttnArgs& a, int dtype, int head_dim, int grid, void* stream, bool tall = false);
 // single launch over FP8 E4M3 pages (bf16 q / out; a.k_scale, a.v_scale set)
-int launch_attention_fp8kv(const AttnArgs& a, int head_dim, int grid, void* stream);
+int launch_attention_fp8kv(const AttnArgs& a, int head_dim, int grid, void* stream, bool tall = false);
 int launch_fill_zero(void* p, size_t bytes, void* stream);
 int launch_read_stream(const void* buf, size_t bytes, int grid, uint32_t* sink, void* stream);
 int launch_merge_planned(const MergeArgs& a, int dtype, int head_dim, int grid, void* stream);

@@ -608,6 +608,15 @@ struct Fp8Kv {
   __device__ static void store_out(char* dst, f32x4_t o) { Bf16<D>::store_out(dst, o); }
 };
 
+// FP8 pages with 128-row row-split units, as Bf16Tall.  Their chunk weighs as much as a 64-row FP8
+// chunk (8; measured on MI355X, 4 x 2048-token windows + 128 decodes, 32/8 heads: weight 4 / 8 / 16
+// / 32 took 889 / 742 / 838 / 1398 us): widening K and V to bf16 costs the same for either height.
+template <int D_>
+struct Fp8KvTall : Fp8Kv<D_> {
+  static constexpr int kRowTiles = 2;
+  static constexpr int kRowGeom = row_geom(kCostRowSplitFp8, kRowTiles);
+};
+
 // ---------------------------------------------------------------------------
 // Per-lane online-softmax state for RT tiles of 16 query rows.
 // Lane (row n = lane%16, quad q) holds O^T[d = 16t + 4q + e][n] for every tile t.
@@ -2686,8 +2695,11 @@ int launch_attention_fused(const AttnArgs& a, int dtype, int D, int grid, void* 
   return D == 128 ? launch_fused_t<F32<128>>(a, grid, stream) : launch_fused_t<F32<64>>(a, grid, stream);
 }
 
-int launch_attention_fp8kv(const AttnArgs& a, int D, int grid, void* stream) {
-  if (D == 128)
+int launch_attention_fp8kv(const AttnArgs& a, int D, int grid, void* stream, bool tall) {
+  if (D == 128 && tall)
+    hipLaunchKernelGGL((attention_fused_kernel<Fp8KvTall<128>, false>), dim3(grid), dim3(kThreads), 0,
+                       as_stream(stream), a);
+  else if (D == 128)
     hipLaunchKernelGGL((attention_fused_kernel<Fp8Kv<128>, false>), dim3(grid), dim3(kThreads), 0,
                        as_stream(stream), a);
   else
@@ -2781,7 +2793,10 @@ int attention_blocks_per_cu(int dtype, int D) {
   if (dtype == PA_BF16) {
     const int a = D == 128 ? blocks_per_cu_t<Bf16<128>>() : blocks_per_cu_t<Bf16<64>>();
     const int b = D == 128 ? fp8_blocks_per_cu_t<Fp8Kv<128>>() : fp8_blocks_per_cu_t<Fp8Kv<64>>();
-    return a < 0 || b < 0 ? -1 : (a < b ? a : b);
+    const int c = D == 128 ? fp8_blocks_per_cu_t<Fp8KvTall<128>>() : b;
+    if (a < 0 || b < 0 || c < 0) return -1;
+    const int m = a < b ? a : b;
+    return m < c ? m : c;
   }
   return D == 128 ? blocks_per_cu_t<F32<128>>() : blocks_per_cu_t<F32<64>>();
 }

@@ -98,6 +98,20 @@ def test_fp8_full_config(c):
     check(w, out, lse)
 
 
+# T_q * Hq above 64 x 1024: the launch runs 128-row row blocks (two row tiles per wave)
+@pytest.mark.parametrize("case", [
+    ("g4", 84, [2500, 1700, 2048, 900], [2000, 1200, 2048, 900], 32, 8),
+    ("g8-mixed", 86, [6000, 9000] + [700 + 37 * i for i in range(40)] + [1200 + 91 * i for i in range(10)],
+     [6000, 3000] + [1] * 40 + [5] * 10, 8, 1),
+], ids=["g4", "g8-mixed"])
+def test_fp8_tall_row_blocks(case):
+    name, seed, n, q, hq, hkv = case
+    assert sum(q) * hq >= 64 * 1024
+    w = W.to_fp8(W.build(f"tall-{name}", seed, n, q, hq, hkv, 128, "bf16"))
+    out, lse = run_fp8(w)
+    check(w, out, lse)
+
+
 def test_fp8_nan_codes_in_unused_slots_change_nothing():
     w = W.to_fp8(W.make_random(116, 6, 400, 32, 8, 128, "bf16", max_q=3))
     o1, l1 = run_fp8(w)
