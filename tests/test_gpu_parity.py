@@ -214,6 +214,29 @@ def test_deterministic_and_staged_equals_one_shot():
     assert torch.equal(o1, out) and torch.equal(l1, lse)
 
 
+def test_repeated_launches_bitwise_equal_under_merge_contention():
+    """128 decode units of 1024 chunks on a grid of a few hundred grains: every unit is split, so
+    about a hundred merges complete concurrently in each launch, through arrival counters that every
+    launch re-zeroes.  Twenty launches back to back (no synchronization between them) must give
+    bitwise identical results, and the first must match the oracle."""
+    n = [32768 - 37 * i for i in range(16)]
+    w = W.build("merge-contention", 87, n, [1] * 16, 64, 8, 128, "bf16")
+    t = pa.to_device(w)
+    desc = pa.make_desc(t["q"], t["k_pool"], t["block_table"], t["seq_lens"], w.scale)
+    ws = pa.alloc_workspace(desc)
+    outs = []
+    for _ in range(20):
+        o = torch.empty_like(t["q"])
+        l = torch.empty(t["q"].shape[:2], dtype=torch.float32, device="cuda")
+        pa.attention(t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"], t["query_start_loc"],
+                     w.scale, out=o, lse=l, workspace=ws)
+        outs.append((o, l))
+    torch.cuda.synchronize()
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+    check(w, *outs[0])
+
+
 def test_staged_equals_one_shot_odd_group():
     """Row blocks that end mid-token (G = 7): the in-kernel plan and the staged planner agree bitwise."""
     w = W.make_random(15, 5, 700, 28, 4, 128, "bf16", max_q=200)
