@@ -224,7 +224,9 @@ pa_status pa_attention_shared_prefix(const pa_desc* desc, const void* q, const v
  * errors as pa_attention.  The grains are cut as in pa_plan's description
  * except that a chunk of a row-split unit weighs 8 instead of 4 (its K and V
  * are widened to bf16 on the way to the MFMAs, while a decode chunk moves half
- * the bytes), so that pa_plan does not describe this call's grains.
+ * the bytes), so that pa_plan does not describe this call's grains.  Row
+ * blocks follow pa_attention's rule (128 rows at head_dim 128 when T_q * Hq
+ * >= 64 * the launch's workgroups; a 128-row chunk also weighs 8).
  */
 pa_status pa_attention_fp8kv(const pa_desc* desc, const void* q, const uint8_t* k_pool, const uint8_t* v_pool,
                              const float* k_scale, const float* v_scale, const int32_t* block_table,
