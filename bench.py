@@ -341,7 +341,7 @@ def main() -> int:
                     help="workload (default 5: long-context decode, the largest that runs on one GPU)")
     ap.add_argument("--part", default="all", choices=["all", "prefill", "decode"],
                     help="configuration 3 only: time its prefill chunks or its decode rows alone")
-    ap.add_argument("--op", default="attention", choices=["attention", "append", "tree", "fp8", "prefix", "tile", "read"],
+    ap.add_argument("--op", default="attention", choices=["attention", "append", "tree", "fp8", "prefix", "tile", "tile-fp8", "read"],
                     help="attention (default): the attention call; append: the paged KV append of the batch's new "
                          "tokens (pa_append_kv); tree: attention with each window a random draft-token tree "
                          "(pa_attention_tree); fp8: attention over the batch's K/V quantized to FP8 E4M3 pages with "
@@ -349,7 +349,8 @@ def main() -> int:
                          "(pa_attention_shared_prefix) on the system-prompt decode batch (8 groups x 16 sequences, "
                          "4096-token shared prefix), --config ignored; tile: pa_attention on a long chunked prefill "
                          "(2 x 2048-token windows on 2048 tokens of context, 32/8 heads, head dim 128), the prefill "
-                         "tile's steady state, reported as MFMA TFLOP/s, --config ignored; read: the device's plain "
+                         "tile's steady state, reported as MFMA TFLOP/s, --config ignored; tile-fp8: the same tile over FP8 "
+                         "E4M3 pages (pa_attention_fp8kv); read: the device's plain "
                          "streaming-read rate (pa_read_stream over 8 GiB), the practical ceiling for the decode "
                          "paths, --config ignored")
     ap.add_argument("--staged", action="store_true",
@@ -371,7 +372,7 @@ def main() -> int:
 
     if args.record_traffic:
         from paged_kv_cache_gqa_amd import workloads as W
-        name = W.LONG_PREFILL_NAME if args.op == "tile" else \
+        name = W.LONG_PREFILL_NAME + ("-fp8kv" if args.op == "tile-fp8" else "") if args.op.startswith("tile") else \
             W.CONFIG_NAMES[args.config] + ("" if args.part == "all" else f"-{args.part}-part") + \
             {"tree": "-tree", "fp8": "-fp8kv"}.get(args.op, "")
         kernel = "attention_kernel" if args.staged else "attention_fused_kernel"
@@ -390,7 +391,7 @@ def main() -> int:
         return bench_prefix(args)
     if args.op == "read":
         return bench_read(args)
-    tile = args.op == "tile"
+    tile = args.op in ("tile", "tile-fp8")
     w = W.make_long_prefill() if tile else W.make_config(args.config)
     if args.part != "all" and not tile:
         ql = w.q_lens()
@@ -399,7 +400,7 @@ def main() -> int:
         w.name = f"{W.CONFIG_NAMES[args.config]}-{args.part}-part"
     if args.op == "append":
         return bench_append(args, w)
-    if args.op == "fp8":
+    if args.op in ("fp8", "tile-fp8"):
         w = W.to_fp8(w)
     alg_bytes = w.algorithmic_bytes()
     alg_flops = w.algorithmic_flops()
@@ -425,7 +426,7 @@ def main() -> int:
     if tree:
         masks, _ = W.random_trees(w.q_lens(), 1000 + args.config)
         tm = torch.from_numpy(masks.view(np.int64)).cuda()
-    fp8 = args.op == "fp8"
+    fp8 = args.op in ("fp8", "tile-fp8")
     mask_arg = (vp(tm.data_ptr()),) if tree else ()
     scale_args = (vp(t["k_scale"].data_ptr()), vp(t["v_scale"].data_ptr())) if fp8 else ()
     attn_args = [(dref, vp(t["q"].data_ptr()), vp(k.data_ptr()), vp(v.data_ptr()), *scale_args,
@@ -530,7 +531,8 @@ def main() -> int:
     }
     if tile:  # an MFMA-bound workload: TFLOP/s against the dense bf16 peak
         k_tf = alg_flops / (attn_mean * 1e-3) / 1e12
-        line.update({"metric": "prefill tile MFMA TFLOP/s (bf16, % of dense peak), 1 MI355X",
+        line.update({"metric": ("prefill tile over FP8 pages, MFMA TFLOP/s (bf16 MFMAs, % of dense bf16 peak), "
+                               "1 MI355X" if fp8 else "prefill tile MFMA TFLOP/s (bf16, % of dense peak), 1 MI355X"),
                      "value": round(tflops, 2), "unit": "TFLOP/s"})
         line["roofline"].update({"bound": "mfma", "achieved": round(k_tf, 2), "peak": BF16_PEAK_TFLOPS,
                                  "unit": "TFLOP/s", "frac": round(k_tf / BF16_PEAK_TFLOPS, 4),
