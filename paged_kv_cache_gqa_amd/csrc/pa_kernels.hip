@@ -179,6 +179,20 @@ __device__ __forceinline__ void lds_read4_b32(const uint32_t (&a)[4], uint32_t& 
       : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
       : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
 }
+// Four 16-byte reads at a[i] + kOff (kOff an immediate byte offset below 64 KiB).
+template <int kOff>
+__device__ __forceinline__ void lds_read4_b128_at(const uint32_t (&a)[4], u32x4_t& r0, u32x4_t& r1, u32x4_t& r2,
+                                                  u32x4_t& r3) {
+  static_assert(kOff >= 0 && kOff < 65536, "ds offset field");
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%8\n"
+      "ds_read_b128 %1, %5 offset:%8\n"
+      "ds_read_b128 %2, %6 offset:%8\n"
+      "ds_read_b128 %3, %7 offset:%8\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(kOff));
+}
 // 16-byte LDS write that the compiler does not order behind DMAs in flight (the data it writes
 // does not overlap any DMA target; LDS operations of one wave execute in issue order).
 __device__ __forceinline__ void lds_write_b128(uint32_t a, u32x4_t v) {
@@ -312,8 +326,10 @@ struct Bf16 {
     return load_frag(nullptr, nullptr, v0, v1, 0u, vl, kKF + g);
   }
   __device__ static u32x4_t v_convert(const VRaw& r) { return r; }
-  __device__ static f32x4_t qk(const u32x4_t* kf, int h, const u32x4_t* qf) {
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  // acc0: the accumulators' start value (zero, or minus the rows' score offsets)
+  __device__ static f32x4_t qk(const u32x4_t* kf, int h, const u32x4_t* qf,
+                               f32x4_t acc0 = f32x4_t{0.f, 0.f, 0.f, 0.f}) {
+    f32x4_t acc = acc0;
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[h * (D / 32) + kk]), as_bf16x8(qf[kk]), acc, 0, 0, 0);
@@ -347,13 +363,22 @@ struct Bf16 {
   template <class RG>
   __device__ static void lds_read_k(const char* slot, int lane, u32x4_t (&kf)[kKF]) {
     const int m = lane & 15, quad = lane >> 4;
-    uint32_t a[kKF];
+    if constexpr (D == 128) {
+      // page 1's block sits kBlk bytes after page 0's: the same four addresses, an immediate offset
+      uint32_t a[4];
 #pragma unroll
-    for (int f = 0; f < kKF; ++f) {
-      const int h = f / (D / 32), kk = f % (D / 32);
-      a[f] = lds_addr(slot + h * RG::kBlk + m * RG::kPitchK + RG::swz_k(m, 4 * kk + quad) * 16);
+      for (int kk = 0; kk < 4; ++kk) a[kk] = lds_addr(slot + m * RG::kPitchK + RG::swz_k(m, 4 * kk + quad) * 16);
+      lds_read4_b128_at<0>(a, kf[0], kf[1], kf[2], kf[3]);
+      lds_read4_b128_at<RG::kBlk>(a, kf[4], kf[5], kf[6], kf[7]);
+    } else {
+      uint32_t a[kKF];
+#pragma unroll
+      for (int f = 0; f < kKF; ++f) {
+        const int h = f / (D / 32), kk = f % (D / 32);
+        a[f] = lds_addr(slot + h * RG::kBlk + m * RG::kPitchK + RG::swz_k(m, 4 * kk + quad) * 16);
+      }
+      lds_read_b128<kKF>(a, kf);
     }
-    lds_read_b128<kKF>(a, kf);
   }
   template <class RG>
   __device__ static void lds_read_v(const char* slot, int lane, u32x4_t (&vf)[kVF]) {
@@ -738,6 +763,30 @@ struct TreeMask {
   int win0;
 };
 
+// Masked keys of one row tile's 8 scores of a chunk (key0: the chunk's first key) set to -inf:
+// keys past the row's position p_row, and with kTree window keys whose bit is clear in the row's
+// tree mask.
+template <int RT, bool kTree>
+__device__ __forceinline__ void mask_scores(float (&x)[8], int p_row, int key0, const TreeMask<RT>& tm, int rt,
+                                            int quad) {
+  const int lim = p_row - key0;  // element j visible iff its key <= lim
+  // tree rows: a window key k (>= 0) is visible only where bit k of the row's mask is set.
+  // Written branch-free (bitwise & | on the conditions, the bit index clamped to 0..63): a
+  // short-circuit form compiled to divergent branches that lost the score of visible keys.
+  const uint32_t m_lo = uint32_t(tm.m[rt]), m_hi = uint32_t(tm.m[rt] >> 32);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    bool vis = p_key(j, quad) <= lim;
+    if constexpr (kTree) {
+      const int k = key0 + p_key(j, quad) - tm.win0;  // window token index of the key
+      const uint32_t kc = uint32_t(min(max(k, 0), 63));
+      const uint32_t bit = ((kc < 32 ? m_lo : m_hi) >> (kc & 31)) & 1u;
+      vis = vis & ((k < 0) | (bit != 0u));
+    }
+    x[j] = vis ? x[j] : -INFINITY;
+  }
+}
+
 // Softmax of NC chunks in two phases.
 //
 // Phase 1 (softmax_prep): the raw scores s[j] (QK^T results of chunk j; half h holds the keys of
@@ -771,24 +820,7 @@ __device__ __forceinline__ void softmax_prep(State<TR, RT>& st, const f32x4_t (&
           x[c][rt][4 + e] *= cs[c].k1;
         }
       }
-      if (mask[c]) {
-        const int lim = p_row[rt] - key0[c];  // element j visible iff its key <= lim
-        // tree rows: a window key k (>= 0) is visible only where bit k of the row's mask is set.
-        // Written branch-free (bitwise & | on the conditions, the bit index clamped to 0..63): a
-        // short-circuit form compiled to divergent branches that lost the score of visible keys.
-        const uint32_t m_lo = uint32_t(tm.m[rt]), m_hi = uint32_t(tm.m[rt] >> 32);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          bool vis = p_key(j, quad) <= lim;
-          if constexpr (kTree) {
-            const int k = key0[c] + p_key(j, quad) - tm.win0;  // window token index of the key
-            const uint32_t kc = uint32_t(min(max(k, 0), 63));
-            const uint32_t bit = ((kc < 32 ? m_lo : m_hi) >> (kc & 31)) & 1u;
-            vis = vis & ((k < 0) | (bit != 0u));
-          }
-          x[c][rt][j] = vis ? x[c][rt][j] : -INFINITY;
-        }
-      }
+      if (mask[c]) mask_scores<RT, kTree>(x[c][rt], p_row[rt], key0[c], tm, rt, quad);
       const float cm = max3(max3(x[c][rt][0], x[c][rt][1], x[c][rt][2]), max3(x[c][rt][3], x[c][rt][4], x[c][rt][5]),
                             max2(x[c][rt][6], x[c][rt][7]));
       lm[rt] = c == 0 ? cm : max2(lm[rt], cm);
@@ -841,6 +873,101 @@ __device__ __forceinline__ void softmax_exp(State<TR, RT>& st, const float (&x)[
       } else {
         pf[c][rt] = TR::make_p(p);
       }
+    }
+    st.l[rt] += sum;
+  }
+}
+
+// The same softmax with each row's running maximum folded into the QK products (bf16 row-split
+// units).  A row keeps its offset o in raw score units (q.k, before the factor sl2): the QK
+// accumulation starts from -o, so the MFMA results are q.k - o, and the row's running maximum in
+// the base-2 domain is m = o * sl2 (o = 0 and m = -inf before the row's first visible key).  The
+// lazy-rescale test then compares the MFMA results with a per-row threshold in raw units
+// (kLazy / sl2, or -inf while m is -inf) without arithmetic on them, and P = 2^((q.k - o) * sl2).
+// Where m moves, the chunk's results are re-based by the offset's change; that is the rare path.
+template <int RT>
+struct ScoreBase {
+  f32x4_t neg[RT];  // -o in all four elements: the QK accumulators' start value
+  float thr[RT];    // a result above this moves the row's maximum
+};
+
+template <int RT>
+__device__ __forceinline__ void score_base_init(ScoreBase<RT>& sb) {
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    sb.neg[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    sb.thr[rt] = -INFINITY;
+  }
+}
+
+// thr_lazy: kLazy / sl2, the raw-unit threshold once a row has a finite maximum
+template <class TR, int RT, int NC, bool kTree>
+__device__ __forceinline__ void softmax_prep_based(State<TR, RT>& st, ScoreBase<RT>& sb,
+                                                   const f32x4_t (&s)[NC][RT][2], const int (&key0)[NC],
+                                                   const int (&p_row)[RT], const TreeMask<RT>& tm,
+                                                   const bool (&mask)[NC], float sl2, float thr_lazy, int lane,
+                                                   float (&x)[NC][RT][8]) {
+  const int quad = lane >> 4;
+  bool over = false;
+  float lm[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[c][rt][e] = s[c][rt][0][e];
+        x[c][rt][4 + e] = s[c][rt][1][e];
+      }
+      if (mask[c]) mask_scores<RT, kTree>(x[c][rt], p_row[rt], key0[c], tm, rt, quad);
+      const float cm = max3(max3(x[c][rt][0], x[c][rt][1], x[c][rt][2]), max3(x[c][rt][3], x[c][rt][4], x[c][rt][5]),
+                            max2(x[c][rt][6], x[c][rt][7]));
+      lm[rt] = c == 0 ? cm : max2(lm[rt], cm);
+    }
+    over |= lm[rt] > sb.thr[rt];  // -inf never passes
+  }
+  if (__any(over)) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float mx = quad_max(lm[rt]);  // the row's largest result against its offset
+      if (__any(mx > sb.thr[rt])) {
+        const float o = -sb.neg[rt][0];
+        // the new offset: the row's largest raw score where that exceeds the old maximum
+        const bool moves = mx > 0.f || st.m[rt] == -INFINITY;
+        const float o_new = mx == -INFINITY ? o : (moves ? mx + o : o);
+        const float m_new = mx == -INFINITY && st.m[rt] == -INFINITY ? -INFINITY : o_new * sl2;
+        const float alpha = fast_exp2(st.m[rt] - (m_new == -INFINITY ? 0.f : m_new));
+        st.l[rt] *= alpha;
+#pragma unroll
+        for (int t = 0; t < TR::kTiles; ++t) st.o[rt][t] *= alpha;
+        st.m[rt] = m_new;
+        const float d = o - o_new;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[c][rt][j] += d;
+        sb.neg[rt] = f32x4_t{-o_new, -o_new, -o_new, -o_new};
+        sb.thr[rt] = m_new == -INFINITY ? -INFINITY : thr_lazy;
+      }
+    }
+  }
+}
+
+template <class TR, int RT, int NC>
+__device__ __forceinline__ void softmax_exp_based(State<TR, RT>& st, const float (&x)[NC][RT][8], float sl2,
+                                                  typename TR::PFrag (&pf)[NC][RT]) {
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    float sum;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) p[j] = fast_exp2(x[c][rt][j] * sl2);
+      // a pairwise sum of the chunk's 8 values (no add of a zero start value)
+      const float cs = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      sum = c == 0 ? cs : sum + cs;
+      pf[c][rt] = TR::make_p(p);
     }
     st.l[rt] += sum;
   }
@@ -1284,6 +1411,11 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, const Seq
   };
   State<TR, RT> st;
   state_init(st);
+  // bf16 pages: the running maxima folded into the QK products
+  constexpr bool kBased = TR::kBf16 && !TR::kScaled;
+  ScoreBase<RT> sb;
+  score_base_init(sb);
+  const float thr_lazy = kLazy / A.scale_log2;
 
   // Wave w copies the (page, kv head) block of K page 0, K page 1, V page 0 or V page 1 (w = 0..3):
   // its pool and head offset are fixed for the unit, the page changes per chunk.  Lane `lane` of DMA
@@ -1345,15 +1477,28 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, const Seq
         const int cj = real ? c + j : c;
         u32x4_t kf[TR::kKF];
         TR::template lds_read_k<RG>(slot_of_chunk(cj), lane, kf);
-        qk_chunk<TR, RT>(getq, kf, sc[j]);
+        if constexpr (kBased) {
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            sc[j][rt][0] = TR::qk(kf, 0, qreg[rt], sb.neg[rt]);
+            sc[j][rt][1] = TR::qk(kf, 1, qreg[rt], sb.neg[rt]);
+          }
+        } else {
+          qk_chunk<TR, RT>(getq, kf, sc[j]);
+        }
         key0[j] = real ? cj * kChunkKeys : (1 << 29);
         msk[j] = !real || cj * kChunkKeys + kChunkKeys - 1 >= mask_from;
         cs[j] = read_scales<TR>(scl[j]);
       }
       float x[NP][RT][8];
-      softmax_prep<TR, RT, NP, kTree>(st, sc, key0, p_row, tm, cs, msk, A.scale_log2, lane, x);
       typename TR::PFrag pf[NP][RT];
-      softmax_exp<TR, RT, NP>(st, x, cs, A.scale_log2, pf);
+      if constexpr (kBased) {
+        softmax_prep_based<TR, RT, NP, kTree>(st, sb, sc, key0, p_row, tm, msk, A.scale_log2, thr_lazy, lane, x);
+        softmax_exp_based<TR, RT, NP>(st, x, A.scale_log2, pf);
+      } else {
+        softmax_prep<TR, RT, NP, kTree>(st, sc, key0, p_row, tm, cs, msk, A.scale_log2, lane, x);
+        softmax_exp<TR, RT, NP>(st, x, cs, A.scale_log2, pf);
+      }
       // V after the scores, so that K and V fragments of the step are not live together
       u32x4_t vf[NP][TR::kVF];
 #pragma unroll
