@@ -289,26 +289,32 @@ def bench_prefix(args) -> int:
 
 
 def bench_read(args) -> int:
-    """The device's plain streaming-read rate (pa_read_stream over an 8 GiB buffer): the practical
-    ceiling that the memory-bound attention paths are measured against, beside the 8 TB/s peak."""
+    """The device's plain streaming-read rate (pa_read_stream over an 8 GiB buffer, or --read-bytes):
+    the practical ceiling that the memory-bound attention paths are measured against, beside the
+    8 TB/s peak; at a configuration's byte count, what a plain read of that many bytes takes."""
     import torch
 
     import paged_kv_cache_gqa_amd as pa
 
-    nbytes = 8 << 30
+    quantum = 16 * 4096  # pa_read_stream reads a multiple of 16 bytes per workgroup
+    nbytes = -(-args.read_bytes // quantum) * quantum
+    # below 2 GiB, passes rotate over several buffers (2 GiB in all), so that no pass is served from
+    # the previous one's lines in the 256 MB memory-attached last-level cache
+    n_buf = max(1, -(-(2 << 30) // nbytes))
     g = torch.Generator(device="cuda").manual_seed(1008)
-    buf = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda", generator=g)
+    bufs = [torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda", generator=g)
+            for _ in range(n_buf)]
     stream = torch.cuda.current_stream()
     rates = {}
     for grid in (256, 512, 1024, 2048, 4096):
         sink = torch.empty((grid,), dtype=torch.int32, device="cuda")
-        for _ in range(max(1, args.warmup // 4)):
-            pa.read_stream(buf, grid, sink)
+        for i in range(max(n_buf, args.warmup // 4)):
+            pa.read_stream(bufs[i % n_buf], grid, sink)
         torch.cuda.synchronize()
         ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
         ev[0].record(stream)
-        for _ in range(args.steps):
-            pa.read_stream(buf, grid, sink)
+        for i in range(args.steps):
+            pa.read_stream(bufs[i % n_buf], grid, sink)
         ev[1].record(stream)
         torch.cuda.synchronize()
         ms = ev[0].elapsed_time(ev[1]) / args.steps
@@ -320,8 +326,8 @@ def bench_read(args) -> int:
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "u32", "data": "synthetic (seeded random words)",
-        "config": {"workload": "one pass over an 8 GiB device buffer, 16-byte loads, one contiguous slice per "
-                               "workgroup of 256 threads", "bytes": nbytes, "grid": best},
+        "config": {"workload": f"one pass over a {nbytes}-byte device buffer ({n_buf} rotated), 16-byte loads, "
+                               "one contiguous slice per workgroup of 256 threads", "bytes": nbytes, "grid": best},
         "by_grid_gbs": {str(k): round(v[0], 1) for k, v in rates.items()},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 5), "traffic": None, "kernel": "pa::read_stream_kernel",
@@ -337,6 +343,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--read-bytes", type=int, default=8 << 30,
+                    help="--op read only: bytes per pass (rounded up to 64 KiB; default 8 GiB)")
     ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5],
                     help="workload (default 5: long-context decode, the largest that runs on one GPU)")
     ap.add_argument("--part", default="all", choices=["all", "prefill", "decode"],
