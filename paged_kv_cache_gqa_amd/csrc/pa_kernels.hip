@@ -1477,6 +1477,9 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, const Seq
         const int cj = real ? c + j : c;
         u32x4_t kf[TR::kKF];
         TR::template lds_read_k<RG>(slot_of_chunk(cj), lane, kf);
+        // matrix work at a raised wave priority: of the two waves sharing a SIMD, the one ready to
+        // issue MFMAs goes first while the other runs its softmax (tile 1-3% faster on three boxes)
+        __builtin_amdgcn_s_setprio(1);
         if constexpr (kBased) {
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) {
@@ -1486,6 +1489,7 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, const Seq
         } else {
           qk_chunk<TR, RT>(getq, kf, sc[j]);
         }
+        __builtin_amdgcn_s_setprio(0);
         key0[j] = real ? cj * kChunkKeys : (1 << 29);
         msk[j] = !real || cj * kChunkKeys + kChunkKeys - 1 >= mask_from;
         cs[j] = read_scales<TR>(scl[j]);
@@ -1514,12 +1518,14 @@ __device__ void run_rowsplit(const AttnArgs& A, const pa_plan_unit& U, const Seq
       }
       // tile by tile, the step's chunks back to back into one accumulator (chunk by chunk, the
       // compiler wrote the second chunk's results beside the accumulators and copied them back)
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int t = 0; t < TR::kTiles; ++t)
 #pragma unroll
           for (int j = 0; j < NP; ++j) st.o[rt][t] = TR::pv(vf[j], t, pf[j][rt], st.o[rt][t]);
+      __builtin_amdgcn_s_setprio(0);
     } else {
 #pragma unroll
       for (int j = 0; j < NP; ++j) nx[j] = page_ids_load(bt_row, min(c + 2 * NP + j, i1 - 1), n_seq);
