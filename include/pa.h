@@ -94,7 +94,9 @@ typedef struct pa_desc {
                                 depends on it: the single launch derives its work list on the
                                 device from seq_lens.  pa_validate reports a longer sequence. */
   int32_t dtype;             /* pa_dtype of q, k_pool, v_pool and out */
-  float scale;               /* multiplies q.k before the softmax */
+  float scale;               /* multiplies q.k before the softmax; any finite value.  0, and
+                                magnitudes whose |scale| * log2(e) is below FLT_MIN, give every
+                                score exactly 0 (uniform weights over the visible keys) */
 } pa_desc;
 
 /* PA_ABI_VERSION of the loaded library. */

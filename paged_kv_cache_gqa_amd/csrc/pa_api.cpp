@@ -2,6 +2,7 @@
 // checks, workspace sizing, and the launches of the gfx950 kernels.
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
 #include <cmath>
 #include <cstring>
 #include <atomic>
@@ -164,9 +165,13 @@ AttnArgs single_launch_args(const pa_desc& d, const void* q, const void* k, cons
   // Scores are taken in the base-2 domain with the positive factor |scale| * log2(e); a negative
   // scale flips Q's sign bits instead.  scale == 0 makes every score 0: Q is cleared (q_keep = 0)
   // and the factor set to 1, so that masked keys (-inf) never meet a zero factor (-inf * 0 = NaN).
-  a.scale_log2 = d.scale == 0.f ? 1.f : std::fabs(d.scale) * 1.44269504088896340736f;
-  a.q_sign = d.scale < 0.f ? (d.dtype == PA_BF16 ? 0x80008000u : 0x80000000u) : 0u;
-  a.q_keep = d.scale == 0.f ? 0u : 0xFFFFFFFFu;
+  // A factor below the smallest normal float counts as 0: the kernels' fp32 arithmetic flushes it
+  // to zero, and scores that small are 0 to fp32 precision anyway (their exponentials round to 1).
+  const float f = std::fabs(d.scale) * 1.44269504088896340736f;
+  const bool zero = !(f >= FLT_MIN);
+  a.scale_log2 = zero ? 1.f : f;
+  a.q_sign = !zero && d.scale < 0.f ? (d.dtype == PA_BF16 ? 0x80008000u : 0x80000000u) : 0u;
+  a.q_keep = zero ? 0u : 0xFFFFFFFFu;
   return a;
 }
 

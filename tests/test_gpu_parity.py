@@ -564,15 +564,17 @@ def test_rising_scores_move_the_maximum_every_chunk(case):
     check(w, out, lse, ref=(ref_o, ref_l), tol=tol)
 
 
-def test_zero_scale_gives_uniform_weights():
+@pytest.mark.parametrize("scale", [0.0, 1e-39, -3e-40])
+def test_zero_scale_gives_uniform_weights(scale):
     """scale = 0: every score is 0, so each row returns the mean of its visible V rows and
     lse = ln(visible keys).  Rows with masked keys in their last chunk (n = 17, ...) must not pick up
-    a NaN from a masked key meeting the zero factor."""
+    a NaN from a masked key meeting the zero factor.  Subnormal scales (whose base-2 factor fp32
+    flushes to zero) give the same to fp32 precision."""
     n = [17, 1, 300, 45, 64]
     q = [1, 1, 40, 3, 64]
     for dt, D in (("bf16", 128), ("f32", 64)):
         import oracle_pins as P
-        w = P._replace(W.build(f"scale0-{dt}", 72, n, q, 8, 2, D, dt, num_pages=40), scale=0.0)
+        w = P._replace(W.build(f"scale0-{dt}", 72, n, q, 8, 2, D, dt, num_pages=40), scale=scale)
         out, lse = run_gpu(w)
         check(w, out, lse)
         ql = w.q_lens()
