@@ -1157,18 +1157,33 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, ch
 }
 
 // s_waitcnt vmcnt(0) lgkmcnt(0): every load of this wave has landed.
-__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x0070); }
+// A compiler barrier for memory operations: loads, stores and DMAs are issued in program order
+// across it.  The waits below count instructions in flight, so wherever they stand for a
+// particular load having landed, the order of issue they count on is fixed with these.
+__device__ __forceinline__ void issue_order() { asm volatile("" ::: "memory"); }
+
+__device__ __forceinline__ void wait_all_loads() {
+  issue_order();
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  issue_order();
+}
 
 // s_waitcnt vmcnt(N), leaving LDS / scalar loads (lgkmcnt) and expcnt unwaited.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
+  issue_order();
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+  issue_order();
 }
 
 // s_waitcnt lgkmcnt(0): this wave's LDS accesses written as inline asm are done; global loads and
 // DMAs in flight are not waited for.
-__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+__device__ __forceinline__ void wait_lds() {
+  issue_order();
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  issue_order();
+}
 
 // Workgroup barrier that orders LDS accesses for the compiler without waiting on global memory.
 __device__ __forceinline__ void lds_barrier() {
@@ -1253,6 +1268,7 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, const Seq
   float scl_cur = load_scale_lane<TR>(A, U.kv_head, cp_ids, lane);
   if constexpr (kKviaLds) dma_k(kslot, cp);
   else load_k<TR>(cp, kl, vl, kf);
+  issue_order();  // V after the K DMA: the loop's first wait for it counts on that order
   load_v<TR>(cp, vl, vr);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
@@ -2154,6 +2170,7 @@ __device__ void run_keysplit_stream(const AttnArgs& A, UnitCursor& cu, Piece p, 
     if (!pre) {
       const ChunkPages cp = pages_of<TR>(A, U.kv_head, page_ids(bt_row, c < p.i1 ? c : p.i0, n_seq));
       dma_k(cp);
+      issue_order();  // V after the K DMA: the loop's first wait for it counts on that order
       load_v<TR>(cp, vl, vr);
     }
 #pragma unroll
@@ -2172,6 +2189,7 @@ __device__ void run_keysplit_stream(const AttnArgs& A, UnitCursor& cu, Piece p, 
       wait_all_loads();
       const ChunkPages cp = pages_of<TR>(A, nkvh, nid);
       dma_k(cp);
+      issue_order();
       load_v<TR>(cp, vl, vr);
     }
     PageIds nx = page_ids(bt_row, min(c + kWaves, p.i1 - 1), n_seq);
