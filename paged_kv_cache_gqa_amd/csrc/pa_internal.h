@@ -70,9 +70,14 @@ inline __host__ __device__ int unit_start_cost(bool key_split, int rows) {
 // 128-row unit leaves 64 KiB of partial state to merge).  Grain boundaries --
 // and so every split of a unit's keys and its partial-result slots -- depend
 // only on the batch shape and the grid.
+// No grain is shorter than a row-split chunk's weight rw (>= kCostKeySplit): S <= (Ck + Cr) / rw.
+// A shorter grain could lie between two chunk starts of a unit and so hold an empty piece of it,
+// which never arrives at the unit's merge (with rw = 8, FP8 pages or 128-row blocks, the first
+// term alone allows grains of ~4 in small batches of mostly decode work).
 constexpr int kRowGrainChunks = 8;
 inline __host__ __device__ int64_t grain_count(int64_t ck, int64_t cr, int grid, int rw = kCostRowSplit) {
   int64_t s = ck / kCostKeySplit + cr / (int64_t(kRowGrainChunks) * rw);
+  if (cr > 0 && s > (ck + cr) / rw) s = (ck + cr) / rw;
   if (s > grid) s = grid;
   if (s < 1 && ck + cr > 0) s = 1;
   return s;

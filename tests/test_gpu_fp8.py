@@ -112,6 +112,19 @@ def test_fp8_tall_row_blocks(case):
     check(w, out, lse)
 
 
+def test_fp8_single_head_mixed_batch_small_grains():
+    """One query head on one kv head (G = 1): 64-row units of 45-60 window tokens among key-split
+    windows of 8-32 tokens.  So little work that, by the decode term of the grain count, grains
+    would be shorter than one FP8 row-split chunk (weight 8); such a grain held an empty piece of a
+    64-row unit that never arrived at its merge, and those rows came out unmerged."""
+    import oracle_pins as P
+    w = W.to_fp8(P._replace(W.make_random(245, 11, 3000, 1, 1, 128, "bf16", max_q=64), scale=128 ** -0.5))
+    assert (w.q_lens() > 32).sum() >= 3 and (w.q_lens() <= 32).sum() >= 6
+    for _ in range(2):  # twice: a unit left unmerged also leaves its arrival counter set
+        out, lse = run_fp8(w)
+        check(w, out, lse)
+
+
 def test_fp8_nan_codes_in_unused_slots_change_nothing():
     w = W.to_fp8(W.make_random(116, 6, 400, 32, 8, 128, "bf16", max_q=3))
     o1, l1 = run_fp8(w)
