@@ -561,7 +561,6 @@ struct Fp8Kv {
   static constexpr int kNF = kKF + kVF;
   static constexpr int kTiles = D / 16;
   static constexpr bool kBf16 = true;
-  static constexpr int kVLoads = 2 * kVF;
   static constexpr bool kScaled = true;
   static constexpr int kRowTiles = 1;
   static constexpr int kRowGeom = row_geom(kCostRowSplitFp8, kRowTiles);
@@ -570,9 +569,6 @@ struct Fp8Kv {
   __device__ static int q_off(int f, int quad) { return (32 * f + 8 * quad) * kEb; }
   __device__ static uint32_t k_lane(int lane) { return uint32_t((lane & 15) * D + 8 * (lane >> 4)); }
   __device__ static uint32_t v_lane(int lane) { return uint32_t((lane & 15) * kPage + 4 * (lane >> 4)); }
-  __device__ static VRaw load_v_raw(const char* v0, const char* v1, uint32_t vl, int t) {
-    return VRaw{ld4(v0 + vl + t * 16 * kPage), ld4(v1 + vl + t * 16 * kPage)};
-  }
   __device__ static u32x4_t v_convert(const VRaw& r) {
     const uint2 a = fp8x4_to_bf16x4(r[0]), b = fp8x4_to_bf16x4(r[1]);
     return u32x4_t{a.x, a.y, b.x, b.y};
@@ -1239,14 +1235,18 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, const Seq
   // global->LDS DMA into this wave's 2-page slot (contiguous 1 KiB per instruction; K fragments
   // read directly from the pool touch 16 rows x 64 B per instruction, which streams ~10% slower
   // at this occupancy) and V goes straight to registers (512 contiguous bytes per instruction).
+  // FP8 pages move K and V by DMA into a 4-page slot: read straight from the pool, a V fragment
+  // is 4 bytes per lane (16 instructions of 256 B per chunk against 4 DMA instructions of 1 KiB).
   // Every load is issued unconditionally: past the wave's last chunk it re-reads the chunk it has
   // (an L2 hit), so the number of loads in flight is the same on every path and the waits --
   // the compiler's for V, the explicit one for the K DMA -- are exact.
   using RG = Ring<TR>;
   constexpr bool kKviaLds = TR::kBf16;  // fp32 pages: K fragments straight to registers
+  constexpr bool kVviaLds = TR::kScaled;  // FP8 pages: V by DMA too
+  constexpr int kSlotBlocks = kVviaLds ? 4 : 2;  // (page, head) blocks of a wave's slot
   constexpr int kQRegion = kWaves * 2 * TR::kQF * 64;  // u32x4 slots of the Q slices (2 row tiles)
-  static_assert(!kKviaLds || (kQRegion * 16 + kWaves * 2 * RG::kBlk <= Smem<TR>::kBytes), "LDS budget");
-  char* kslot = reinterpret_cast<char*>(sm.buf + kQRegion) + w * 2 * RG::kBlk;
+  static_assert(!kKviaLds || (kQRegion * 16 + kWaves * kSlotBlocks * RG::kBlk <= Smem<TR>::kBytes), "LDS budget");
+  char* kslot = reinterpret_cast<char*>(sm.buf + kQRegion) + w * kSlotBlocks * RG::kBlk;
   const uint32_t kl = TR::k_lane(lane), vl = TR::v_lane(lane);
   auto dma_k = [&](char* slot, const ChunkPages& cp) {
     constexpr int kPer = RG::kBlk / 1024;  // DMA instructions per page
@@ -1261,6 +1261,86 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, const Seq
   };
   const int c = i0 + w;
   u32x4_t kf[TR::kKF];
+  const int mine = i1 > c ? (i1 - c + kWaves - 1) / kWaves : 0;  // chunks of this wave
+  if constexpr (kVviaLds) {
+    // FP8 pages: the slot holds K page 0, K page 1, V page 0, V page 1 (V^T rows of 16 codes, no
+    // swizzle).  Each step waits for everything in flight (its chunk's scales, K and V), reads the
+    // K and V fragments, then issues the next chunk's scales, K and V: they land during the whole
+    // step's compute, with no count to keep.
+    auto dma_v = [&](const ChunkPages& cp) {
+      constexpr int kPer = RG::kBlk / 1024;
+      const __amdgpu_buffer_rsrc_t r0 = block_rsrc(cp.v0, RG::kBlk), r1 = block_rsrc(cp.v1, RG::kBlk);
+#pragma unroll
+      for (int i = 0; i < 2 * kPer; ++i) {
+        const int o = (i % kPer) * 1024 + 16 * lane;
+        const int r = o / RG::kPitchV, cc = (o % RG::kPitchV) / 16;
+        dma16(i < kPer ? r0 : r1, uint32_t(r * RG::kPitchV + RG::swz_v(r, cc) * 16),
+              kslot + (2 + i / kPer) * RG::kBlk + (i % kPer) * 1024);
+      }
+    };
+    // lane (m, quad), fragment t: the 4 codes of keys 4 quad .. 4 quad + 3 of both pages at d = 16 t + m
+    auto read_v_raw = [&](typename TR::VRaw (&vr)[TR::kVF]) {
+      const int m = lane & 15;
+#pragma unroll
+      for (int t0 = 0; t0 < TR::kVF; t0 += 2) {
+        uint32_t a[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int d = 16 * (t0 + i) + m;
+          a[2 * i] = lds_addr(kslot + 2 * RG::kBlk + d * RG::kPitchV + 4 * quad);
+          a[2 * i + 1] = lds_addr(kslot + 3 * RG::kBlk + d * RG::kPitchV + 4 * quad);
+        }
+        uint32_t x0, x1, x2, x3;
+        lds_read4_b32(a, x0, x1, x2, x3);
+        vr[t0] = typename TR::VRaw{x0, x1};
+        vr[t0 + 1] = typename TR::VRaw{x2, x3};
+      }
+    };
+    PageIds cp_ids = page_ids(bt_row, c < i1 ? c : i0, n_seq);
+    ChunkPages cp = pages_of<TR>(A, U.kv_head, cp_ids);
+    float scl_cur = load_scale_lane<TR>(A, U.kv_head, cp_ids, lane);
+    dma_k(kslot, cp);
+    dma_v(cp);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int f = 0; f < TR::kQF; ++f) lds_write_b128(lds_addr(qlds + (rt * TR::kQF + f) * 64 + lane), qtmp[rt][f]);
+    PageIds nx = page_ids(bt_row, min(c + kWaves, i1 - 1), n_seq);
+    auto getq_asm = [&](int rt, u32x4_t (&qf)[TR::kQF]) {
+      uint32_t a[TR::kQF];
+#pragma unroll
+      for (int f = 0; f < TR::kQF; ++f) a[f] = lds_addr(qlds + (rt * TR::kQF + f) * 64 + lane);
+      lds_read_b128<TR::kQF>(a, qf);
+    };
+    for (int j = 0; j < mine; ++j) {
+      const int cc = c + j * kWaves;
+      const int key0 = cc * kChunkKeys;
+      const int cn = cc + kWaves;
+      if (cn < i1) {
+        cp_ids = nx;
+        cp = pages_of<TR>(A, U.kv_head, nx);
+      }
+      wait_all_loads();  // this chunk's scales, K and V have landed (nothing else is in flight)
+      TR::template lds_read_k<RG>(kslot, lane, kf);
+      typename TR::VRaw vr[TR::kVF];
+      read_v_raw(vr);  // both reads complete in place before the slot is refilled
+      asm volatile("" ::: "memory");
+      const float scl_nxt = load_scale_lane<TR>(A, U.kv_head, cp_ids, lane);
+      dma_k(kslot, cp);
+      dma_v(cp);
+      typename TR::PFrag pf[RT];
+      softmax_chunk<TR, RT, kTree>(st, getq_asm, kf, key0, p_row, tm, read_scales<TR>(scl_cur),
+                                   key0 + kChunkKeys - 1 >= mask_from, A.scale_log2, lane, pf);
+      asm volatile("" ::: "memory");
+      scl_cur = scl_nxt;
+      nx = page_ids(bt_row, min(cn + kWaves, i1 - 1), n_seq);
+      u32x4_t vf[TR::kVF];
+#pragma unroll
+      for (int f = 0; f < TR::kVF; ++f) vf[f] = TR::v_convert(vr[f]);
+      if (key0 + kChunkKeys > n_seq) TR::sanitize_v(vf, quad, n_seq - key0);  // the sequence's last chunk
+      pv_chunk<TR, RT>(st, vf, pf);
+    }
+  } else {
   typename TR::VRaw vr[TR::kVF];
   PageIds cp_ids = page_ids(bt_row, c < i1 ? c : i0, n_seq);
   ChunkPages cp = pages_of<TR>(A, U.kv_head, cp_ids);
@@ -1280,7 +1360,6 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, const Seq
 
   // The loop body has a single path.  A step past the wave's last chunk is a dummy: all its keys
   // are masked and its V is zeroed, so it adds nothing.
-  const int mine = i1 > c ? (i1 - c + kWaves - 1) / kWaves : 0;  // chunks of this wave
   // Page ids are loaded one iteration before their DMA is issued, after the iteration's last LDS
   // read (those reads wait for every LDS and scalar load in flight).
   PageIds nx = page_ids(bt_row, min(c + kWaves, i1 - 1), n_seq);
@@ -1326,7 +1405,8 @@ __device__ void run_keysplit(const AttnArgs& A, const pa_plan_unit& U, const Seq
     pv_chunk<TR, RT>(st, vf, pf);
     load_v<TR>(cp, vl, vr);
   }
-  if constexpr (kKviaLds) wait_all_loads();  // the last (unused) K DMA has landed before LDS is reused
+  }
+  if constexpr (kKviaLds) wait_all_loads();  // the last (unused) DMA has landed before LDS is reused
   __syncthreads();  // every wave is done with its Q slice before the merge buffer overwrites it
 
   // merge the 4 waves' states through LDS
