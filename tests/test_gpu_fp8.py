@@ -59,6 +59,18 @@ def test_fp8_random(case):
     check(w, out, lse)
 
 
+def test_fp8_edge_lengths():
+    """Key-split units over FP8 pages at page and chunk boundaries: n = 1, 16, 17, 31, 32, 33, ... keys (units of
+    one chunk leave three of the four waves without one), zero-query sequences, verify windows of one and of two
+    row tiles (G = 4: 5 and 8 tokens), at head dims 64 and 128."""
+    n = [1, 16, 17, 31, 32, 33, 48, 5, 64, 97, 129, 8]
+    q = [1, 1, 0, 3, 8, 1, 0, 5, 1, 1, 4, 8]
+    for D in (64, 128):
+        w = W.to_fp8(W.build(f"edges-fp8-{D}", 43, n, q, 8, 2, D, "bf16", num_pages=50))
+        out, lse = run_fp8(w)
+        check(w, out, lse)
+
+
 MIXED = [
     # seed, prefill windows, decode sequences, Hq, Hkv, D
     (121, 3, 60, 8, 1, 128),
