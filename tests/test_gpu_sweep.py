@@ -1,0 +1,79 @@
+"""GPU parity sweep: seeded random batches of every kind the call accepts, against the fp64 oracle.
+
+Each case draws its own shape: page format (bf16, fp32 or FP8 E4M3 pages), head dim (64 or 128), KV heads
+(1, 2, 4 or 8) and GQA group (1, 2, 3, 4, 5 or 8), 1-40 sequences in shuffled order mixing decode steps
+(1 token), verify windows (2-8 tokens) and prefill windows (9-400 tokens) over prior contexts of 0-1500 keys,
+plus zero-query sequences.  Every case is also run twice and must be bitwise equal (the split points depend
+only on the batch shape).  Tolerances as everywhere: fp32 1e-5 max-abs; bf16 and FP8 pages 2e-2 max-abs and
+2e-3 mean-abs, for out and lse."""
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_cache_gqa_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU-only container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import paged_kv_cache_gqa_amd as pa  # noqa: E402
+
+FORMATS = ("bf16", "f32", "fp8")
+
+
+def sweep_case(seed: int):
+    """The seeded batch of one case (inputs only: no attention arithmetic)."""
+    rng = np.random.default_rng(9000 + seed)
+    fmt = FORMATS[seed % 3]
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 3, 4, 5, 8]))
+    b = int(rng.integers(1, 40, endpoint=True))
+    kind = rng.choice(["decode", "verify", "prefill", "none"], size=b, p=[0.5, 0.25, 0.15, 0.10])
+    max_prefill = 120 if fmt == "f32" else 400
+    q = np.array([{"decode": 1, "none": 0}.get(k, 0) if k in ("decode", "none") else
+                  int(rng.integers(2, 8, endpoint=True)) if k == "verify" else
+                  int(rng.integers(9, max_prefill, endpoint=True)) for k in kind], dtype=np.int64)
+    prior = rng.integers(0, 600 if fmt == "f32" else 1500, b, endpoint=True)
+    n = np.maximum(prior + q, 1)
+    w = W.build(f"sweep-{seed}-{fmt}-D{d}-{hkv}x{g}", 9000 + seed, n, q, hkv * g, hkv, d,
+                "f32" if fmt == "f32" else "bf16", rng=rng)
+    return (W.to_fp8(w) if fmt == "fp8" else w), fmt
+
+
+def run(w, fmt):
+    t = pa.to_device(w)
+    if fmt == "fp8":
+        out, lse = pa.attention_fp8kv(t["q"], t["k_pool"], t["v_pool"], t["k_scale"], t["v_scale"], t["block_table"],
+                                      t["seq_lens"], t["query_start_loc"], w.scale)
+    else:
+        out, lse = pa.attention(t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                                t["query_start_loc"], w.scale)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("seed", range(96))
+def test_random_batch_sweep(seed):
+    w, fmt = sweep_case(seed)
+    out, lse = run(w, fmt)
+    out2, lse2 = run(w, fmt)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2), f"{w.name}: not bitwise reproducible"
+    if fmt == "fp8":
+        ref_o, ref_l = oracle.attention_fp8(w.q, w.k_pool, w.v_pool, w.meta["k_scale"], w.meta["v_scale"],
+                                            w.block_table, w.seq_lens, w.query_start_loc, w.scale)
+    else:
+        ref_o, ref_l = oracle.attention_workload(w)
+    o, l = out.float().cpu().numpy(), lse.cpu().numpy()
+    eo, el = np.abs(o - ref_o), np.abs(l - ref_l)
+    msg = (f"{w.name} (B={w.num_seqs}, T_q={w.num_q_tokens}): max|dout|={eo.max() if eo.size else 0:.3e} "
+           f"mean={eo.mean() if eo.size else 0:.3e} max|dlse|={el.max() if el.size else 0:.3e}")
+    print(msg, flush=True)
+    assert np.isfinite(o).all() and np.isfinite(l).all(), msg
+    if eo.size:
+        if fmt == "f32":
+            assert eo.max() <= 1e-5 and el.max() <= 1e-5, msg
+        else:
+            assert eo.max() <= 2e-2 and el.max() <= 2e-2 and eo.mean() <= 2e-3 and el.mean() <= 2e-3, msg
