@@ -77,3 +77,75 @@ def test_random_batch_sweep(seed):
             assert eo.max() <= 1e-5 and el.max() <= 1e-5, msg
         else:
             assert eo.max() <= 2e-2 and el.max() <= 2e-2 and eo.mean() <= 2e-3 and el.mean() <= 2e-3, msg
+
+
+def tree_case(seed: int):
+    """A seeded batch of verify windows of 1-80 tokens (trees up to 64 tokens, longer windows causal) over
+    prior contexts of 0-3000 keys, with random draft trees; bf16 or fp32 pages."""
+    rng = np.random.default_rng(9500 + seed)
+    dt = "f32" if seed % 4 == 3 else "bf16"
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2, 8]))
+    g = int(rng.choice([1, 3, 4, 8]))
+    b = int(rng.integers(1, 24, endpoint=True))
+    q = rng.integers(1, 80 if rng.random() < 0.3 else 12, b, endpoint=True)
+    n = rng.integers(0, 800 if dt == "f32" else 3000, b, endpoint=True) + q
+    w = W.build(f"tree-sweep-{seed}-{dt}-D{d}-{hkv}x{g}", 9500 + seed, n, q, hkv * g, hkv, d, dt, rng=rng)
+    masks, _ = W.random_trees(w.q_lens(), 9500 + seed)
+    return w, masks
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_tree_sweep(seed):
+    w, masks = tree_case(seed)
+    t = pa.to_device(w)
+    tm = torch.from_numpy(np.ascontiguousarray(masks, dtype=np.uint64).view(np.int64)).cuda()
+    out, lse = pa.attention_tree(t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                                 t["query_start_loc"], tm, w.scale)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.attention_tree(w.q, w.k_pool, w.v_pool, w.block_table, w.seq_lens, w.query_start_loc,
+                                         masks, w.scale)
+    o, l = out.float().cpu().numpy(), lse.cpu().numpy()
+    eo, el = np.abs(o - ref_o), np.abs(l - ref_l)
+    msg = f"{w.name} (B={w.num_seqs}, T_q={w.num_q_tokens}): max|dout|={eo.max():.3e} mean={eo.mean():.3e} max|dlse|={el.max():.3e}"
+    print(msg, flush=True)
+    assert np.isfinite(o).all() and np.isfinite(l).all(), msg
+    mx, mean = (1e-5, 1.0) if w.dtype == "f32" else (2e-2, 2e-3)
+    assert eo.max() <= mx and el.max() <= mx and eo.mean() <= mean and el.mean() <= mean, msg
+
+
+def prefix_case(seed: int):
+    """A seeded shared-prefix batch: 1-6 groups of 1-8 sequences, prefixes of 0-2048 keys (multiples of 16),
+    private suffixes of 1-600 keys holding windows of up to 1, 6 or 120 tokens; bf16 or fp32 pages."""
+    rng = np.random.default_rng(9700 + seed)
+    dt = "f32" if seed % 4 == 3 else "bf16"
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2, 8]))
+    g = int(rng.choice([1, 4, 8]))
+    ng = int(rng.integers(1, 6, endpoint=True))
+    sizes = [int(x) for x in rng.integers(1, 8, ng, endpoint=True)]
+    plens = [16 * int(x) for x in rng.integers(0, 128, ng, endpoint=True)]
+    mq = int(rng.choice([1, 6, 120]))
+    return W.make_shared_prefix(9700 + seed, sizes, plens, 600, mq, hkv * g, hkv, d, dt,
+                                name=f"prefix-sweep-{seed}-{dt}-D{d}-{hkv}x{g}")
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shared_prefix_sweep(seed):
+    w = prefix_case(seed)
+    t = pa.to_device(w)
+    gs = torch.from_numpy(w.meta["group_start"].astype(np.int32)).cuda()
+    pl = torch.from_numpy(w.meta["prefix_len"].astype(np.int32)).cuda()
+    out, lse = pa.attention_shared_prefix(t["q"], t["k_pool"], t["v_pool"], t["block_table"], t["seq_lens"],
+                                          t["query_start_loc"], gs, pl, w.scale)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.attention_workload(w)  # the cascade is an exact rearrangement of plain attention
+    o, l = out.float().cpu().numpy(), lse.cpu().numpy()
+    eo, el = np.abs(o - ref_o), np.abs(l - ref_l)
+    msg = (f"{w.name} (groups {len(w.meta['prefix_len'])}, T_q={w.num_q_tokens}): "
+           f"max|dout|={eo.max() if eo.size else 0:.3e} mean={eo.mean() if eo.size else 0:.3e}")
+    print(msg, flush=True)
+    assert np.isfinite(o).all() and np.isfinite(l).all(), msg
+    if eo.size:
+        mx, mean = (1e-5, 1.0) if w.dtype == "f32" else (2e-2, 2e-3)
+        assert eo.max() <= mx and el.max() <= mx and eo.mean() <= mean and el.mean() <= mean, msg
