@@ -198,11 +198,11 @@ pa_status pa_attention_noalloc(const pa_desc* desc, const void* q, const void* k
  * prefix) and the same first prefix_len[g] / 16 block-table entries; breaking
  * these is undefined behaviour.  The shared pages are read once per group and
  * KV head (all the group's query rows form MFMA tiles over them), each
- * sequence's remaining keys once; the two partial results are merged by
- * log-sum-exp.  group_start [num_groups+1] and prefix_len [num_groups] are
+ * sequence's remaining keys once; the second pass folds the first pass's
+ * result for each row into its output by log-sum-exp.  group_start [num_groups+1] and prefix_len [num_groups] are
  * int32 device arrays.  Workspace: pa_shared_prefix_workspace_size bytes,
  * 256-byte aligned, zero arrival counters as for pa_attention (it begins with
- * the pa_attention workspace).  Enqueues four kernels; 1 <= num_groups <= B.
+ * the pa_attention workspace).  Enqueues three kernels; 1 <= num_groups <= B.
  */
 pa_status pa_shared_prefix_workspace_size(const pa_desc* desc, int32_t num_groups, size_t* bytes);
 pa_status pa_attention_shared_prefix(const pa_desc* desc, const void* q, const void* k_pool, const void* v_pool,

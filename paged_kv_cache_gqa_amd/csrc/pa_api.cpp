@@ -159,6 +159,8 @@ AttnArgs single_launch_args(const pa_desc& d, const void* q, const void* k, cons
   a.v_scale = nullptr;
   a.key_base = nullptr;
   a.out_f32 = nullptr;
+  a.prior_o = nullptr;
+  a.prior_lse = nullptr;
   a.arrive = arrive;
   a.num_q_heads = d.num_q_heads;
   a.max_pages = d.max_pages_per_seq;
@@ -398,14 +400,13 @@ pa_status pa_attention_shared_prefix(const pa_desc* desc, const void* q, const v
   a.out_f32 = pw.part_o;
   if (pa::launch_attention_fused(a, desc->dtype, desc->head_dim, grid, stream, pa::tall_blocks(dp, grid)) != 0)
     return PA_ERR_HIP;
-  // suffix pass: every sequence from the end of its prefix on, causal as usual
-  pa::AttnArgs b = attn_args(*desc, q, k_pool, v_pool, block_table, pw.suf_seq_lens, qsl, out, pw.part_lse + rows, ws);
+  // suffix pass: every sequence from the end of its prefix on, causal as usual; each row's final
+  // output folds in the prefix pass's result for it (log-sum-exp weights), so no merge launch follows
+  pa::AttnArgs b = attn_args(*desc, q, k_pool, v_pool, block_table, pw.suf_seq_lens, qsl, out, lse, ws);
   b.key_base = pw.key_base;
-  b.out_f32 = pw.part_o + rows * desc->head_dim;
-  if (pa::launch_attention_fused(b, desc->dtype, desc->head_dim, grid, stream, pa::tall_blocks(*desc, grid)) != 0)
-    return PA_ERR_HIP;
-  // log-sum-exp merge of the two passes into out / lse
-  return pa::launch_merge(2, rows, desc->head_dim, pw.part_o, pw.part_lse, desc->dtype, out, lse, stream) == 0
+  b.prior_o = pw.part_o;
+  b.prior_lse = pw.part_lse;
+  return pa::launch_attention_fused(b, desc->dtype, desc->head_dim, grid, stream, pa::tall_blocks(*desc, grid)) == 0
              ? PA_OK
              : PA_ERR_HIP;
 }

@@ -123,6 +123,8 @@ struct AttnArgs {
   const int32_t* key_base;    // [B] or null: sequence s's keys start at key key_base[s] (a multiple of 16)
                               // of its block-table row; seq_lens then count keys from there
   float* out_f32;             // [T_q][Hq][D] or null: final results go here in fp32 instead of to out
+  const float* prior_o;       // [T_q][Hq][D] and [T_q][Hq] fp32, read by kernels of a trait with kPrior only:
+  const float* prior_lse;     // each row's result over other keys, folded into its final output (log-sum-exp)
   int32_t* arrive;  // [grains]: pieces of the split unit whose first piece is in grain k that have
                     // finished (single-launch path; zero between calls)
   int32_t num_q_heads;

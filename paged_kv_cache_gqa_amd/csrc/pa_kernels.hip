@@ -304,6 +304,7 @@ struct Bf16 {
   static constexpr int kVLoads = 2 * kVF;  // global load instructions per chunk of V (two pages per tile)
   static constexpr int kEbKV = kEb;        // bytes per K/V pool element
   static constexpr bool kScaled = false;   // per-(page, head) K/V scales
+  static constexpr bool kPrior = false;  // final outputs fold in a result over other keys (WithPrior)
   static constexpr int kRowTiles = 1;  // 16-row tiles of each wave in a row-split unit
   static constexpr int kRowGeom = row_geom(kCostRowSplit, kRowTiles);  // the planner's row-split geometry
   using VRaw = u32x4_t;                    // a V fragment as loaded
@@ -452,6 +453,7 @@ struct F32 {
   static constexpr int kVLoads = kVF;
   static constexpr int kEbKV = kEb;
   static constexpr bool kScaled = false;
+  static constexpr bool kPrior = false;
   static constexpr int kRowTiles = 1;
   static constexpr int kRowGeom = row_geom(kCostRowSplit, kRowTiles);
   using VRaw = u32x4_t;
@@ -562,6 +564,7 @@ struct Fp8Kv {
   static constexpr int kTiles = D / 16;
   static constexpr bool kBf16 = true;
   static constexpr bool kScaled = true;
+  static constexpr bool kPrior = false;
   static constexpr int kRowTiles = 1;
   static constexpr int kRowGeom = row_geom(kCostRowSplitFp8, kRowTiles);
   using VRaw = u32x2_t;  // 4 codes of page 0 (keys 4q..4q+3), 4 codes of page 1
@@ -637,6 +640,33 @@ struct Fp8KvTall : Fp8Kv<D_> {
   static constexpr int kRowTiles = 2;
   static constexpr int kRowGeom = row_geom(kCostRowSplitFp8, kRowTiles);
 };
+
+// A trait whose final outputs fold in a result over other keys of the same rows (AttnArgs::prior_o /
+// prior_lse, log-sum-exp weights): the suffix pass of shared-prefix attention finishes its rows with
+// the prefix pass's results this way instead of a separate merge launch.
+template <class B>
+struct WithPrior : B {
+  static constexpr bool kPrior = true;
+};
+
+// (o, lse) over some keys of row `orow` and the prior result over the others -> the result over both.
+// A side that saw no key (lse = -inf) has weight 0.
+__device__ __forceinline__ void fold_prior(const float* prior_o, const float* prior_lse, int64_t orow, int D, int d,
+                                           f32x4_t& o, float& lse) {
+  const float lp = prior_lse[orow];
+  if (lp == -INFINITY) return;
+  const f32x4_t op = *reinterpret_cast<const f32x4_t*>(prior_o + orow * D + d);
+  if (lse == -INFINITY) {
+    o = op;
+    lse = lp;
+    return;
+  }
+  const float m = fmaxf(lse, lp);
+  const float ws = fast_exp2((lse - m) * kLog2e), wp = fast_exp2((lp - m) * kLog2e);
+  const float inv = 1.f / (ws + wp);
+  o = (o * ws + op * wp) * inv;
+  lse = m + fast_log2(ws + wp) * kLn2;
+}
 
 // ---------------------------------------------------------------------------
 // Per-lane online-softmax state for RT tiles of 16 query rows.
@@ -1096,6 +1126,7 @@ __device__ __forceinline__ void emit(const AttnArgs& A, const RowInfo& ri, int r
   const int d = 16 * t + 4 * quad;
   if (part < 0) {
     const int64_t elem = (int64_t(ri.tok) * A.num_q_heads + ri.head) * TR::D + d;
+    if constexpr (TR::kPrior) fold_prior(A.prior_o, A.prior_lse, int64_t(ri.tok) * A.num_q_heads + ri.head, TR::D, d, o, lse_nat);
     if (A.out_f32) *reinterpret_cast<f32x4_t*>(A.out_f32 + elem) = o;  // cascade pass: fp32 result
     else TR::store_out(static_cast<char*>(A.out) + elem * TR::kEb, o);
     if (write_lse) A.lse[int64_t(ri.tok) * A.num_q_heads + ri.head] = lse_nat;
@@ -1929,10 +1960,16 @@ __device__ bool cursor_next(UnitCursor& cu, const PlanView& v, P seq_lens, P qsl
 // first + j: position 1 -- the grain's last unit -- for j = 0, position 0 after) into out / lse.
 // All kThreads threads of the workgroup take part.  A thread takes kInFlight of its rows at a time
 // and loads kPieces pieces of them together before folding them in, in piece order.
+// Results over other keys folded into a merge's final rows (read only when TR::kPrior).
+struct Prior {
+  const float* o;
+  const float* lse;
+};
+
 template <class TR, int kInFlight, int kPieces>
 __device__ void merge_unit_stream(const float* part_o, const float* part_lse, void* out, float* out_f32, float* lse,
                            cptr<int32_t> qsl, int num_q_heads, int group, const pa_plan_unit& U, int64_t first,
-                           int n_pieces) {
+                           int n_pieces, Prior pr = {nullptr, nullptr}) {
   constexpr int kLanesPerRow = TR::D / 4;
   constexpr int kRowsPerPass = kThreads / kLanesPerRow;
   const int q0 = qsl[U.seq];
@@ -1986,10 +2023,12 @@ __device__ void merge_unit_stream(const float* part_o, const float* part_lse, vo
       const int head = U.kv_head * group + (rr - tk * group);
       const int64_t orow = int64_t(q0 + tk) * num_q_heads + head;
       // a row that saw no key at all (possible under a tree mask) gets out = 0, lse = -inf
-      const f32x4_t res = O[i] * (L[i] > 0.f ? 1.f / L[i] : 0.f);
+      f32x4_t res = O[i] * (L[i] > 0.f ? 1.f / L[i] : 0.f);
+      float lse_v = L[i] > 0.f ? M[i] + fast_log2(L[i]) * kLn2 : -INFINITY;
+      if constexpr (TR::kPrior) fold_prior(pr.o, pr.lse, orow, TR::D, 4 * d4, res, lse_v);
       if (out_f32) *reinterpret_cast<f32x4_t*>(out_f32 + orow * TR::D + 4 * d4) = res;
       else TR::store_out(static_cast<char*>(out) + (orow * TR::D + 4 * d4) * TR::kEb, res);
-      if (d4 == 0) lse[orow] = L[i] > 0.f ? M[i] + fast_log2(L[i]) * kLn2 : -INFINITY;
+      if (d4 == 0) lse[orow] = lse_v;
     }
   }
 }
@@ -2006,10 +2045,10 @@ constexpr int kMergeFastPieces = 8;
 template <class TR>
 __device__ void merge_unit(const float* part_o, const float* part_lse, void* out, float* out_f32, float* lse,
                            cptr<int32_t> qsl, int num_q_heads, int group, const pa_plan_unit& U, int64_t first,
-                           int n_pieces, float* wbuf) {
+                           int n_pieces, float* wbuf, Prior pr = {nullptr, nullptr}) {
   // key-split units (<= 32 rows) take one round trip for up to 4 pieces in the streaming form
   if (n_pieces > kMergeFastPieces || U.n_rows <= kSplitRows) {
-    merge_unit_stream<TR, 4, 4>(part_o, part_lse, out, out_f32, lse, qsl, num_q_heads, group, U, first, n_pieces);
+    merge_unit_stream<TR, 4, 4>(part_o, part_lse, out, out_f32, lse, qsl, num_q_heads, group, U, first, n_pieces, pr);
     return;
   }
   const int q0 = qsl[U.seq];
@@ -2054,11 +2093,30 @@ __device__ void merge_unit(const float* part_o, const float* part_lse, void* out
       L += e[j];
     }
     // a row that saw no key at all (possible under a tree mask) gets out = 0, lse = -inf
-    const float inv = L > 0.f ? 1.f / L : 0.f;
+    float inv = L > 0.f ? 1.f / L : 0.f;
+    float lse_v = L > 0.f ? M + fast_log2(L) * kLn2 : -INFINITY;
+    if constexpr (TR::kPrior) {  // the pieces' weights scaled by the unit's share against the prior result
+      const float lp = pr.lse[out_row(r)];
+      float wp = 0.f;
+      if (lp != -INFINITY) {
+        if (lse_v == -INFINITY) {
+          wp = 1.f;
+          lse_v = lp;
+        } else {
+          const float m = fmaxf(lse_v, lp);
+          const float ws = fast_exp2((lse_v - m) * kLog2e), wq = fast_exp2((lp - m) * kLog2e);
+          const float t = 1.f / (ws + wq);
+          inv *= ws * t;
+          wp = wq * t;
+          lse_v = m + fast_log2(ws + wq) * kLn2;
+        }
+      }
+      wbuf[kMergeFastPieces * kPartRows + r] = wp;
+    }
 #pragma unroll
     for (int j = 0; j < kMergeFastPieces; ++j)
       if (j < n_pieces) wbuf[j * kPartRows + r] = e[j] * inv;
-    lse[out_row(r)] = L > 0.f ? M + fast_log2(L) * kLn2 : -INFINITY;
+    lse[out_row(r)] = lse_v;
   }
   wait_lds();
   lds_barrier();  // wbuf written (a full __syncthreads would also wait for the o loads in flight)
@@ -2081,6 +2139,8 @@ __device__ void merge_unit(const float* part_o, const float* part_lse, void* out
       const int r = rbase + r0 + i * kRowsPerPass;
       if (r >= U.n_rows) continue;
       const int64_t orow = out_row(r);
+      if constexpr (TR::kPrior)
+        acc[i] += *reinterpret_cast<const f32x4_t*>(pr.o + orow * TR::D + 4 * d4) * wbuf[kMergeFastPieces * kPartRows + r];
       if (out_f32) *reinterpret_cast<f32x4_t*>(out_f32 + orow * TR::D + 4 * d4) = acc[i];
       else TR::store_out(static_cast<char*>(out) + (orow * TR::D + 4 * d4) * TR::kEb, acc[i]);
     }
@@ -2116,7 +2176,7 @@ __device__ void arrive_and_merge(const AttnArgs& A, const pa_plan_unit& U, int64
   __syncthreads();  // flag read by every thread before it is reused
   if (!last) return;
   merge_unit<TR>(A.part_o, A.part_lse, A.out, A.out_f32, A.lse, ro(A.plan.qsl), A.num_q_heads, A.plan.group, U,
-                 first, n_pieces, wbuf);
+                 first, n_pieces, wbuf, Prior{A.prior_o, A.prior_lse});
   if (threadIdx.x == 0) __hip_atomic_store(A.arrive + first, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -2935,6 +2995,24 @@ static int launch_fused_t(const AttnArgs& a, int grid, void* stream) {
 }
 
 int launch_attention_fused(const AttnArgs& a, int dtype, int D, int grid, void* stream, bool tall) {
+  if (a.prior_lse) {  // causal masks only (the shared-prefix suffix pass)
+    if (dtype == PA_BF16 && D == 128 && tall)
+      hipLaunchKernelGGL((attention_fused_kernel<WithPrior<Bf16Tall<128>>, false>), dim3(grid), dim3(kThreads), 0,
+                         as_stream(stream), a);
+    else if (dtype == PA_BF16 && D == 128)
+      hipLaunchKernelGGL((attention_fused_kernel<WithPrior<Bf16<128>>, false>), dim3(grid), dim3(kThreads), 0,
+                         as_stream(stream), a);
+    else if (dtype == PA_BF16)
+      hipLaunchKernelGGL((attention_fused_kernel<WithPrior<Bf16<64>>, false>), dim3(grid), dim3(kThreads), 0,
+                         as_stream(stream), a);
+    else if (D == 128)
+      hipLaunchKernelGGL((attention_fused_kernel<WithPrior<F32<128>>, false>), dim3(grid), dim3(kThreads), 0,
+                         as_stream(stream), a);
+    else
+      hipLaunchKernelGGL((attention_fused_kernel<WithPrior<F32<64>>, false>), dim3(grid), dim3(kThreads), 0,
+                         as_stream(stream), a);
+    return int(hipGetLastError());
+  }
   if (dtype == PA_BF16 && D == 128 && tall && !a.tree_mask) {
     hipLaunchKernelGGL((attention_fused_kernel<Bf16Tall<128>, false>), dim3(grid), dim3(kThreads), 0,
                        as_stream(stream), a);
